@@ -1,0 +1,210 @@
+"""fp64 CPU oracle for kernelised linear attention, global and block-causal.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+this package.  The product path (the HIP library and its Python binding)
+never imports, calls or falls back to anything here, and nothing here
+imports the product.
+
+Sources (web pages about SANA-Video; cited by title and section):
+
+* [TR] "Nvidia, MIT ve diğerleri video yapay zeka devrimini başlattı"
+  (aihaber.org), section "Sabit Bellekli KV önbelleğe alma mekanizması":
+  the video is cut into N blocks; later blocks fuse earlier blocks'
+  features through linear attention and never the reverse; the attention
+  can be split along token order with identical results, every token's
+  result coming from KV products plus accumulation; KV1 is cached, KV2 is
+  added to give KV1-2, and after block n the global KV matrix results;
+  each block's work is the accumulated KVsum plus its own KV.
+* [ZH] sd114.wiki article on SANA-Video, section "1. 线性 DiT：用 O(N)
+  替代 O(N²)": attention is split into a kernel-function mapping followed
+  by a global aggregation, never building the N x N attention matrix;
+  section "2. 块线性注意力 + 恒定内存 KV 缓存": each chunk keeps only one
+  accumulated state as global context, updated by composition, with no
+  stored history of keys and values.
+* [EN] "SANA-Video: Efficient Video Generation with Block Linear Diffusion
+  Transformer" (chatpaper.ai), abstract, designs (1) Linear DiT and
+  (2) Constant-Memory KV cache for Block Linear Attention.
+
+What the pages leave open, and the reading taken here (the same reading
+the HIP library implements):
+
+* The kernel-function mapping is phi(x) = max(x, 0) (ReLU), applied to
+  queries and keys only, never to values.
+* The pages never write a normaliser.  The output is normalised by the
+  kernel-weight row sum plus a positive eps:
+  o_i = phi(q_i)^T S / (phi(q_i) . z + eps), with S = sum_j phi(k_j) v_j^T
+  (d x d) and z = sum_j phi(k_j) (d) over the tokens query i may see.
+* Visibility: bidirectional inside a block, causal across blocks
+  ([TR]: each block uses KVsum plus its *own* KV).  Token j is visible to
+  query i iff block(j) <= block(i).
+
+Layout: every tensor is a numpy array [B, H, T, d]; a state is a pair
+(S [B, H, d, d], z [B, H, d]) with S[a, c] = sum_t phi(k_t)[a] v_t[c].
+All arithmetic is float64 (or exact rationals in ``quadratic_exact``).
+"""
+
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "phi",
+    "kv_of_block",
+    "readout",
+    "chunk_forward",
+    "global_forward",
+    "stream_forward",
+    "prefix_forward",
+    "quadratic_forward",
+    "quadratic_exact",
+    "zero_state",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def phi(x):
+    """Kernel-function mapping ([ZH] section 1): ReLU, elementwise."""
+    x = _f64(x)
+    return np.where(x > 0.0, x, 0.0)
+
+
+def zero_state(B, H, d):
+    """The state before the first block: S_0 = 0, z_0 = 0 ([TR]: the cache
+    starts empty and KV1 is the first thing put in it)."""
+    return np.zeros((B, H, d, d)), np.zeros((B, H, d))
+
+
+def kv_of_block(K, V):
+    """One block's KV product ([TR], [ZH] section 2).
+
+    KV = phi(K)^T V  ([B, H, d, d], rows indexed by the key feature a,
+    columns by the value feature c) and k = phi(K)^T 1 ([B, H, d]).
+    """
+    fK = phi(K)
+    V = _f64(V)
+    KV = np.matmul(np.swapaxes(fK, -1, -2), V)
+    k = fK.sum(axis=-2)
+    return KV, k
+
+
+def readout(Q, S, z, eps):
+    """Global aggregation for a set of queries against one state.
+
+    o_i = phi(q_i)^T S / (phi(q_i) . z + eps), per (b, h).  Q is [B,H,T,d].
+    """
+    fQ = phi(Q)
+    num = np.matmul(fQ, S)                              # [B,H,T,d]
+    den = np.matmul(fQ, z[..., :, None]) + float(eps)   # [B,H,T,1]
+    return num / den
+
+
+def chunk_forward(Q, K, V, S_in, z_in, eps):
+    """One block of the block-causal form ([TR]: KVsum plus the current
+    block's KV): S_out = S_in + KV_n, z_out = z_in + k_n, and the block's
+    queries read S_out / z_out.  Returns (O, S_out, z_out)."""
+    KV, k = kv_of_block(K, V)
+    S_out = _f64(S_in) + KV
+    z_out = _f64(z_in) + k
+    return readout(Q, S_out, z_out, eps), S_out, z_out
+
+
+def global_forward(Q, K, V, eps):
+    """Global (non-causal) linear attention ([ZH] section 1; [EN] design
+    (1)): one state over every token, read by every query.
+    Returns (O, S, z)."""
+    B, H, _, d = np.shape(Q)
+    S0, z0 = zero_state(B, H, d)
+    return chunk_forward(Q, K, V, S0, z0, eps)
+
+
+def stream_forward(blocks, eps, S0=None, z0=None):
+    """Block-wise streaming with a carried state ([TR]; [ZH] section 2).
+
+    ``blocks`` is an iterable of (Q_n, K_n, V_n).  Returns
+    (outputs, states) where states[n] = (S_n, z_n) after block n.
+    """
+    outs, states = [], []
+    S, z = S0, z0
+    for Qn, Kn, Vn in blocks:
+        if S is None:
+            B, H, _, d = np.shape(Qn)
+            S, z = zero_state(B, H, d)
+        O, S, z = chunk_forward(Qn, Kn, Vn, S, z, eps)
+        outs.append(O)
+        states.append((S, z))
+    return outs, states
+
+
+def prefix_forward(Q, K, V, bounds, eps):
+    """The same block-causal result by a separate route: every block's KV
+    first, then an inclusive prefix sum over the block axis ([TR]: KV1,
+    KV1-2, ..., global KV), then every block's queries against its prefix.
+
+    Q, K, V are the whole sequence [B,H,T,d]; ``bounds`` lists the block
+    start offsets (first 0) and ends with T.  Returns (O, S_prefix, z_prefix)
+    with S_prefix [C,B,H,d,d] and z_prefix [C,B,H,d].
+    """
+    C = len(bounds) - 1
+    KVs, ks = [], []
+    for n in range(C):
+        a, b = bounds[n], bounds[n + 1]
+        KV, k = kv_of_block(K[:, :, a:b], V[:, :, a:b])
+        KVs.append(KV)
+        ks.append(k)
+    S_pre = np.cumsum(np.stack(KVs), axis=0)
+    z_pre = np.cumsum(np.stack(ks), axis=0)
+    O = np.empty(np.shape(Q), dtype=np.float64)
+    for n in range(C):
+        a, b = bounds[n], bounds[n + 1]
+        O[:, :, a:b] = readout(Q[:, :, a:b], S_pre[n], z_pre[n], eps)
+    return O, S_pre, z_pre
+
+
+def quadratic_forward(Q, K, V, block_id, eps):
+    """Explicit quadratic form under the block-causal mask (tiny inputs).
+
+    W_ij = (phi(q_i) . phi(k_j)) * [block(j) <= block(i)],
+    o_i = sum_j W_ij v_j / (sum_j W_ij + eps).  This builds the T x T
+    matrix that linear attention avoids ([ZH] section 1), which is why it
+    is an independent route to the same numbers.  ``block_id`` is a length
+    T integer sequence.
+    """
+    fQ, fK, V = phi(Q), phi(K), _f64(V)
+    bid = np.asarray(block_id)
+    mask = (bid[None, :] <= bid[:, None]).astype(np.float64)   # [i, j]
+    W = np.matmul(fQ, np.swapaxes(fK, -1, -2)) * mask
+    return np.matmul(W, V) / (W.sum(axis=-1, keepdims=True) + float(eps))
+
+
+def quadratic_exact(q, k, v, block_id, eps):
+    """The quadratic form in exact rational arithmetic, pure Python loops.
+
+    q, k, v are nested lists [T][d] of ints or Fractions for one (b, h);
+    eps is a Fraction.  Every operation (max, x, +, /) is rational, so the
+    result (a [T][d] list of Fractions) is exact.
+    """
+    T = len(q)
+    d = len(q[0])
+    eps = Fraction(eps)
+
+    def relu(x):
+        x = Fraction(x)
+        return x if x > 0 else Fraction(0)
+
+    out = []
+    for i in range(T):
+        wsum = Fraction(0)
+        acc = [Fraction(0)] * d
+        for j in range(T):
+            if block_id[j] > block_id[i]:
+                continue
+            w = sum((relu(q[i][a]) * relu(k[j][a]) for a in range(d)), Fraction(0))
+            wsum += w
+            for c in range(d):
+                acc[c] += w * Fraction(v[j][c])
+        out.append([acc[c] / (wsum + eps) for c in range(d)])
+    return out

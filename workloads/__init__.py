@@ -1,0 +1,120 @@
+"""Seeded synthetic inputs shaped like SANA-Video's latent-token workloads.
+
+This module is shared by the tests, the benchmark and the oracle checks.
+It draws random numbers and rounds them to the storage precision; it holds
+none of the attention arithmetic.
+
+Token grids.  A 5 s, 81-frame clip becomes 21 latent frames (4x temporal
+compression); with the 8x spatial VAE plus a 2x2 patch the grid is the
+frame size / 16 per side: 480x832 -> 30x52 = 1,560 tokens per latent
+frame, 720x1280 -> 45x80 = 3,600 ("Nvidia, MIT ve diğerleri video yapay
+zeka devrimini başlattı", sections on DC-AE-V and the Wan-VAE / F8T4C16
+comparison).  The pages' quality benchmark (VBench) is not used; these
+seeded normal tensors stand in for real latents.
+
+Every tensor is [B, H, T, d] float32 holding values that are exactly
+representable in the configuration's storage type (bfloat16 values are
+rounded to nearest-even).  Any (config, tensor, chunk) triple can be
+regenerated on its own: the stream is
+``np.random.default_rng(np.random.SeedSequence([cfg, tensor, chunk]))``
+with tensor 0 = Q, 1 = K, 2 = V, 3 = the outlier-row mask.
+"""
+
+from dataclasses import dataclass
+
+import numpy as np
+
+EPS = float(np.float32(1e-6))
+
+Q_ID, K_ID, V_ID, MASK_ID = 0, 1, 2, 3
+
+
+@dataclass(frozen=True)
+class Workload:
+    cid: int            # seed namespace
+    name: str
+    form: str           # "global" or "chunk"
+    B: int
+    H: int
+    d: int
+    L: int              # tokens per call (per chunk, or the whole sequence)
+    chunks: int         # number of calls in sequence
+    dtype: str          # "f32" or "bf16"
+    scale: float = 1.0
+    outlier_frac: float = 0.0
+    outlier_scale: float = 1.0
+
+    @property
+    def tokens(self):
+        return self.L * self.chunks
+
+
+LAT_480 = 21 * 30 * 52   # 32,760
+LAT_720 = 21 * 45 * 80   # 75,600
+
+WORKLOADS = {
+    1: Workload(1, "tiny-f32-block-causal", "chunk", 1, 2, 32, 64, 4, "f32"),
+    2: Workload(2, "480p-5s-global", "global", 1, 16, 64, LAT_480, 1, "bf16"),
+    3: Workload(3, "720p-5s-global", "global", 1, 32, 64, LAT_720, 1, "bf16", scale=0.5),
+    4: Workload(4, "480p-1min-stream", "chunk", 1, 16, 64, LAT_480, 12, "bf16"),
+    5: Workload(5, "long-horizon-d128", "chunk", 4, 16, 128, 4 * 32 * 32, 40, "bf16",
+                outlier_frac=0.01, outlier_scale=8.0),
+}
+
+# The timed workload: one block-causal chunk at the 720p latent shape, the
+# config-3 distribution, chunk 1 read against the state left by chunk 0.
+CHUNK_720P = Workload(3, "720p-chunk", "chunk", 1, 32, 64, LAT_720, 2, "bf16", scale=0.5)
+
+
+def bf16_round(x):
+    """Round float32 values to the nearest bfloat16 (ties to even); the
+    result is float32 holding bf16-representable values.  Finite inputs."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _rng(cid, tensor, chunk):
+    return np.random.default_rng(np.random.SeedSequence([int(cid), int(tensor), int(chunk)]))
+
+
+def draw(cid, tensor, chunk, shape, dtype="bf16", scale=1.0,
+         outlier_frac=0.0, outlier_scale=1.0):
+    """One seeded tensor of standard normals, scaled, with optional outlier
+    rows, rounded to the storage precision."""
+    x = _rng(cid, tensor, chunk).standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    if outlier_frac > 0.0:
+        B, H, T, _ = shape
+        u = _rng(cid, MASK_ID, chunk).random(size=(3, B, H, T))
+        rows = u[tensor] < outlier_frac
+        x[rows] *= np.float32(outlier_scale)
+    if dtype == "bf16":
+        x = bf16_round(x)
+    return x
+
+
+def chunk_qkv(w, chunk):
+    """(Q, K, V) of chunk ``chunk`` of workload ``w`` as float32 arrays."""
+    shape = (w.B, w.H, w.L, w.d)
+    kw = dict(dtype=w.dtype, scale=w.scale, outlier_frac=w.outlier_frac,
+              outlier_scale=w.outlier_scale)
+    return tuple(draw(w.cid, t, chunk, shape, **kw) for t in (Q_ID, K_ID, V_ID))
+
+
+def random_qkv(seed, B, H, L, d, dtype="bf16", scale=1.0, chunk=0):
+    """Ad-hoc test shapes: the same generator under a caller-chosen seed."""
+    w = Workload(seed, "adhoc", "chunk", B, H, d, L, 1, dtype, scale=scale)
+    return chunk_qkv(w, chunk)
+
+
+def random_state(seed, B, H, d, tokens=1000):
+    """A plausible fp32 carried state (S, z): what ``tokens`` N(0,1) keys
+    and values would leave behind, drawn directly (S ~ N(0, tokens/2),
+    z ~ |N| * tokens/2.5) without running attention."""
+    g = _rng(seed, 7, 0)
+    S = (g.standard_normal((B, H, d, d)) * np.sqrt(tokens / 2.0)).astype(np.float32)
+    z = (np.abs(g.standard_normal((B, H, d))) * 0.1 + 0.4) * tokens
+    return S, z.astype(np.float32)
