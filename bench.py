@@ -1,0 +1,250 @@
+"""Benchmark: block-causal linear attention on one 720p latent chunk.
+
+One step is one la_chunk_forward call (KV reduction, split reduce + state
+add, readout) over a 720p 5 s latent chunk: B=1, H=32, d=64, L=75,600
+tokens (21 latent frames of 45 x 80), bfloat16 q/k/v, float32 output and
+state, read against the state left by the previous chunk.  Inputs are
+seeded synthetic normals x 0.5, resident in HBM before timing; two input
+sets alternate so consecutive steps never reuse cached inputs.
+
+Prints one JSON line.  `value` is latent tokens per second of the whole
+call; `roofline` covers the dominant kernel (the readout) with algorithmic
+bytes per launch over its average launch time from HIP events recorded on
+the library's stream inside the timed region; `cpu_baseline` times the fp64
+oracle on the same workload on the host.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain copy kernel for counter scaling
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "latent tokens/sec + % peak HBM BW, block-causal linear attn, 720p chunk"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "readout_720p_chunk_traffic.json")
+KERNEL_SOURCES = ["la_common.h", "kv_reduce.h", "state_update.h", "readout.h", "linattn.hip"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_causal_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_alg(B, H, L, d, s_in=2, s_out=4):
+    """Algorithmic HBM bytes of one chunk call and of each stage."""
+    tok = B * H * L * d
+    st = B * H * (d * d + d) * 4
+    kv = 2 * tok * s_in                  # read K, V once
+    readout = tok * (s_in + s_out) + st  # read Q, write O, read the updated state
+    call = 3 * tok * s_in + tok * s_out + 2 * st
+    return call, kv, readout
+
+
+def flops(B, H, L, d):
+    return 4 * B * H * L * d * d + 4 * B * H * L * d
+
+
+def stored_traffic(launch_bytes_alg):
+    """HBM bytes per readout launch from committed rocprofv3 counters, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, seconds_min=10.0):
+    """The fp64 oracle on the same 720p chunk, on the host cores."""
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    Q, K, V = workloads.chunk_qkv(w, 1)
+    B, H, L, d = w.B, w.H, w.L, w.d
+    S0 = np.random.default_rng(0).standard_normal((B, H, d, d)) * 100.0
+    z0 = np.full((B, H, d), 1e4)
+    runs, t_total = 0, 0.0
+    while t_total < seconds_min and runs < 5:
+        t0 = time.perf_counter()
+        oracle.chunk_forward(Q, K, V, S0, z0, workloads.EPS)
+        t_total += time.perf_counter() - t0
+        runs += 1
+    per = t_total / runs
+    return {"value": B * L / per, "unit": "latent tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"the full 720p chunk (B=1, H=32, d=64, L=75,600), fp64 numpy, "
+                      f"{runs} run(s), {per:.2f} s each; host cpus visible: "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def copy_calibration(steps):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    n = 1 << 28  # 256 Mi floats = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--kv-splits", type=int, default=0)
+    ap.add_argument("--plain-steps", type=int, default=0,
+                    help="also time this many steps without stage events (for comparison)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(heads shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_causal_linear_amd as la
+    import workloads
+
+    if args.copy_calibration:
+        copy_calibration(max(args.steps, 1))
+        return
+
+    w = workloads.CHUNK_720P
+    B, H, L, d = w.B, w.H, w.L, w.d
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating inputs for {w.name} (B={B} H={H} L={L} d={d})")
+
+    def upload(x):
+        return torch.from_numpy(x).to(dev).to(torch.bfloat16)
+
+    q0, k0, v0 = (upload(x) for x in workloads.chunk_qkv(w, 0))
+    sets = []
+    for chunk in (1, 2):
+        q, k, v = (upload(x) for x in workloads.chunk_qkv(w, chunk))
+        out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
+        st = torch.empty((B, H, d * d + d), dtype=torch.float32, device=dev)
+        sets.append((q, k, v, out, st))
+    # the committed state after chunk 0
+    _, state0 = la.global_forward(q0, k0, v0, eps=workloads.EPS)
+    del q0, k0, v0
+    torch.cuda.synchronize()
+    splits, rtok = la.plan(B, H, L, d, kv_splits=args.kv_splits)
+    log(f"plan: kv_splits={splits} readout_tokens_per_workgroup={rtok}")
+
+    def step(i, ev=None):
+        q, k, v, out, st = sets[i & 1]
+        la.chunk_forward(q, k, v, state0, out=out, state_out=st, eps=workloads.EPS,
+                         kv_splits=args.kv_splits, stage_events=ev)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    # timed region: every call records its stage events on the library's stream
+    evs = [la.StageEvents() for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    stages = np.array([e.elapsed_ms() for e in evs])  # [steps, 3] ms
+    for e in evs:
+        e.close()
+    ms = ms_total / args.steps
+    log(f"timed: {ms * 1e3:.1f} us/step")
+
+    plain_ms = None
+    if args.plain_steps > 0:
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.plain_steps):
+            step(i)
+        end.record()
+        torch.cuda.synchronize()
+        plain_ms = start.elapsed_time(end) / args.plain_steps
+        log(f"without stage events: {plain_ms * 1e3:.1f} us/step")
+
+    call_b, kv_b, ro_b = bytes_alg(B, H, L, d)
+    kv_ms, red_ms, ro_ms = (float(x) for x in stages.mean(axis=0))
+    tokens_per_s = B * L / (ms * 1e-3)
+    ro_gbs = ro_b / (ro_ms * 1e-3) / 1e9
+    kv_gbs = kv_b / (kv_ms * 1e-3) / 1e9
+    call_gbs = call_b / (ms * 1e-3) / 1e9
+    traffic = stored_traffic(ro_b)
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "latent tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "720p-chunk block-causal la_chunk_forward", "B": B, "H": H,
+                   "d": d, "L": L, "q_k_v": "bf16", "out": "f32", "state": "f32",
+                   "kv_splits": splits, "readout_tokens_per_workgroup": rtok},
+        "hbm_frac": call_gbs / PEAK_HBM_GBS,
+        "achieved_GBs": call_gbs,
+        "roofline": {"bound": "hbm", "kernel": "readout_bf16<64>", "achieved": ro_gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ro_gbs / PEAK_HBM_GBS,
+                     "traffic": traffic, "bytes_alg_per_launch": ro_b,
+                     "launch_us": ro_ms * 1e3},
+        "stages_us": {"kv_partial": kv_ms * 1e3, "state_reduce": red_ms * 1e3,
+                      "readout": ro_ms * 1e3},
+        "kv_partial_GBs": kv_gbs,
+        "mfma_frac_call": flops(B, H, L, d) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+    }
+    if plain_ms is not None:
+        result["ms_per_step_without_stage_events"] = plain_ms
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

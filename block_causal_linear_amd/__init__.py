@@ -1,0 +1,289 @@
+"""Python binding of liblinattn, the gfx950 linear-attention library.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, output buffers are allocated with torch when the caller does not
+pass them, and raw device pointers plus the current HIP stream go to the C
+ABI (include/linattn.h).  Every arithmetic step runs in the library's HIP
+kernels.  There is no fallback: if liblinattn.so is missing or a call is
+rejected, an exception is raised.
+
+Shapes: q, k, v and out are [B, H, L, d]; a state is [B, H, d*d + d] float32
+(S[a, c] at a*d + c, then z).  d is 32, 64 or 128; q/k/v are float32 or
+bfloat16; out is float32 (default) or bfloat16.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_OK, LA_E_INVAL, LA_E_UNSUPPORTED, LA_E_ALIGN, LA_E_ALIAS, LA_E_HIP = range(6)
+LA_F32, LA_BF16 = 0, 1
+DEFAULT_EPS = 1e-6
+
+_DTYPE = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} (status {status})")
+
+
+class LaunchOpts(ctypes.Structure):
+    _fields_ = [("kv_splits", ctypes.c_int), ("readout_tokens", ctypes.c_int),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "la_state_reset": [_P, _I, _I, _I, _P],
+    "la_chunk_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
+    "la_chunk_forward_ex": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
+                            ctypes.POINTER(LaunchOpts), _P],
+    "la_global_forward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
+    "la_global_forward_ex": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
+                             ctypes.POINTER(LaunchOpts), _P],
+    "la_plan": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
+    "la_status_string": [_I],
+    "la_abi_version": [],
+}
+EXPORTS = tuple(_SIGNATURES)
+
+
+def lib():
+    """The loaded liblinattn (ctypes.CDLL); raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m block_causal_linear_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, argtypes in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_char_p if name == "la_status_string" else ctypes.c_int
+        _lib = handle
+    return _lib
+
+
+def _status_string(status):
+    try:
+        return lib().la_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - only when the library itself is missing
+        return "unknown"
+
+
+def _check(status, what):
+    if status != LA_OK:
+        raise LinAttnError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def head_dim_of_state(state):
+    """d from a state's last dimension d*d + d."""
+    e = state.shape[-1]
+    d = (math.isqrt(4 * e + 1) - 1) // 2
+    if d * d + d != e:
+        raise ValueError(f"state last dimension {e} is not d*d + d")
+    return d
+
+
+def new_state(B, H, d, device="cuda"):
+    """A zero state [B, H, d*d + d] float32 (allocated by torch, cleared by
+    the library's fill kernel)."""
+    st = torch.empty((B, H, d * d + d), dtype=torch.float32, device=device)
+    state_reset(st)
+    return st
+
+
+def state_reset(state):
+    B, H, _ = state.shape
+    d = head_dim_of_state(state)
+    _need(state, "state", torch.float32)
+    _check(lib().la_state_reset(_ptr(state), B, H, d, _stream(state.device)), "la_state_reset")
+    return state
+
+
+def split_state(state):
+    """Views (S [B, H, d, d], z [B, H, d]) of a state tensor."""
+    d = head_dim_of_state(state)
+    return state[..., : d * d].unflatten(-1, (d, d)), state[..., d * d:]
+
+
+def _need(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _prepare(q, k, v, out, out_dtype, state_out, B_H_d=None):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, L, d]")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, L, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+    _need(out, "out")
+    if out.shape != q.shape or out.dtype not in _DTYPE or out.device != q.device:
+        raise ValueError("out must be [B, H, L, d], float32 or bfloat16, on q's device")
+    if state_out is None:
+        state_out = torch.empty((B, H, d * d + d), dtype=torch.float32, device=q.device)
+    _need(state_out, "state_out", torch.float32)
+    if tuple(state_out.shape) != (B, H, d * d + d) or state_out.device != q.device:
+        raise ValueError(f"state_out must be [{B}, {H}, {d * d + d}] on q's device")
+    return out, state_out
+
+
+def _opts(kv_splits, readout_tokens, stage_events):
+    if not kv_splits and not readout_tokens and stage_events is None:
+        return None
+    o = LaunchOpts()
+    o.kv_splits = int(kv_splits or 0)
+    o.readout_tokens = int(readout_tokens or 0)
+    if stage_events is not None:
+        o.stage_events = stage_events.as_ctypes()
+    return o
+
+
+def chunk_forward(q, k, v, state_in, out=None, state_out=None, eps=DEFAULT_EPS,
+                  out_dtype=torch.float32, kv_splits=0, readout_tokens=0, stage_events=None):
+    """One block of the block-causal form: returns (out, state_out) with
+    state_out = state_in + phi(K)^T V (and + phi(K)^T 1 for z) and every query
+    of the block read against state_out.  state_out may be state_in."""
+    out, state_out = _prepare(q, k, v, out, out_dtype, state_out)
+    _need(state_in, "state_in", torch.float32)
+    if state_in.shape != state_out.shape or state_in.device != q.device:
+        raise ValueError("state_in must match state_out's shape and device")
+    B, H, L, d = q.shape
+    o = _opts(kv_splits, readout_tokens, stage_events)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out), _ptr(state_out),
+            B, H, L, d, _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps))
+    L_ = lib()
+    if o is None:
+        rc = L_.la_chunk_forward(*args, _stream(q.device))
+    else:
+        rc = L_.la_chunk_forward_ex(*args, ctypes.byref(o), _stream(q.device))
+    _check(rc, "la_chunk_forward")
+    return out, state_out
+
+
+def global_forward(q, k, v, out=None, state_out=None, eps=DEFAULT_EPS,
+                   out_dtype=torch.float32, kv_splits=0, readout_tokens=0, stage_events=None):
+    """Global (non-causal) linear attention: returns (out, state_out) where
+    state_out holds the global (S, z)."""
+    out, state_out = _prepare(q, k, v, out, out_dtype, state_out)
+    B, H, L, d = q.shape
+    o = _opts(kv_splits, readout_tokens, stage_events)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_out),
+            B, H, L, d, _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps))
+    L_ = lib()
+    if o is None:
+        rc = L_.la_global_forward(*args, _stream(q.device))
+    else:
+        rc = L_.la_global_forward_ex(*args, ctypes.byref(o), _stream(q.device))
+    _check(rc, "la_global_forward")
+    return out, state_out
+
+
+def plan(B, H, L, d, in_dtype=torch.bfloat16, out_dtype=torch.float32, kv_splits=0,
+         readout_tokens=0):
+    """(kv_splits, readout_tokens_per_workgroup) the library would use."""
+    s, t = ctypes.c_int(), ctypes.c_int()
+    _check(lib().la_plan(B, H, L, d, _DTYPE[in_dtype], _DTYPE[out_dtype], int(kv_splits),
+                         int(readout_tokens), ctypes.byref(s), ctypes.byref(t)), "la_plan")
+    return s.value, t.value
+
+
+def abi_version():
+    return lib().la_abi_version()
+
+
+# ---------------------------------------------------------------------------
+# HIP events for per-stage timing (plumbing over libamdhip64).
+
+_hip = None
+
+
+def _hiplib():
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _hip = h
+    return _hip
+
+
+class StageEvents:
+    """Four HIP events that a forward call records around its stages:
+    [before KV reduction, before split reduce, before readout, after]."""
+
+    def __init__(self):
+        h = _hiplib()
+        self._arr = (ctypes.c_void_p * 4)()
+        for i in range(4):
+            ev = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self._arr[i] = ev.value
+
+    def as_ctypes(self):
+        return ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p))
+
+    def elapsed_ms(self):
+        """(kv, reduce, readout) milliseconds of the last recorded call."""
+        h = _hiplib()
+        if h.hipEventSynchronize(self._arr[3]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        out = []
+        for i in range(3):
+            ms = ctypes.c_float()
+            if h.hipEventElapsedTime(ctypes.byref(ms), self._arr[i], self._arr[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return tuple(out)
+
+    def close(self):
+        h = _hiplib()
+        for i in range(4):
+            if self._arr[i]:
+                h.hipEventDestroy(self._arr[i])
+                self._arr[i] = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

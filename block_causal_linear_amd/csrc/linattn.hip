@@ -1,0 +1,289 @@
+// Host side of the C ABI declared in include/linattn.h: argument checks,
+// launch planning, and the three launches of a forward call
+// (KV reduction -> split reduce + state add -> readout) on the caller's
+// stream.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "linattn.h"
+#include "la_common.h"
+#include "kv_reduce.h"
+#include "readout.h"
+#include "state_update.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+// KV workgroups the planner aims for: two per compute unit of a 256-CU
+// MI355X (measured best at the 720p chunk: 16 splits x 32 heads).
+constexpr int kKvTargetWorkgroups = 512;
+// A split should carry at least this many tokens per (d + 1) so that its
+// partial (d*d + d floats) stays small next to the K/V bytes it reads.
+constexpr int kKvMinTokensPerFeature = 8;
+// Readout workgroups the planner aims for: four per compute unit, each with a
+// contiguous token range of one head, so the state is staged into LDS once
+// per workgroup (measured best at the 720p chunk among 512..4736).
+constexpr int kReadoutTargetWorkgroups = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int elem_size(int dt) { return dt == LA_BF16 ? 2 : 4; }
+
+struct Plan {
+  int splits;       // 0 when L == 0
+  int tps;          // tokens per split
+  int kv_tile;      // tokens per KV tile
+  int readout_tpw;  // tokens per readout workgroup
+};
+
+int check_shape(int B, int H, int L, int d, int in_dt, int out_dt) {
+  if (B <= 0 || H <= 0 || L < 0) return LA_E_INVAL;
+  if (B > 65535 || H > 65535) return LA_E_INVAL;
+  if (d != 32 && d != 64 && d != 128) return LA_E_UNSUPPORTED;
+  if ((in_dt != LA_F32 && in_dt != LA_BF16) || (out_dt != LA_F32 && out_dt != LA_BF16))
+    return LA_E_UNSUPPORTED;
+  // keep every per-head element index inside 31 bits
+  if (static_cast<long long>(L) * d >= (1LL << 31)) return LA_E_INVAL;
+  return LA_OK;
+}
+
+Plan make_plan(int B, int H, int L, int d, int in_dt, int out_dt, int request,
+               int readout_request) {
+  Plan p{};
+  p.kv_tile = in_dt == LA_BF16 ? 64 : 16;
+  const long long bhc = static_cast<long long>(B) * H;
+  // readout workgroup tile: four waves x one wave tile (bf16), or 128 tokens
+  const int ro_unit = in_dt == LA_BF16 ? 4 * (d == 128 ? 32 : 16 * LA_READOUT_ROWS) : 128;
+  long long tpw = readout_request;
+  if (tpw <= 0) {
+    const long long per_head = (kReadoutTargetWorkgroups + bhc - 1) / bhc;
+    tpw = (L + per_head - 1) / per_head;
+  }
+  if (tpw < 1) tpw = 1;
+  tpw = (tpw + ro_unit - 1) / ro_unit * ro_unit;
+  const long long whole = (static_cast<long long>(L) + ro_unit - 1) / ro_unit * ro_unit;
+  if (tpw > whole && whole > 0) tpw = whole;
+  p.readout_tpw = static_cast<int>(tpw);
+  if (L == 0) {
+    p.splits = 0;
+    p.tps = 0;
+    return p;
+  }
+  const int ntiles = (L + p.kv_tile - 1) / p.kv_tile;
+  long long s;
+  if (request > 0) {
+    s = request;
+  } else {
+    s = (kKvTargetWorkgroups + bhc - 1) / bhc;
+    const long long by_size = L / (kKvMinTokensPerFeature * (d + 1));
+    s = s < by_size ? s : by_size;
+  }
+  if (s > ntiles) s = ntiles;
+  // the partials live in `out`: splits * (d*d + d) * 4 bytes per (b, h)
+  const long long cap = static_cast<long long>(L) * d * elem_size(out_dt) /
+                        (static_cast<long long>(d * d + d) * 4);
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  const int per = static_cast<int>((L + s - 1) / s);
+  p.tps = (per + p.kv_tile - 1) / p.kv_tile * p.kv_tile;
+  p.splits = (L + p.tps - 1) / p.tps;
+  return p;
+}
+
+int record(const la_launch_opts* o, int i, hipStream_t stream) {
+  if (o == nullptr || o->stage_events == nullptr) return LA_OK;
+  return hipEventRecord(o->stage_events[i], stream) == hipSuccess ? LA_OK : LA_E_HIP;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? LA_OK : LA_E_HIP; }
+
+template <int D>
+int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int H, int L,
+              const float* state_in, float* dst, hipStream_t stream) {
+  const dim3 grid(p.splits, H, B);
+  if (in_dt == LA_BF16)
+    la::kv_partial_bf16<D><<<grid, la::kBlock, 0, stream>>>(
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), L, p.tps, state_in, dst);
+  else
+    la::kv_partial_f32<D><<<grid, la::kBlock, 0, stream>>>(
+        static_cast<const float*>(k), static_cast<const float*>(v), L, p.tps, state_in, dst);
+  return launched();
+}
+
+template <int D>
+int launch_readout(const Plan& p, const void* q, int in_dt, int out_dt, int B, int H, int L,
+                   const float* state, void* out, float eps, hipStream_t stream) {
+  const dim3 grid((L + p.readout_tpw - 1) / p.readout_tpw, H, B);
+  if (in_dt == LA_BF16) {
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    if (out_dt == LA_BF16)
+      la::readout_bf16<D, true><<<grid, la::kBlock, 0, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+    else
+      la::readout_bf16<D, false><<<grid, la::kBlock, 0, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+  } else {
+    const float* qq = static_cast<const float*>(q);
+    constexpr size_t smem = la::readout_f32_smem<D>();
+    if (out_dt == LA_BF16) {
+      if (smem > 65536 &&
+          hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
+        return LA_E_HIP;
+      la::readout_f32<D, true><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+    } else {
+      if (smem > 65536 &&
+          hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
+        return LA_E_HIP;
+      la::readout_f32<D, false><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+    }
+  }
+  return launched();
+}
+
+template <int D>
+int run(const Plan& p, const void* q, const void* k, const void* v, const float* state_in,
+        void* out, float* state_out, int B, int H, int L, int in_dt, int out_dt, float eps,
+        const la_launch_opts* opts, hipStream_t stream) {
+  constexpr int E = D * D + D;
+  const int n4 = E / 4;
+  const dim3 red_grid((n4 + la::kWave - 1) / la::kWave, H, B);
+  int rc;
+  if ((rc = record(opts, 0, stream)) != LA_OK) return rc;
+  float* partials = static_cast<float*>(out);
+  if (p.splits >= 1) {
+    float* dst = p.splits == 1 ? state_out : partials;
+    if ((rc = launch_kv<D>(p, k, v, in_dt, B, H, L, state_in, dst, stream)) != LA_OK) return rc;
+  }
+  if ((rc = record(opts, 1, stream)) != LA_OK) return rc;
+  if (p.splits != 1) {
+    la::state_reduce<<<red_grid, la::kBlock, 0, stream>>>(
+        reinterpret_cast<const float4*>(partials), p.splits, n4,
+        reinterpret_cast<const float4*>(state_in), reinterpret_cast<float4*>(state_out));
+    if ((rc = launched()) != LA_OK) return rc;
+  }
+  if ((rc = record(opts, 2, stream)) != LA_OK) return rc;
+  if (L > 0) {
+    if ((rc = launch_readout<D>(p, q, in_dt, out_dt, B, H, L, state_out, out, eps, stream)) != LA_OK)
+      return rc;
+  }
+  return record(opts, 3, stream);
+}
+
+int forward(const void* q, const void* k, const void* v, const float* state_in, bool chunk,
+            void* out, float* state_out, int B, int H, int L, int d, int in_dt, int out_dt,
+            float eps, const la_launch_opts* opts, hipStream_t stream) {
+  int rc = check_shape(B, H, L, d, in_dt, out_dt);
+  if (rc != LA_OK) return rc;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
+  if (state_out == nullptr || (chunk && state_in == nullptr)) return LA_E_INVAL;
+  if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr)) return LA_E_INVAL;
+  const void* ptrs[] = {q, k, v, out, state_in, state_out};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return LA_E_ALIGN;
+
+  const size_t bh = static_cast<size_t>(B) * H;
+  const size_t in_bytes = bh * L * d * elem_size(in_dt);
+  const size_t out_bytes = bh * L * d * elem_size(out_dt);
+  const size_t st_bytes = bh * (static_cast<size_t>(d) * d + d) * sizeof(float);
+  if (L > 0) {
+    const void* ins[] = {q, k, v};
+    for (const void* p : ins)
+      if (overlaps(out, out_bytes, p, in_bytes) || overlaps(state_out, st_bytes, p, in_bytes))
+        return LA_E_ALIAS;
+    if (overlaps(out, out_bytes, state_out, st_bytes) ||
+        overlaps(out, out_bytes, state_in, st_bytes))
+      return LA_E_ALIAS;
+  }
+  if (state_in != state_out && overlaps(state_in, st_bytes, state_out, st_bytes)) return LA_E_ALIAS;
+
+  const Plan p = make_plan(B, H, L, d, in_dt, out_dt, opts ? opts->kv_splits : 0,
+                           opts ? opts->readout_tokens : 0);
+  switch (d) {
+    case 32:
+      return run<32>(p, q, k, v, state_in, out, state_out, B, H, L, in_dt, out_dt, eps, opts, stream);
+    case 64:
+      return run<64>(p, q, k, v, state_in, out, state_out, B, H, L, in_dt, out_dt, eps, opts, stream);
+    default:
+      return run<128>(p, q, k, v, state_in, out, state_out, B, H, L, in_dt, out_dt, eps, opts, stream);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_state_reset(float* state, int B, int H, int d, hipStream_t stream) {
+  if (B <= 0 || H <= 0) return LA_E_INVAL;
+  if (d != 32 && d != 64 && d != 128) return LA_E_UNSUPPORTED;
+  if (state == nullptr) return LA_E_INVAL;
+  if (!aligned16(state)) return LA_E_ALIGN;
+  const size_t n4 = static_cast<size_t>(B) * H * (static_cast<size_t>(d) * d + d) / 4;
+  size_t blocks = (n4 + la::kBlock - 1) / la::kBlock;
+  if (blocks > 4096) blocks = 4096;
+  la::fill_zero<<<static_cast<unsigned>(blocks), la::kBlock, 0, stream>>>(
+      reinterpret_cast<float4*>(state), n4);
+  return launched();
+}
+
+int la_chunk_forward(const void* q, const void* k, const void* v, const float* state_in, void* out,
+                     float* state_out, int B, int H, int L, int d, int in_dt, int out_dt, float eps,
+                     hipStream_t stream) {
+  return forward(q, k, v, state_in, true, out, state_out, B, H, L, d, in_dt, out_dt, eps, nullptr,
+                 stream);
+}
+
+int la_chunk_forward_ex(const void* q, const void* k, const void* v, const float* state_in,
+                        void* out, float* state_out, int B, int H, int L, int d, int in_dt,
+                        int out_dt, float eps, const la_launch_opts* opts, hipStream_t stream) {
+  return forward(q, k, v, state_in, true, out, state_out, B, H, L, d, in_dt, out_dt, eps, opts,
+                 stream);
+}
+
+int la_global_forward(const void* q, const void* k, const void* v, void* out, float* state_out,
+                      int B, int H, int N, int d, int in_dt, int out_dt, float eps,
+                      hipStream_t stream) {
+  return forward(q, k, v, nullptr, false, out, state_out, B, H, N, d, in_dt, out_dt, eps, nullptr,
+                 stream);
+}
+
+int la_global_forward_ex(const void* q, const void* k, const void* v, void* out, float* state_out,
+                         int B, int H, int N, int d, int in_dt, int out_dt, float eps,
+                         const la_launch_opts* opts, hipStream_t stream) {
+  return forward(q, k, v, nullptr, false, out, state_out, B, H, N, d, in_dt, out_dt, eps, opts,
+                 stream);
+}
+
+int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_request,
+            int readout_tokens_request, int* kv_splits, int* readout_tokens) {
+  const int rc = check_shape(B, H, L, d, in_dt, out_dt);
+  if (rc != LA_OK) return rc;
+  if (kv_splits == nullptr || readout_tokens == nullptr) return LA_E_INVAL;
+  const Plan p = make_plan(B, H, L, d, in_dt, out_dt, kv_splits_request, readout_tokens_request);
+  *kv_splits = p.splits;
+  *readout_tokens = p.readout_tpw;
+  return LA_OK;
+}
+
+const char* la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "ok";
+    case LA_E_INVAL: return "invalid argument";
+    case LA_E_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case LA_E_ALIGN: return "pointer not 16-byte aligned";
+    case LA_E_ALIAS: return "illegal buffer overlap";
+    case LA_E_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int la_abi_version(void) { return kAbiVersion; }
+
+}  // extern "C"

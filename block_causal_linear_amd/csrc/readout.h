@@ -1,0 +1,286 @@
+// Readout of a block's queries against the updated state:
+//   o_i = phi(q_i)^T S / (phi(q_i) . z + eps)
+// (sd114.wiki article on SANA-Video, section "1. 线性 DiT": a kernel
+// mapping followed by a global aggregation, no N x N matrix; the block reads
+// KVsum plus its own KV, "Nvidia, MIT ve diğerleri video yapay zeka devrimini
+// başlattı", section "Sabit Bellekli KV önbelleğe alma mekanizması").
+#pragma once
+
+#include "la_common.h"
+
+// Two waves per SIMD is the most that fits d = 64 and d = 128 without spills.
+#ifndef LA_READOUT_MIN_WAVES
+#define LA_READOUT_MIN_WAVES 2
+#endif
+// (Measured at the 720p chunk: plain loads and stores beat the
+// non-temporal forms, and two 16-token row blocks per wave tile beat four.)
+#ifndef LA_READOUT_STREAM_STORES
+#define LA_READOUT_STREAM_STORES 0
+#endif
+#ifndef LA_READOUT_STREAM_LOADS
+#define LA_READOUT_STREAM_LOADS 0
+#endif
+// 16-token row blocks per wave tile at d <= 64.
+#ifndef LA_READOUT_ROWS
+#define LA_READOUT_ROWS 2
+#endif
+
+namespace la {
+
+// ---------------------------------------------------------------------------
+// bfloat16 queries on MFMA 16x16x32.
+//
+// phi(q) is exact in bfloat16.  The float32 state is split into a pair of
+// bfloat16 values S = S_hi + S_lo (S_lo rounds S - S_hi), which carries 16
+// significant bits; bf16 x bf16 products are exact in float32, so two MFMAs
+// per operand give phi(q)^T S with float32 accumulation and a representation
+// error of about 2^-17 relative per state entry.  The denominator phi(q).z
+// is a fifth column block whose B operand holds z (hi and lo) in every
+// column, so each lane's accumulator already holds the denominator of the
+// rows it owns: no cross-lane traffic.
+//
+// Row and column placement.  A row block is 16 tokens; MFMA row m holds
+// token sigma(m) = 4 (m % 4) + m / 4 of the block, so accumulator element i
+// of lane l (row 4 (l / 16) + i) is token 4 i + l / 16.  Column n of column
+// block nb holds state column pi(nb, n) = 16 W (nb / W) + W n + nb % W, where
+// W (4, or 2 when d = 32) values make one vector store.  Together these make
+// every store instruction of a wavefront write 4 consecutive tokens' rows
+// (1 KB at d = 64, float32) contiguously.
+//
+// The state is staged once per workgroup in LDS as S^T split into hi/lo
+// planes ([column block row][feature a], padded rows), so a B operand is a
+// single 16-byte LDS read.
+
+template <int D>
+struct ReadoutShape {
+  static constexpr int KS = D / 32;              // k-steps of 32 features
+  static constexpr int NBK = D / 16;             // 16-column blocks of S
+  static constexpr int W = (D == 32) ? 2 : 4;    // values per vector store
+  static constexpr int GRP = NBK / W;            // vector stores per token row
+  static constexpr int R = (D == 128) ? 2 : LA_READOUT_ROWS;  // 16-token row blocks per wave tile
+  static constexpr int TILE = 16 * R;            // tokens per wave tile
+  static constexpr int RS = D + 8;               // LDS row stride (bf16 elements)
+  static constexpr int UPR = D / 8;              // 16-byte units per query row
+  static constexpr int MIN_WAVES = LA_READOUT_MIN_WAVES;  // occupancy target per SIMD
+};
+
+template <typename T>
+__device__ __forceinline__ void store_out(T v, T* p) {
+#if LA_READOUT_STREAM_STORES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+__device__ __forceinline__ uint4 load_q(const uint4* p) {
+#if LA_READOUT_STREAM_LOADS
+  return load_stream(p);
+#else
+  return *p;
+#endif
+}
+
+// LDS row of state column c (inverse of pi above).
+template <int D>
+__device__ __forceinline__ int state_col_row(int c) {
+  constexpr int W = ReadoutShape<D>::W;
+  const int grp = c / (16 * W);
+  const int cc = c % (16 * W);
+  return 16 * (W * grp + cc % W) + cc / W;
+}
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kBlock, ReadoutShape<D>::MIN_WAVES) void readout_bf16(const uint16_t* __restrict__ q,
+                                                       const float* __restrict__ state,
+                                                       void* __restrict__ out, int L, int tpw,
+                                                       float eps) {
+  using Sh = ReadoutShape<D>;
+  constexpr int E = D * D + D;
+  constexpr int RS = Sh::RS;
+  __shared__ __attribute__((aligned(16))) uint16_t s_hi[(D + 1) * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t s_lo[(D + 1) * RS];
+
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const int tb = blockIdx.x * tpw;
+  const int te = min(L, tb + tpw);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = lane & 15, g = lane >> 4;
+
+  const float* st = state + bh * E;
+  for (int e = tid; e < D * D; e += kBlock) {
+    const int a = e / D, c = e % D;
+    const float x = st[e];
+    const uint16_t hi = to_bf16(x);
+    const uint16_t lo = to_bf16(x - from_bf16(hi));
+    const int row = state_col_row<D>(c);
+    s_hi[row * RS + a] = hi;
+    s_lo[row * RS + a] = lo;
+  }
+  for (int a = tid; a < D; a += kBlock) {
+    const float x = st[D * D + a];
+    const uint16_t hi = to_bf16(x);
+    s_hi[D * RS + a] = hi;
+    s_lo[D * RS + a] = to_bf16(x - from_bf16(hi));
+  }
+  __syncthreads();
+
+  const uint4* qb = reinterpret_cast<const uint4*>(q + bh * static_cast<size_t>(L) * D);
+  const int tok_a = 4 * (n & 3) + (n >> 2);  // token (within a row block) of A row n
+
+  // A operands of one wave tile: phi(q) rows, zero past the end of the range.
+  auto load_a = [&](uint4 (&a)[Sh::R][Sh::KS], int tile) {
+#pragma unroll
+    for (int r = 0; r < Sh::R; ++r) {
+      const int tok = tile + 16 * r + tok_a;
+#pragma unroll
+      for (int s = 0; s < Sh::KS; ++s)
+        a[r][s] = tok < te ? relu_bf16x8(load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g))
+                           : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  uint4 a[Sh::R][Sh::KS];
+  int tile = tb + wave * Sh::TILE;
+  if (tile < te) load_a(a, tile);
+  for (; tile < te; tile += 4 * Sh::TILE) {
+    // B operands are re-read from LDS every tile instead of living in 80
+    // registers for the kernel's lifetime; this keeps two waves per SIMD.
+    asm volatile("" ::: "memory");
+    // issue the next tile's loads before this tile's MFMAs and stores
+    uint4 an[Sh::R][Sh::KS];
+    const int next = tile + 4 * Sh::TILE;
+    if (next < te) load_a(an, next);
+
+    f32x4 acc[Sh::R][Sh::NBK];
+    f32x4 accz[Sh::R];
+#pragma unroll
+    for (int r = 0; r < Sh::R; ++r) {
+      accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < Sh::NBK; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < Sh::KS; ++s) {
+      const int off = 8 * (4 * s + g);
+      const uint4 zh = *reinterpret_cast<const uint4*>(&s_hi[D * RS + off]);
+      const uint4 zl = *reinterpret_cast<const uint4*>(&s_lo[D * RS + off]);
+#pragma unroll
+      for (int r = 0; r < Sh::R; ++r) {
+        accz[r] = mfma_16x16x32(a[r][s], zh, accz[r]);
+        accz[r] = mfma_16x16x32(a[r][s], zl, accz[r]);
+      }
+#pragma unroll
+      for (int c = 0; c < Sh::NBK; ++c) {
+        const int row = 16 * c + n;
+        const uint4 bh16 = *reinterpret_cast<const uint4*>(&s_hi[row * RS + off]);
+        const uint4 bl16 = *reinterpret_cast<const uint4*>(&s_lo[row * RS + off]);
+#pragma unroll
+        for (int r = 0; r < Sh::R; ++r) {
+          acc[r][c] = mfma_16x16x32(a[r][s], bh16, acc[r][c]);
+          acc[r][c] = mfma_16x16x32(a[r][s], bl16, acc[r][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < Sh::R; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = tile + 16 * r + 4 * i + g;
+        if (tok >= te) continue;
+        const float inv = 1.0f / (accz[r][i] + eps);
+        const size_t row0 = static_cast<size_t>(bh * L + tok) * D;
+#pragma unroll
+        for (int gr = 0; gr < Sh::GRP; ++gr) {
+          const int col = 16 * Sh::W * gr + Sh::W * n;
+          if constexpr (Sh::W == 4) {
+            const float o0 = acc[r][4 * gr + 0][i] * inv, o1 = acc[r][4 * gr + 1][i] * inv;
+            const float o2 = acc[r][4 * gr + 2][i] * inv, o3 = acc[r][4 * gr + 3][i] * inv;
+            if constexpr (OUT_BF16) {
+              const u32x2 pk = {pack2(to_bf16(o0), to_bf16(o1)), pack2(to_bf16(o2), to_bf16(o3))};
+              store_out(pk, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + row0 + col));
+            } else {
+              store_out(f32x4{o0, o1, o2, o3},
+                        reinterpret_cast<f32x4*>(static_cast<float*>(out) + row0 + col));
+            }
+          } else {
+            const float o0 = acc[r][2 * gr + 0][i] * inv, o1 = acc[r][2 * gr + 1][i] * inv;
+            if constexpr (OUT_BF16) {
+              store_out(pack2(to_bf16(o0), to_bf16(o1)),
+                        reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + row0 + col));
+            } else {
+              store_out(f32x2{o0, o1}, reinterpret_cast<f32x2*>(static_cast<float*>(out) + row0 + col));
+            }
+          }
+        }
+      }
+    if (next < te) {
+#pragma unroll
+      for (int r = 0; r < Sh::R; ++r)
+#pragma unroll
+        for (int s = 0; s < Sh::KS; ++s) a[r][s] = an[r][s];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 queries: plain VALU.  The state sits in LDS; each thread owns
+// (token, column) outputs of a 32-token tile; the denominators are formed
+// once per token.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kBlock) void readout_f32(const float* __restrict__ q,
+                                                      const float* __restrict__ state,
+                                                      void* __restrict__ out, int L, int tpw,
+                                                      float eps) {
+  constexpr int TT = 32;
+  constexpr int E = D * D + D;
+  extern __shared__ float smem[];
+  float* sS = smem;             // E
+  float* sq = smem + E;         // TT * D
+  float* sden = sq + TT * D;    // TT
+
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const int tb = blockIdx.x * tpw;
+  const int te = min(L, tb + tpw);
+  const int tid = threadIdx.x;
+  const float* st = state + bh * E;
+  for (int e = tid; e < E; e += kBlock) sS[e] = st[e];
+  const float* qb = q + bh * static_cast<size_t>(L) * D;
+
+  for (int base = tb; base < te; base += TT) {
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kBlock) {
+      const int t = e / D;
+      const float x = (base + t < te) ? qb[static_cast<size_t>(base) * D + e] : 0.f;
+      sq[e] = x > 0.f ? x : 0.f;
+    }
+    __syncthreads();
+    if (tid < TT) {
+      float den = 0.f;
+      for (int a = 0; a < D; ++a) den = fmaf(sq[tid * D + a], sS[D * D + a], den);
+      sden[tid] = den + eps;
+    }
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kBlock) {
+      const int t = e / D, c = e % D;
+      if (base + t >= te) continue;
+      float num = 0.f;
+      for (int a = 0; a < D; ++a) num = fmaf(sq[t * D + a], sS[a * D + c], num);
+      const float o = num / sden[t];
+      const size_t idx = (bh * L + base + t) * static_cast<size_t>(D) + c;
+      if constexpr (OUT_BF16)
+        static_cast<uint16_t*>(out)[idx] = to_bf16(o);
+      else
+        static_cast<float*>(out)[idx] = o;
+    }
+  }
+}
+
+template <int D>
+constexpr size_t readout_f32_smem() {
+  return sizeof(float) * (D * D + D + 32 * D + 32);
+}
+
+}  // namespace la

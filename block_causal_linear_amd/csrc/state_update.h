@@ -1,0 +1,78 @@
+// State update of the block-causal form: S_out = S_in + sum_s P_s and
+// z_out = z_in + sum_s p_s ("Nvidia, MIT ve diğerleri video yapay zeka
+// devrimini başlattı", section "Sabit Bellekli KV önbelleğe alma
+// mekanizması": KV1 is cached, the next block's KV is added to it, and the
+// last block's addition yields the global KV matrix).
+#pragma once
+
+#include "la_common.h"
+
+namespace la {
+
+// One workgroup per 64 float4 of the (d*d + d) state of one (b, h): its
+// four wavefronts each sum one contiguous quarter of the splits (in split
+// order, loads unrolled by four), then wave 0 adds the four quarters in
+// order and adds the result to S_in.  The order is fixed, so repeated runs
+// are bitwise identical.  splits == 0 copies state_in (or writes zeros when
+// state_in is null).  state_in may equal state_out: each element is read
+// before it is written, by the same thread.
+__global__ __launch_bounds__(kBlock) void state_reduce(const float4* __restrict__ partials,
+                                                       int splits, int n4,
+                                                       const float4* state_in,
+                                                       float4* state_out) {
+  __shared__ float4 part[kBlock / kWave][kWave];
+  const int j = threadIdx.x / kWave;
+  const int el = threadIdx.x % kWave;
+  const int e = blockIdx.x * kWave + el;
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const int per = (splits + 3) / 4;
+  const int s0 = min(splits, j * per);
+  const int s1 = min(splits, s0 + per);
+  float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [](float4& a, const float4& x) {
+    a.x += x.x;
+    a.y += x.y;
+    a.z += x.z;
+    a.w += x.w;
+  };
+  if (e < n4) {
+    const float4* p = partials + bh * static_cast<size_t>(splits) * n4 + e;
+    int s = s0;
+    for (; s + 4 <= s1; s += 4) {
+      const float4 x0 = p[static_cast<size_t>(s) * n4];
+      const float4 x1 = p[static_cast<size_t>(s + 1) * n4];
+      const float4 x2 = p[static_cast<size_t>(s + 2) * n4];
+      const float4 x3 = p[static_cast<size_t>(s + 3) * n4];
+      add(kv, x0);
+      add(kv, x1);
+      add(kv, x2);
+      add(kv, x3);
+    }
+    for (; s < s1; ++s) add(kv, p[static_cast<size_t>(s) * n4]);
+  }
+  part[j][el] = kv;
+  __syncthreads();
+  if (j != 0 || e >= n4) return;
+  float4 t = part[0][el];
+  add(t, part[1][el]);
+  add(t, part[2][el]);
+  add(t, part[3][el]);
+  const size_t idx = bh * n4 + e;
+  if (state_in != nullptr) {
+    const float4 si = state_in[idx];
+    t.x = si.x + t.x;
+    t.y = si.y + t.y;
+    t.z = si.z + t.z;
+    t.w = si.w + t.w;
+  }
+  state_out[idx] = t;
+}
+
+// Zero fill (used instead of a memset so that callers may graph-capture it).
+__global__ __launch_bounds__(kBlock) void fill_zero(float4* __restrict__ p, size_t n4) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * kBlock;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kBlock + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+}  // namespace la

@@ -1,0 +1,166 @@
+/*
+ * linattn.h - C ABI of a gfx950 (MI355X) library for kernelised linear
+ * attention over video latent tokens, in its global form and its
+ * block-causal (chunk-wise, constant-memory state) form.
+ *
+ * Sources, cited by page title and section:
+ *  [TR] "Nvidia, MIT ve diğerleri video yapay zeka devrimini başlattı"
+ *       (aihaber.org), section "Sabit Bellekli KV önbelleğe alma
+ *       mekanizması": a video is cut into blocks; later blocks fuse earlier
+ *       blocks' features and never the reverse; the computation splits along
+ *       token order with identical results; KV1 is cached, KV2 added to give
+ *       KV1-2, and after the last block the global KV matrix results; each
+ *       block costs only the accumulated KVsum plus its own KV.
+ *  [ZH] sd114.wiki article on SANA-Video, section "1. 线性 DiT" (kernel
+ *       mapping then global aggregation, no N x N matrix) and section
+ *       "2. 块线性注意力 + 恒定内存 KV 缓存" (one accumulated state per chunk,
+ *       constant memory, no stored history of keys and values).
+ *  [EN] "SANA-Video: Efficient Video Generation with Block Linear Diffusion
+ *       Transformer", abstract, designs (1) and (2).
+ *
+ * What is computed (per batch b and head h; phi(x) = max(x, 0)):
+ *   KV  = phi(K)^T V          (d x d, row a = key feature, column c = value feature)
+ *   k   = phi(K)^T 1          (d)
+ *   S_out = S_in + KV,  z_out = z_in + k
+ *   o_i = phi(q_i)^T S_out / (phi(q_i) . z_out + eps)   for every query i of the call
+ * The pages do not write the normaliser; the eps-regularised row sum above,
+ * and phi = ReLU, are this library's fixed choices.  Inside one call every
+ * query sees every key of the call (bidirectional within a block); across
+ * calls the state carries only earlier blocks (causal across blocks).
+ *
+ * Layouts (all contiguous, row-major):
+ *   q, k, v : [B][H][L][d] of in_dt      (token-major per head)
+ *   out     : [B][H][L][d] of out_dt
+ *   state   : [B][H][d*d + d] float32    S[a][c] at a*d + c, then z[a] at d*d + a
+ * d is 32, 64 or 128.  in_dt is LA_F32 or LA_BF16; out_dt is LA_F32 or
+ * LA_BF16; the state and all accumulation are float32.
+ *
+ * Ownership: the caller allocates every buffer (device memory) and owns it.
+ * The library allocates nothing and keeps no state between calls.  While a
+ * forward call runs, the front of `out` serves as scratch for per-split
+ * partial KV sums; `out` is completely overwritten with the result before
+ * the call's last kernel ends.
+ *
+ * Streams and errors: every call only enqueues work on `stream` (0 = the
+ * null stream) and returns at once.  Arguments are checked before anything
+ * is enqueued; a rejected call enqueues nothing and returns:
+ *   LA_E_INVAL        null pointer where L > 0, B/H <= 0, L < 0, eps < 0 or not finite
+ *   LA_E_UNSUPPORTED  d not in {32, 64, 128}, or an unknown dtype code
+ *   LA_E_ALIGN        a pointer not 16-byte aligned
+ *   LA_E_ALIAS        `out` overlaps an input or a state, or state_out overlaps
+ *                     q/k/v/out, or state_out partially overlaps state_in
+ *   LA_E_HIP          a kernel launch failed (hipGetLastError after launch)
+ * Faults inside kernels surface at the caller's next synchronisation.
+ * Calls are thread-safe; calls on different streams may run concurrently
+ * as long as their buffers are disjoint.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_OK 0
+#define LA_E_INVAL 1
+#define LA_E_UNSUPPORTED 2
+#define LA_E_ALIGN 3
+#define LA_E_ALIAS 4
+#define LA_E_HIP 5
+
+#define LA_F32 0
+#define LA_BF16 1
+
+/*
+ * la_state_reset - start of a video: S = 0, z = 0 ([TR]: the cache is empty
+ * before KV1 is put in it).
+ *   state : [B][H][d*d + d] float32, device memory, written.
+ * Clears with a fill kernel (no memset node), so it may be graph-captured.
+ */
+int la_state_reset(float* state, int B, int H, int d, hipStream_t stream);
+
+/*
+ * la_chunk_forward - one block of the block-causal form ([TR]: each block
+ * reads KVsum plus its own KV; [ZH] section 2: one accumulated state, no
+ * key/value history).
+ *   q, k, v   : [B][H][L][d] in_dt, read.  The block's tokens.
+ *   state_in  : [B][H][d*d+d] float32, read only.  The state after the
+ *               previous block (zeros for the first block).
+ *   out       : [B][H][L][d] out_dt, written (and used as scratch).
+ *   state_out : [B][H][d*d+d] float32, written: state_in + this block's KV.
+ *               May be the same pointer as state_in (in-place commit).
+ *   eps       : added to every denominator; >= 0 and finite.
+ * L = 0 is allowed: state_out = state_in and q/k/v/out may be NULL.
+ * Because state_in is never written (unless it is state_out), a diffusion
+ * sampler may call this repeatedly against one committed state.
+ */
+int la_chunk_forward(const void* q, const void* k, const void* v,
+                     const float* state_in, void* out, float* state_out,
+                     int B, int H, int L, int d, int in_dt, int out_dt,
+                     float eps, hipStream_t stream);
+
+/*
+ * la_global_forward - global (non-causal) linear attention over N tokens
+ * ([ZH] section 1; [EN] design (1)): la_chunk_forward with a zero state_in.
+ *   state_out receives the global (S, z) ([TR]: the global KV matrix).
+ * N = 0 is allowed: state_out = 0.
+ */
+int la_global_forward(const void* q, const void* k, const void* v,
+                      void* out, float* state_out,
+                      int B, int H, int N, int d, int in_dt, int out_dt,
+                      float eps, hipStream_t stream);
+
+/*
+ * Launch options for the _ex variants (same computation, same rules):
+ *   kv_splits     : token splits per (b, h) for the KV reduction; 0 lets the
+ *                   library choose.  A request is clamped to [1, the number
+ *                   of 64-token tiles] and to what the scratch in `out` holds.
+ *                   Results differ between split counts only by float32
+ *                   summation order.
+ *   readout_tokens: tokens per readout workgroup; 0 lets the library choose.
+ *                   A request is rounded up to the readout's workgroup tile
+ *                   (256 tokens, or 128 at d = 128; 128 for float32 inputs).
+ *                   Results do not depend on it.
+ *   stage_events  : NULL, or 4 caller-created events recorded on `stream`
+ *                   before the KV reduction, before the split reduce, before
+ *                   the readout, and after the readout (for timing).
+ */
+typedef struct la_launch_opts {
+  int kv_splits;
+  int readout_tokens;
+  hipEvent_t* stage_events;
+} la_launch_opts;
+
+int la_chunk_forward_ex(const void* q, const void* k, const void* v,
+                        const float* state_in, void* out, float* state_out,
+                        int B, int H, int L, int d, int in_dt, int out_dt,
+                        float eps, const la_launch_opts* opts, hipStream_t stream);
+
+int la_global_forward_ex(const void* q, const void* k, const void* v,
+                         void* out, float* state_out,
+                         int B, int H, int N, int d, int in_dt, int out_dt,
+                         float eps, const la_launch_opts* opts, hipStream_t stream);
+
+/*
+ * la_plan - the launch shape a forward call with these arguments (and the
+ * given kv_splits / readout_tokens requests, 0 = library's choice) would use,
+ * with no device work: *kv_splits receives the split count (1 = the KV
+ * kernel writes state_out directly and the split reduce is skipped),
+ * *readout_tokens the tokens per readout workgroup.  Returns a status code.
+ */
+int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_request,
+            int readout_tokens_request, int* kv_splits, int* readout_tokens);
+
+/* Static text for a status code. */
+const char* la_status_string(int status);
+
+/* ABI version of this header (increases on incompatible change). */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,123 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+function include/linattn.h declares, and rejects bad arguments before it
+enqueues anything (every call here fails validation, so no HIP call is
+made and the fake pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_causal_linear_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(la.LIB_PATH),
+                                reason="liblinattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(la_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"la_state_reset", "la_chunk_forward", "la_global_forward"} <= set(names)
+    lib = ctypes.CDLL(la.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(la.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert la.abi_version() == 1
+    for code in range(6):
+        assert la._status_string(code) != "unknown status"
+    assert la._status_string(99) == "unknown status"
+
+
+A = 1 << 20  # fake, 16-byte aligned addresses; never dereferenced
+BF16, F32 = la.LA_BF16, la.LA_F32
+
+
+def chunk(q=A, k=2 * A, v=3 * A, si=4 * A, out=5 * A, so=6 * A, B=1, H=2, L=64, d=64,
+          idt=BF16, odt=F32, eps=1e-6):
+    return la.lib().la_chunk_forward(q, k, v, si, out, so, B, H, L, d, idt, odt, eps, None)
+
+
+def glob(q=A, k=2 * A, v=3 * A, out=5 * A, so=6 * A, B=1, H=2, N=64, d=64, idt=BF16, odt=F32,
+         eps=1e-6):
+    return la.lib().la_global_forward(q, k, v, out, so, B, H, N, d, idt, odt, eps, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), la.LA_E_INVAL),
+    (dict(H=-1), la.LA_E_INVAL),
+    (dict(L=-5), la.LA_E_INVAL),
+    (dict(B=70000), la.LA_E_INVAL),
+    (dict(L=1 << 26, d=64), la.LA_E_INVAL),
+    (dict(d=48), la.LA_E_UNSUPPORTED),
+    (dict(d=256), la.LA_E_UNSUPPORTED),
+    (dict(idt=7), la.LA_E_UNSUPPORTED),
+    (dict(odt=3), la.LA_E_UNSUPPORTED),
+    (dict(eps=-1.0), la.LA_E_INVAL),
+    (dict(eps=float("nan")), la.LA_E_INVAL),
+    (dict(eps=float("inf")), la.LA_E_INVAL),
+    (dict(q=None), la.LA_E_INVAL),
+    (dict(v=None), la.LA_E_INVAL),
+    (dict(out=None), la.LA_E_INVAL),
+    (dict(si=None), la.LA_E_INVAL),
+    (dict(so=None), la.LA_E_INVAL),
+    (dict(q=A + 8), la.LA_E_ALIGN),
+    (dict(out=5 * A + 4), la.LA_E_ALIGN),
+    (dict(so=6 * A + 2), la.LA_E_ALIGN),
+    (dict(out=A), la.LA_E_ALIAS),                 # out == q
+    (dict(out=2 * A + 4096), la.LA_E_ALIAS),      # out overlaps k
+    (dict(so=3 * A + 256), la.LA_E_ALIAS),        # state_out inside v
+    (dict(so=5 * A + 1024), la.LA_E_ALIAS),       # state_out inside out
+    (dict(si=5 * A), la.LA_E_ALIAS),              # state_in inside out
+    (dict(si=6 * A + 16), la.LA_E_ALIAS),         # partial state overlap
+])
+def test_chunk_rejects(kw, code):
+    assert chunk(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), la.LA_E_INVAL),
+    (dict(d=16), la.LA_E_UNSUPPORTED),
+    (dict(k=None), la.LA_E_INVAL),
+    (dict(so=None), la.LA_E_INVAL),
+    (dict(k=2 * A + 4), la.LA_E_ALIGN),
+    (dict(out=3 * A), la.LA_E_ALIAS),
+])
+def test_global_rejects(kw, code):
+    assert glob(**kw) == code
+
+
+def test_state_reset_rejects():
+    f = la.lib().la_state_reset
+    assert f(None, 1, 1, 64, None) == la.LA_E_INVAL
+    assert f(A, 0, 1, 64, None) == la.LA_E_INVAL
+    assert f(A, 1, 1, 40, None) == la.LA_E_UNSUPPORTED
+    assert f(A + 4, 1, 1, 64, None) == la.LA_E_ALIGN
+
+
+def test_plan_shapes():
+    # the 720p chunk: 32 heads -> 16 splits of 4736 tokens
+    s, t = la.plan(1, 32, 75600, 64)
+    assert s == 16
+    # tiny chunks write the state directly from the KV kernel
+    assert la.plan(1, 2, 64, 32, in_dtype=la.torch.float32)[0] == 1
+    # requests are clamped to the tile count and to the scratch in `out`
+    assert la.plan(1, 1, 100, 64, kv_splits=50)[0] == 1
+    assert la.plan(1, 1, 6400, 64, kv_splits=7)[0] == 7
+    assert la.plan(1, 1, 0, 64)[0] == 0
+    # readout: 32 workgroups per head at 720p, 128-token multiples
+    assert la.plan(1, 32, 75600, 64)[1] == 2432
+    assert la.plan(1, 32, 75600, 64, readout_tokens=300)[1] == 384
+    with pytest.raises(la.LinAttnError):
+        la.plan(1, 1, 10, 48)

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Bounds (normwise per (b, h, block) slice, max |got - ref| / max |ref|):
+1e-5 for float32 inputs, 2e-3 for bfloat16 inputs with float32 output.
+The state (S, z) is compared the same way.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import TOL, dev, host, out_err, report, state_err, state_np
+
+import block_causal_linear_amd as la
+
+pytestmark = pytest.mark.gpu
+EPS = workloads.EPS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_chunk(Q, K, V, S_in_np, dtype, kv_splits=0, out_dtype=torch.float32):
+    st_in = torch.from_numpy(S_in_np).cuda()
+    out, st = la.chunk_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), st_in,
+                               eps=EPS, kv_splits=kv_splits, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return host(out), host(st)
+
+
+def check_chunk(name, Q, K, V, S_in, z_in, dtype, kv_splits=0):
+    O_ref, S_ref, z_ref = oracle.chunk_forward(Q, K, V, S_in, z_in, EPS)
+    O, st = run_chunk(Q, K, V, state_np(S_in, z_in), dtype, kv_splits)
+    eo = out_err(O, O_ref)
+    es, ez = state_err(st, S_ref, z_ref)
+    report(name, out=eo, S=es, z=ez)
+    assert eo <= TOL[dtype], eo
+    assert es <= TOL[dtype] and ez <= TOL[dtype], (es, ez)
+    return O, st
+
+
+# ---------------------------------------------------------------------------
+# small shapes spanning several tiles and a ragged tail
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("L", [1, 15, 64, 333, 2085])
+def test_chunk_small(dtype, d, L):
+    B, H = 2, 3
+    Q, K, V = workloads.random_qkv(1000 + L, B, H, L, d, dtype=dtype)
+    S_in, z_in = workloads.random_state(L + d, B, H, d)
+    S_in, z_in = S_in.astype(np.float64), z_in.astype(np.float64)
+    check_chunk(f"chunk {dtype} d={d} L={L}", Q, K, V, S_in, z_in, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_global_small(dtype, d):
+    B, H, N = 1, 2, 1500
+    Q, K, V = workloads.random_qkv(77, B, H, N, d, dtype=dtype)
+    O_ref, S_ref, z_ref = oracle.global_forward(Q, K, V, EPS)
+    out, st = la.global_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), eps=EPS)
+    torch.cuda.synchronize()
+    eo = out_err(host(out), O_ref)
+    es, ez = state_err(host(st), S_ref, z_ref)
+    report(f"global {dtype} d={d}", out=eo, S=es, z=ez)
+    assert eo <= TOL[dtype] and es <= TOL[dtype] and ez <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+
+
+def test_config1_tiny_f32_stream():
+    w = workloads.WORKLOADS[1]
+    state = la.new_state(w.B, w.H, w.d)
+    blocks = [workloads.chunk_qkv(w, n) for n in range(w.chunks)]
+    outs, states = oracle.stream_forward(blocks, EPS)
+    for n, (Q, K, V) in enumerate(blocks):
+        out, state = la.chunk_forward(dev(Q, "f32"), dev(K, "f32"), dev(V, "f32"), state,
+                                      state_out=state, eps=EPS)
+        torch.cuda.synchronize()
+        eo = out_err(host(out), outs[n])
+        es, ez = state_err(host(state), *states[n])
+        report(f"config1 chunk {n}", out=eo, S=es, z=ez)
+        assert eo <= TOL["f32"] and es <= TOL["f32"] and ez <= TOL["f32"]
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_global_video_latent(cid):
+    w = workloads.WORKLOADS[cid]
+    Q, K, V = workloads.chunk_qkv(w, 0)
+    out, st = la.global_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), eps=EPS)
+    torch.cuda.synchronize()
+    O_ref, S_ref, z_ref = oracle.global_forward(Q, K, V, EPS)
+    eo = out_err(host(out), O_ref)
+    es, ez = state_err(host(st), S_ref, z_ref)
+    report(w.name, out=eo, S=es, z=ez)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
+def test_chunk_720p():
+    """The timed workload: chunk 1 of a 720p latent against chunk 0's state,
+    in the launch configuration the benchmark uses."""
+    w = workloads.CHUNK_720P
+    Q0, K0, V0 = workloads.chunk_qkv(w, 0)
+    Q1, K1, V1 = workloads.chunk_qkv(w, 1)
+    del Q0
+    KV0, k0 = oracle.kv_of_block(K0, V0)
+    del K0, V0
+    st0_np = state_np(KV0, k0)          # the float32 state the GPU receives
+    d = w.d
+    S0 = st0_np[..., : d * d].reshape(KV0.shape).astype(np.float64)
+    z0 = st0_np[..., d * d:].astype(np.float64)
+    st0 = torch.from_numpy(st0_np).cuda()
+    out, st1 = la.chunk_forward(dev(Q1, "bf16"), dev(K1, "bf16"), dev(V1, "bf16"), st0, eps=EPS)
+    torch.cuda.synchronize()
+    O_ref, S_ref, z_ref = oracle.chunk_forward(Q1, K1, V1, S0, z0, EPS)
+    eo = out_err(host(out), O_ref)
+    es, ez = state_err(host(st1), S_ref, z_ref)
+    report("720p chunk", out=eo, S=es, z=ez)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
+def test_stream_480p_1min():
+    """12 chunks with the state resident on the GPU (in place); every chunk's
+    output and state checked against a full-sequence recomputation that
+    takes all block KVs first and prefix-sums them."""
+    w = workloads.WORKLOADS[4]
+    state = la.new_state(w.B, w.H, w.d)
+    KVs, ks = [], []
+    worst = [0.0, 0.0, 0.0]
+    for n in range(w.chunks):
+        Q, K, V = workloads.chunk_qkv(w, n)
+        out, state = la.chunk_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), state,
+                                      state_out=state, eps=EPS)
+        KV, k = oracle.kv_of_block(K, V)
+        KVs.append(KV)
+        ks.append(k)
+        S_pre = np.sum(np.stack(KVs), axis=0)
+        z_pre = np.sum(np.stack(ks), axis=0)
+        O_ref = oracle.readout(Q, S_pre, z_pre, EPS)
+        torch.cuda.synchronize()
+        eo = out_err(host(out), O_ref)
+        es, ez = state_err(host(state), S_pre, z_pre)
+        report(f"480p stream chunk {n}", out=eo, S=es, z=ez)
+        worst = [max(a, b) for a, b in zip(worst, (eo, es, ez))]
+    assert max(worst) <= TOL["bf16"], worst
+
+
+def test_long_horizon_d128():
+    """40 chunks, B=4, H=16, d=128, 1% outlier rows x8; per-chunk drift of
+    S, z and O against the fp64 carried state."""
+    w = workloads.WORKLOADS[5]
+    state = la.new_state(w.B, w.H, w.d)
+    S = np.zeros((w.B, w.H, w.d, w.d))
+    z = np.zeros((w.B, w.H, w.d))
+    worst = 0.0
+    for n in range(w.chunks):
+        Q, K, V = workloads.chunk_qkv(w, n)
+        out, state = la.chunk_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), state,
+                                      state_out=state, eps=EPS)
+        O_ref, S, z = oracle.chunk_forward(Q, K, V, S, z, EPS)
+        torch.cuda.synchronize()
+        eo = out_err(host(out), O_ref)
+        es, ez = state_err(host(state), S, z)
+        report(f"long-horizon chunk {n}", out=eo, S=es, z=ez)
+        worst = max(worst, eo, es, ez)
+    assert worst <= TOL["bf16"], worst
+
+
+# ---------------------------------------------------------------------------
+# invariances, reproducibility, state handling, edge cases
+
+
+def test_split_invariance_and_reproducibility():
+    B, H, L, d = 1, 4, 9000, 64
+    Q, K, V = workloads.random_qkv(5, B, H, L, d)
+    S_in, z_in = workloads.random_state(6, B, H, d)
+    O_ref, S_ref, z_ref = oracle.chunk_forward(Q, K, V, S_in, z_in, 1e-6)
+    base = None
+    for splits in (0, 1, 2, 5, 17, 100):
+        O, st = run_chunk(Q, K, V, state_np(S_in, z_in), "bf16", kv_splits=splits)
+        eo = out_err(O, O_ref)
+        es, _ = state_err(st, S_ref, z_ref)
+        report(f"splits={splits}", out=eo, S=es)
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+        if base is None:
+            base = (O, st)
+        else:
+            # only float32 summation order differs between split counts
+            assert out_err(O, base[0]) < 1e-5
+    O2, st2 = run_chunk(Q, K, V, state_np(S_in, z_in), "bf16", kv_splits=0)
+    assert np.array_equal(O2, base[0]) and np.array_equal(st2, base[1])
+
+
+def test_in_place_state_matches_out_of_place():
+    B, H, L, d = 2, 2, 700, 64
+    Q, K, V = workloads.random_qkv(8, B, H, L, d)
+    S_in, z_in = workloads.random_state(9, B, H, d)
+    st_np = state_np(S_in, z_in)
+    q, k, v = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    a_in = torch.from_numpy(st_np).cuda()
+    out_a, st_a = la.chunk_forward(q, k, v, a_in, eps=EPS)
+    b_state = torch.from_numpy(st_np).cuda()
+    out_b, st_b = la.chunk_forward(q, k, v, b_state, state_out=b_state, eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b) and torch.equal(st_a, st_b)
+    assert torch.equal(a_in.cpu(), torch.from_numpy(st_np))  # state_in untouched
+
+
+def test_state_checkpoint_roundtrip_is_bitwise():
+    B, H, L, d = 1, 2, 500, 64
+    chunks = [workloads.random_qkv(30 + n, B, H, L, d) for n in range(4)]
+    dv = [tuple(dev(x, "bf16") for x in c) for c in chunks]
+    st = la.new_state(B, H, d)
+    outs = []
+    for q, k, v in dv:
+        o, st = la.chunk_forward(q, k, v, st, state_out=st, eps=EPS)
+        outs.append(o.clone())
+    st2 = la.new_state(B, H, d)
+    for q, k, v in dv[:2]:
+        _, st2 = la.chunk_forward(q, k, v, st2, state_out=st2, eps=EPS)
+    saved = st2.cpu()
+    st3 = saved.cuda()
+    for i, (q, k, v) in enumerate(dv[2:]):
+        o, st3 = la.chunk_forward(q, k, v, st3, state_out=st3, eps=EPS)
+        assert torch.equal(o, outs[2 + i])
+    torch.cuda.synchronize()
+    assert torch.equal(st3, st)
+
+
+def test_empty_chunk_and_sequence():
+    B, H, d = 1, 3, 64
+    S_in, z_in = workloads.random_state(11, B, H, d)
+    st_in = torch.from_numpy(state_np(S_in, z_in)).cuda()
+    e = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    out, st = la.chunk_forward(e, e, e, st_in, eps=EPS)
+    torch.cuda.synchronize()
+    assert out.shape == (B, H, 0, d) and torch.equal(st, st_in)
+    out, st = la.global_forward(e, e, e, eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st) == 0
+
+
+def test_degenerate_rows():
+    """All-non-positive query rows give exactly 0; all-non-positive key rows
+    contribute nothing (their values can be anything: the result is bitwise
+    unchanged, and equals the oracle with those tokens removed)."""
+    B, H, L, d = 1, 2, 300, 64
+    Q, K, V = workloads.random_qkv(12, B, H, L, d)
+    Q[:, :, 7] = -np.abs(Q[:, :, 7])
+    K[:, :, 100:150] = -np.abs(K[:, :, 100:150])
+    V2 = V.copy()
+    V2[:, :, 100:150] = workloads.random_qkv(99, B, H, 50, d)[2]
+    out, st = la.global_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), eps=EPS)
+    out2, st2 = la.global_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V2, "bf16"), eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[:, :, 7]) == 0
+    assert torch.equal(out, out2) and torch.equal(st, st2)
+    Kd = np.delete(K, np.s_[100:150], axis=2)
+    Vd = np.delete(V, np.s_[100:150], axis=2)
+    O_ref, _, _ = oracle.global_forward(Q, Kd, Vd, EPS)
+    assert out_err(host(out), O_ref) <= TOL["bf16"]
+
+
+def test_bf16_output():
+    B, H, L, d = 1, 4, 3000, 64
+    Q, K, V = workloads.random_qkv(13, B, H, L, d)
+    S_in, z_in = workloads.random_state(14, B, H, d)
+    O_ref, _, _ = oracle.chunk_forward(Q, K, V, S_in, z_in, EPS)
+    O, _ = run_chunk(Q, K, V, state_np(S_in, z_in), "bf16", out_dtype=torch.bfloat16)
+    eo = out_err(O, O_ref)
+    report("bf16 out", out=eo)
+    assert eo <= 2.0 ** -8
+
+
+def test_binding_rejects_bad_buffers():
+    B, H, L, d = 1, 1, 128, 64
+    x = torch.zeros((B, H, L, d), dtype=torch.bfloat16, device="cuda")
+    st = la.new_state(B, H, d)
+    with pytest.raises(la.LinAttnError) as e:
+        la.chunk_forward(x, x, x, st, out=x, eps=EPS)
+    assert e.value.status == la.LA_E_ALIAS
+    flat = torch.zeros(B * H * L * d + 8, dtype=torch.bfloat16, device="cuda")
+    mis = flat[4:4 + B * H * L * d].view(B, H, L, d)
+    with pytest.raises(la.LinAttnError) as e:
+        la.global_forward(mis, x, x, eps=EPS)
+    assert e.value.status == la.LA_E_ALIGN
+    out = torch.empty((B, H, L, d), dtype=torch.float32, device="cuda")
+    with pytest.raises(la.LinAttnError) as e:
+        la.chunk_forward(x, x, x, st, out=out, state_out=out.view(-1)[: d * d + d].view(1, 1, -1),
+                         eps=EPS)
+    assert e.value.status == la.LA_E_ALIAS

@@ -69,10 +69,15 @@ CHUNK_720P = Workload(3, "720p-chunk", "chunk", 1, 32, 64, LAT_720, 2, "bf16", s
 def bf16_round(x):
     """Round float32 values to the nearest bfloat16 (ties to even); the
     result is float32 holding bf16-representable values.  Finite inputs."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32)
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)
+    # finite values: the largest bit pattern plus 0x8000 still fits in 32 bits
+    lsb = u >> 16
+    lsb &= 1
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
+    return x
 
 
 def _rng(cid, tensor, chunk):
