@@ -164,7 +164,7 @@ def main():
     del q0, k0, v0
     torch.cuda.synchronize()
     splits, rtok = la.plan(B, H, L, d, kv_splits=args.kv_splits)
-    log(f"plan: kv_splits={splits} readout_tokens_per_workgroup={rtok}")
+    log(f"plan: kv_splits={splits} readout_workgroups={rtok}")
 
     def step(i, ev=None):
         q, k, v, out, st = sets[i & 1]
@@ -226,10 +226,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": "720p-chunk block-causal la_chunk_forward", "B": B, "H": H,
                    "d": d, "L": L, "q_k_v": "bf16", "out": "f32", "state": "f32",
-                   "kv_splits": splits, "readout_tokens_per_workgroup": rtok},
+                   "kv_splits": splits, "readout_workgroups": rtok},
         "hbm_frac": call_gbs / PEAK_HBM_GBS,
         "achieved_GBs": call_gbs,
-        "roofline": {"bound": "hbm", "kernel": "readout_bf16<64>", "achieved": ro_gbs,
+        "roofline": {"bound": "hbm", "kernel": "readout_sweep_bf16<64>", "achieved": ro_gbs,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ro_gbs / PEAK_HBM_GBS,
                      "traffic": traffic, "bytes_alg_per_launch": ro_b,
                      "launch_us": ro_ms * 1e3},

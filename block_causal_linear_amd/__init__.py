@@ -35,7 +35,7 @@ class LinAttnError(RuntimeError):
 
 
 class LaunchOpts(ctypes.Structure):
-    _fields_ = [("kv_splits", ctypes.c_int), ("readout_tokens", ctypes.c_int),
+    _fields_ = [("kv_splits", ctypes.c_int), ("readout_workgroups", ctypes.c_int),
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
 
 
@@ -162,19 +162,19 @@ def _prepare(q, k, v, out, out_dtype, state_out, B_H_d=None):
     return out, state_out
 
 
-def _opts(kv_splits, readout_tokens, stage_events):
-    if not kv_splits and not readout_tokens and stage_events is None:
+def _opts(kv_splits, readout_workgroups, stage_events):
+    if not kv_splits and not readout_workgroups and stage_events is None:
         return None
     o = LaunchOpts()
     o.kv_splits = int(kv_splits or 0)
-    o.readout_tokens = int(readout_tokens or 0)
+    o.readout_workgroups = int(readout_workgroups or 0)
     if stage_events is not None:
         o.stage_events = stage_events.as_ctypes()
     return o
 
 
 def chunk_forward(q, k, v, state_in, out=None, state_out=None, eps=DEFAULT_EPS,
-                  out_dtype=torch.float32, kv_splits=0, readout_tokens=0, stage_events=None):
+                  out_dtype=torch.float32, kv_splits=0, readout_workgroups=0, stage_events=None):
     """One block of the block-causal form: returns (out, state_out) with
     state_out = state_in + phi(K)^T V (and + phi(K)^T 1 for z) and every query
     of the block read against state_out.  state_out may be state_in."""
@@ -183,7 +183,7 @@ def chunk_forward(q, k, v, state_in, out=None, state_out=None, eps=DEFAULT_EPS,
     if state_in.shape != state_out.shape or state_in.device != q.device:
         raise ValueError("state_in must match state_out's shape and device")
     B, H, L, d = q.shape
-    o = _opts(kv_splits, readout_tokens, stage_events)
+    o = _opts(kv_splits, readout_workgroups, stage_events)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out), _ptr(state_out),
             B, H, L, d, _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps))
     L_ = lib()
@@ -196,12 +196,12 @@ def chunk_forward(q, k, v, state_in, out=None, state_out=None, eps=DEFAULT_EPS,
 
 
 def global_forward(q, k, v, out=None, state_out=None, eps=DEFAULT_EPS,
-                   out_dtype=torch.float32, kv_splits=0, readout_tokens=0, stage_events=None):
+                   out_dtype=torch.float32, kv_splits=0, readout_workgroups=0, stage_events=None):
     """Global (non-causal) linear attention: returns (out, state_out) where
     state_out holds the global (S, z)."""
     out, state_out = _prepare(q, k, v, out, out_dtype, state_out)
     B, H, L, d = q.shape
-    o = _opts(kv_splits, readout_tokens, stage_events)
+    o = _opts(kv_splits, readout_workgroups, stage_events)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_out),
             B, H, L, d, _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps))
     L_ = lib()
@@ -214,11 +214,11 @@ def global_forward(q, k, v, out=None, state_out=None, eps=DEFAULT_EPS,
 
 
 def plan(B, H, L, d, in_dtype=torch.bfloat16, out_dtype=torch.float32, kv_splits=0,
-         readout_tokens=0):
-    """(kv_splits, readout_tokens_per_workgroup) the library would use."""
+         readout_workgroups=0):
+    """(kv_splits, readout_workgroups) the library would use."""
     s, t = ctypes.c_int(), ctypes.c_int()
     _check(lib().la_plan(B, H, L, d, _DTYPE[in_dtype], _DTYPE[out_dtype], int(kv_splits),
-                         int(readout_tokens), ctypes.byref(s), ctypes.byref(t)), "la_plan")
+                         int(readout_workgroups), ctypes.byref(s), ctypes.byref(t)), "la_plan")
     return s.value, t.value
 
 

@@ -48,6 +48,23 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two floats -> bfloat16 hi/lo pairs, packed the way an MFMA operand holds
+// consecutive k elements: *hi = {bf16(x0), bf16(x1)}, *lo = {bf16(x0 - hi0),
+// bf16(x1 - hi1)}.  hi + lo carries 16 significant bits of each value.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t* hi, uint32_t* lo) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  const bf16x2 h = __builtin_convertvector(f32x2v{x0, x1}, bf16x2);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+  const float h0 = __uint_as_float(hb << 16), h1 = __uint_as_float(hb & 0xFFFF0000u);
+  const bf16x2 l = __builtin_convertvector(f32x2v{x0 - h0, x1 - h1}, bf16x2);
+  *hi = hb;
+  *lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// 1/x with v_rcp_f32 (1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 __device__ __forceinline__ float from_bf16(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }

@@ -22,9 +22,12 @@ constexpr int kKvTargetWorkgroups = 512;
 // A split should carry at least this many tokens per (d + 1) so that its
 // partial (d*d + d floats) stays small next to the K/V bytes it reads.
 constexpr int kKvMinTokensPerFeature = 8;
-// Readout workgroups the planner aims for: four per compute unit, each with a
-// contiguous token range of one head, so the state is staged into LDS once
-// per workgroup (measured best at the 720p chunk among 512..4736).
+// Readout workgroups the planner aims for.  The sweep readout (bf16, d <= 64)
+// runs three waves per SIMD: 768 workgroups of four waves fill a 256-CU
+// MI355X once.  The per-head readout (d = 128, float32) gives each workgroup a
+// contiguous token range of one head; 1024 was measured best at the 720p
+// shape among 512..4736.
+constexpr int kSweepWorkgroups = 768;
 constexpr int kReadoutTargetWorkgroups = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -38,10 +41,13 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 int elem_size(int dt) { return dt == LA_BF16 ? 2 : 4; }
 
 struct Plan {
-  int splits;       // 0 when L == 0
-  int tps;          // tokens per split
-  int kv_tile;      // tokens per KV tile
-  int readout_tpw;  // tokens per readout workgroup
+  int splits;          // 0 when L == 0
+  int tps;             // tokens per split
+  int kv_tile;         // tokens per KV tile
+  bool sweep;          // readout_sweep_bf16 (else the per-head readout)
+  int readout_tpw;     // per-head readout: tokens per workgroup
+  int readout_wgs;     // readout workgroups in the grid
+  int units_per_head;  // sweep readout: four-tile units per (b, h)
 };
 
 int check_shape(int B, int H, int L, int d, int in_dt, int out_dt) {
@@ -60,21 +66,32 @@ Plan make_plan(int B, int H, int L, int d, int in_dt, int out_dt, int request,
   Plan p{};
   p.kv_tile = in_dt == LA_BF16 ? 64 : 16;
   const long long bhc = static_cast<long long>(B) * H;
-  // readout workgroup tile: four waves x one wave tile (bf16), or 128 tokens
-  const int ro_unit = in_dt == LA_BF16 ? 4 * (d == 128 ? 32 : 16 * LA_READOUT_ROWS) : 128;
-  long long tpw = readout_request;
-  if (tpw <= 0) {
-    const long long per_head = (kReadoutTargetWorkgroups + bhc - 1) / bhc;
-    tpw = (L + per_head - 1) / per_head;
+  p.sweep = in_dt == LA_BF16 && d <= 64;
+  if (p.sweep) {
+    constexpr int unit = 4 * 16 * LA_READOUT_ROWS;
+    p.units_per_head = (L + unit - 1) / unit;
+    long long wgs = readout_request > 0 ? readout_request : kSweepWorkgroups;
+    const long long most = bhc * p.units_per_head;
+    if (wgs > most) wgs = most;
+    if (wgs < 1) wgs = 1;
+    p.readout_wgs = static_cast<int>(wgs);
+    p.readout_tpw = 0;
+  } else {
+    // workgroup tile: four waves x one wave tile (bf16 d = 128), or 128 tokens
+    const int ro_unit = in_dt == LA_BF16 ? 4 * 32 : 128;
+    const long long target = readout_request > 0 ? readout_request : kReadoutTargetWorkgroups;
+    const long long per_head = (target + bhc - 1) / bhc;
+    long long tpw = (L + per_head - 1) / per_head;
+    if (tpw < 1) tpw = 1;
+    tpw = (tpw + ro_unit - 1) / ro_unit * ro_unit;
+    p.readout_tpw = static_cast<int>(tpw);
+    p.readout_wgs = static_cast<int>(((L + tpw - 1) / tpw) * bhc);
+    p.units_per_head = 0;
   }
-  if (tpw < 1) tpw = 1;
-  tpw = (tpw + ro_unit - 1) / ro_unit * ro_unit;
-  const long long whole = (static_cast<long long>(L) + ro_unit - 1) / ro_unit * ro_unit;
-  if (tpw > whole && whole > 0) tpw = whole;
-  p.readout_tpw = static_cast<int>(tpw);
   if (L == 0) {
     p.splits = 0;
     p.tps = 0;
+    p.readout_wgs = 0;
     return p;
   }
   const int ntiles = (L + p.kv_tile - 1) / p.kv_tile;
@@ -121,6 +138,19 @@ int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int
 template <int D>
 int launch_readout(const Plan& p, const void* q, int in_dt, int out_dt, int B, int H, int L,
                    const float* state, void* out, float eps, hipStream_t stream) {
+  if constexpr (D <= 64) {
+    if (p.sweep) {
+      const uint16_t* qq = static_cast<const uint16_t*>(q);
+      const int total = B * H * p.units_per_head;
+      if (out_dt == LA_BF16)
+        la::readout_sweep_bf16<D, true><<<p.readout_wgs, la::kBlock, 0, stream>>>(
+            qq, state, out, L, p.units_per_head, total, eps);
+      else
+        la::readout_sweep_bf16<D, false><<<p.readout_wgs, la::kBlock, 0, stream>>>(
+            qq, state, out, L, p.units_per_head, total, eps);
+      return launched();
+    }
+  }
   const dim3 grid((L + p.readout_tpw - 1) / p.readout_tpw, H, B);
   if (in_dt == LA_BF16) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -205,7 +235,7 @@ int forward(const void* q, const void* k, const void* v, const float* state_in, 
   if (state_in != state_out && overlaps(state_in, st_bytes, state_out, st_bytes)) return LA_E_ALIAS;
 
   const Plan p = make_plan(B, H, L, d, in_dt, out_dt, opts ? opts->kv_splits : 0,
-                           opts ? opts->readout_tokens : 0);
+                           opts ? opts->readout_workgroups : 0);
   switch (d) {
     case 32:
       return run<32>(p, q, k, v, state_in, out, state_out, B, H, L, in_dt, out_dt, eps, opts, stream);
@@ -262,13 +292,14 @@ int la_global_forward_ex(const void* q, const void* k, const void* v, void* out,
 }
 
 int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_request,
-            int readout_tokens_request, int* kv_splits, int* readout_tokens) {
+            int readout_workgroups_request, int* kv_splits, int* readout_workgroups) {
   const int rc = check_shape(B, H, L, d, in_dt, out_dt);
   if (rc != LA_OK) return rc;
-  if (kv_splits == nullptr || readout_tokens == nullptr) return LA_E_INVAL;
-  const Plan p = make_plan(B, H, L, d, in_dt, out_dt, kv_splits_request, readout_tokens_request);
+  if (kv_splits == nullptr || readout_workgroups == nullptr) return LA_E_INVAL;
+  const Plan p = make_plan(B, H, L, d, in_dt, out_dt, kv_splits_request,
+                           readout_workgroups_request);
   *kv_splits = p.splits;
-  *readout_tokens = p.readout_tpw;
+  *readout_workgroups = p.readout_wgs;
   return LA_OK;
 }
 

@@ -24,6 +24,10 @@
 #ifndef LA_READOUT_ROWS
 #define LA_READOUT_ROWS 2
 #endif
+// Sweep readout: consecutive wave tiles of one head a wave takes per visit.
+#ifndef LA_SWEEP_RUN
+#define LA_SWEEP_RUN 1
+#endif
 
 namespace la {
 
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(kBlock, ReadoutShape<D>::MIN_WAVES) void readout_bf
       for (int i = 0; i < 4; ++i) {
         const int tok = tile + 16 * r + 4 * i + g;
         if (tok >= te) continue;
-        const float inv = 1.0f / (accz[r][i] + eps);
+        const float inv = fast_rcp(accz[r][i] + eps);
         const size_t row0 = static_cast<size_t>(bh * L + tok) * D;
 #pragma unroll
         for (int gr = 0; gr < Sh::GRP; ++gr) {
@@ -222,6 +226,186 @@ __global__ __launch_bounds__(kBlock, ReadoutShape<D>::MIN_WAVES) void readout_bf
 #pragma unroll
         for (int s = 0; s < Sh::KS; ++s) a[r][s] = an[r][s];
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sweep schedule for d <= 64 (the bandwidth path).
+//
+// The output is two thirds of the readout's HBM traffic, and HBM write
+// bandwidth on MI355X depends on how many far-apart regions are written at
+// once: measured with this access pattern at the 720p shape, a single
+// window that the whole GPU sweeps through sustains ~5.8 TB/s, while one
+// contiguous range per workgroup (or per head) sustains ~5.0 TB/s.  So the
+// work is cut into units of four adjacent wave tiles (4 x 16R tokens of one
+// (b, h)), enumerated head-major, and workgroup k takes units k, k + G,
+// k + 2G, ...: at any moment the GPU works on G adjacent units.
+//
+// Consecutive units of a workgroup belong to different heads, so each unit
+// rebuilds the B operands (S and z as bf16 hi/lo pairs) from the float32
+// state in L2.  Wave s < d/32 converts k-step s: with the column placement
+// pi above, lane (n, g) reads S[32s + 8g + j][W n .. W n + W-1], j = 0..7, as
+// W-float vectors (each load instruction reads four whole state rows), and
+// the pairs (j, j+1) convert straight into packed operand words.  The
+// operands go to LDS in lane order (one conflict-free 16-byte write per
+// lane and operand), double-buffered so one barrier per unit suffices; the
+// next unit's state and queries are loaded before this unit's MFMAs.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* __restrict__ q,
+                                                                const float* __restrict__ state,
+                                                                void* __restrict__ out, int L,
+                                                                int units_per_head, int total_units,
+                                                                float eps) {
+  using Sh = ReadoutShape<D>;
+  static_assert(D <= 64 && Sh::GRP == 1, "sweep readout covers d = 32 and d = 64");
+  constexpr int E = D * D + D;
+  constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, R = Sh::R;
+  constexpr int NF = KS * (NBK + 1) * 2;  // operands: [k-step][column block, z last][hi, lo]
+  using vecW = float __attribute__((ext_vector_type(W)));
+  __shared__ uint4 frag[2][NF][kWave];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  const int tok_a = 4 * (n & 3) + (n >> 2);
+  auto fi = [](int s, int c, int p) { return (s * (NBK + 1) + c) * 2 + p; };
+
+  vecW sraw[8];
+  f32x4 zraw[2];
+  // state rows of k-step `wave` (producer waves only)
+  auto load_state = [&](int bh) {
+    if (wave < KS) {
+      const float* st = state + static_cast<size_t>(bh) * E;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        sraw[j] = *reinterpret_cast<const vecW*>(st + (32 * wave + 8 * g + j) * D + W * n);
+      zraw[0] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * wave + 8 * g);
+      zraw[1] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * wave + 8 * g + 4);
+    }
+  };
+  auto build = [&](int buf) {
+    if (wave < KS) {
+#pragma unroll
+      for (int c = 0; c < NBK; ++c) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) split_bf16x2(sraw[j][c], sraw[j + 1][c], &h[j / 2], &l[j / 2]);
+        frag[buf][fi(wave, c, 0)][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+        frag[buf][fi(wave, c, 1)][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+      }
+      uint32_t h[4], l[4];
+      split_bf16x2(zraw[0][0], zraw[0][1], &h[0], &l[0]);
+      split_bf16x2(zraw[0][2], zraw[0][3], &h[1], &l[1]);
+      split_bf16x2(zraw[1][0], zraw[1][1], &h[2], &l[2]);
+      split_bf16x2(zraw[1][2], zraw[1][3], &h[3], &l[3]);
+      frag[buf][fi(wave, NBK, 0)][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+      frag[buf][fi(wave, NBK, 1)][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+  };
+  auto load_a = [&](uint4 (&a)[R][KS], int bh, int t0) {
+    const uint4* qb = reinterpret_cast<const uint4*>(q + static_cast<size_t>(bh) * L * D);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int tok = t0 + 16 * r + tok_a;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        a[r][s] = tok < L ? relu_bf16x8(load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g))
+                          : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto consume = [&](int buf, const uint4 (&a)[R][KS], int bh, int t0) {
+    f32x4 acc[R][NBK];
+    f32x4 accz[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NBK; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 zh = frag[buf][fi(s, NBK, 0)][lane], zl = frag[buf][fi(s, NBK, 1)][lane];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        accz[r] = mfma_16x16x32(a[r][s], zh, accz[r]);
+        accz[r] = mfma_16x16x32(a[r][s], zl, accz[r]);
+      }
+#pragma unroll
+      for (int c = 0; c < NBK; ++c) {
+        const uint4 bh16 = frag[buf][fi(s, c, 0)][lane], bl16 = frag[buf][fi(s, c, 1)][lane];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          acc[r][c] = mfma_16x16x32(a[r][s], bh16, acc[r][c]);
+          acc[r][c] = mfma_16x16x32(a[r][s], bl16, acc[r][c]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * r + 4 * i + g;
+        if (tok >= L) continue;
+        const float inv = fast_rcp(accz[r][i] + eps);
+        const size_t row0 = (static_cast<size_t>(bh) * L + tok) * D;
+        const int col = W * n;
+        if constexpr (W == 4) {
+          const float o0 = acc[r][0][i] * inv, o1 = acc[r][1][i] * inv;
+          const float o2 = acc[r][2][i] * inv, o3 = acc[r][3][i] * inv;
+          if constexpr (OUT_BF16) {
+            const u32x2 pk = {pack2(to_bf16(o0), to_bf16(o1)), pack2(to_bf16(o2), to_bf16(o3))};
+            store_out(pk, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + row0 + col));
+          } else {
+            store_out(f32x4{o0, o1, o2, o3},
+                      reinterpret_cast<f32x4*>(static_cast<float*>(out) + row0 + col));
+          }
+        } else {
+          const float o0 = acc[r][0][i] * inv, o1 = acc[r][1][i] * inv;
+          if constexpr (OUT_BF16) {
+            store_out(pack2(to_bf16(o0), to_bf16(o1)),
+                      reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + row0 + col));
+          } else {
+            store_out(f32x2{o0, o1}, reinterpret_cast<f32x2*>(static_cast<float*>(out) + row0 + col));
+          }
+        }
+      }
+  };
+
+  // The unit index is uniform across the workgroup, so every wave takes the
+  // same number of barriers; waves whose tile lies past the end of a head
+  // load zeros and store nothing.
+  int unit = blockIdx.x;
+  if (unit >= total_units) return;
+  int bh = unit / units_per_head;
+  int t0 = ((unit - bh * units_per_head) * 4 + wave) * Sh::TILE;
+  uint4 a[R][KS];
+  load_state(bh);
+  load_a(a, bh, t0);
+  for (int i = 0;; ++i) {
+    const int buf = i & 1;
+    // buf was last read before the previous iteration's barrier
+    build(buf);
+    __syncthreads();
+    const int next = unit + gridDim.x;
+    const bool more = next < total_units;
+    int nbh = 0, nt0 = 0;
+    uint4 an[R][KS];
+    if (more) {
+      nbh = next / units_per_head;
+      nt0 = ((next - nbh * units_per_head) * 4 + wave) * Sh::TILE;
+      load_state(nbh);
+      load_a(an, nbh, nt0);
+    }
+    consume(buf, a, bh, t0);
+    if (!more) break;
+    unit = next;
+    bh = nbh;
+    t0 = nt0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[r][s] = an[r][s];
   }
 }
 

@@ -119,17 +119,18 @@ int la_global_forward(const void* q, const void* k, const void* v,
  *                   of 64-token tiles] and to what the scratch in `out` holds.
  *                   Results differ between split counts only by float32
  *                   summation order.
- *   readout_tokens: tokens per readout workgroup; 0 lets the library choose.
- *                   A request is rounded up to the readout's workgroup tile
- *                   (256 tokens, or 128 at d = 128; 128 for float32 inputs).
- *                   Results do not depend on it.
+ *   readout_workgroups: workgroups of the readout grid; 0 lets the library
+ *                   choose.  At d <= 64 with bfloat16 inputs every wave
+ *                   sweeps 32-token tiles of all heads, and the request is
+ *                   clamped to one wave per tile; otherwise it is rounded to
+ *                   whole workgroups per (b, h).  Results do not depend on it.
  *   stage_events  : NULL, or 4 caller-created events recorded on `stream`
  *                   before the KV reduction, before the split reduce, before
  *                   the readout, and after the readout (for timing).
  */
 typedef struct la_launch_opts {
   int kv_splits;
-  int readout_tokens;
+  int readout_workgroups;
   hipEvent_t* stage_events;
 } la_launch_opts;
 
@@ -145,13 +146,13 @@ int la_global_forward_ex(const void* q, const void* k, const void* v,
 
 /*
  * la_plan - the launch shape a forward call with these arguments (and the
- * given kv_splits / readout_tokens requests, 0 = library's choice) would use,
- * with no device work: *kv_splits receives the split count (1 = the KV
+ * given kv_splits / readout_workgroups requests, 0 = library's choice) would
+ * use, with no device work: *kv_splits receives the split count (1 = the KV
  * kernel writes state_out directly and the split reduce is skipped),
- * *readout_tokens the tokens per readout workgroup.  Returns a status code.
+ * *readout_workgroups the readout grid size.  Returns a status code.
  */
 int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_request,
-            int readout_tokens_request, int* kv_splits, int* readout_tokens);
+            int readout_workgroups_request, int* kv_splits, int* readout_workgroups);
 
 /* Static text for a status code. */
 const char* la_status_string(int status);

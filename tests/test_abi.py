@@ -116,8 +116,12 @@ def test_plan_shapes():
     assert la.plan(1, 1, 100, 64, kv_splits=50)[0] == 1
     assert la.plan(1, 1, 6400, 64, kv_splits=7)[0] == 7
     assert la.plan(1, 1, 0, 64)[0] == 0
-    # readout: 32 workgroups per head at 720p, 128-token multiples
-    assert la.plan(1, 32, 75600, 64)[1] == 2432
-    assert la.plan(1, 32, 75600, 64, readout_tokens=300)[1] == 384
+    # readout: the sweep grid (768 workgroups) at 720p; a request is honoured
+    # up to one workgroup per 128-token unit
+    assert la.plan(1, 32, 75600, 64)[1] == 768
+    assert la.plan(1, 32, 75600, 64, readout_workgroups=300)[1] == 300
+    assert la.plan(1, 1, 100, 64, readout_workgroups=300)[1] == 1
+    # d = 128 keeps per-head workgroups: 4*16 heads, 4096 tokens -> 16 per head
+    assert la.plan(4, 16, 4096, 128)[1] == 4 * 16 * 16
     with pytest.raises(la.LinAttnError):
         la.plan(1, 1, 10, 48)
