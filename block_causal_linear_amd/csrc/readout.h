@@ -134,15 +134,16 @@ __global__ __launch_bounds__(kBlock, ReadoutShape<D>::MIN_WAVES) void readout_bf
   const uint4* qb = reinterpret_cast<const uint4*>(q + bh * static_cast<size_t>(L) * D);
   const int tok_a = 4 * (n & 3) + (n >> 2);  // token (within a row block) of A row n
 
-  // A operands of one wave tile: phi(q) rows, zero past the end of the range.
+  // A operands of one wave tile: phi(q) rows.  Rows past the end of the
+  // range read row te - 1 instead (their outputs are never stored), so the
+  // loads carry no branch and no wait right after issue.
   auto load_a = [&](uint4 (&a)[Sh::R][Sh::KS], int tile) {
 #pragma unroll
     for (int r = 0; r < Sh::R; ++r) {
-      const int tok = tile + 16 * r + tok_a;
+      const int tok = min(tile + 16 * r + tok_a, te - 1);
 #pragma unroll
       for (int s = 0; s < Sh::KS; ++s)
-        a[r][s] = tok < te ? relu_bf16x8(load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g))
-                           : make_uint4(0, 0, 0, 0);
+        a[r][s] = load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g);
     }
   };
 
@@ -158,6 +159,10 @@ __global__ __launch_bounds__(kBlock, ReadoutShape<D>::MIN_WAVES) void readout_bf
     const int next = tile + 4 * Sh::TILE;
     if (next < te) load_a(an, next);
 
+#pragma unroll
+    for (int r = 0; r < Sh::R; ++r)
+#pragma unroll
+      for (int s = 0; s < Sh::KS; ++s) a[r][s] = relu_bf16x8(a[r][s]);
     f32x4 acc[Sh::R][Sh::NBK];
     f32x4 accz[Sh::R];
 #pragma unroll
@@ -243,13 +248,18 @@ __global__ __launch_bounds__(kBlock, ReadoutShape<D>::MIN_WAVES) void readout_bf
 //
 // Consecutive units of a workgroup belong to different heads, so each unit
 // rebuilds the B operands (S and z as bf16 hi/lo pairs) from the float32
-// state in L2.  Wave s < d/32 converts k-step s: with the column placement
-// pi above, lane (n, g) reads S[32s + 8g + j][W n .. W n + W-1], j = 0..7, as
-// W-float vectors (each load instruction reads four whole state rows), and
-// the pairs (j, j+1) convert straight into packed operand words.  The
-// operands go to LDS in lane order (one conflict-free 16-byte write per
-// lane and operand), double-buffered so one barrier per unit suffices; the
-// next unit's state and queries are loaded before this unit's MFMAs.
+// state in L2.  The d/32 x d/16 (k-step, column block) pairs are shared out
+// over the four waves (two each at d = 64): with the column placement pi
+// above, a wave's pairs are adjacent state columns, so lane (n, g) reads
+// S[32s + 8g + j][W n + c0 .. W n + c0 + PW - 1], j = 0..7, as one vector,
+// and rows (j, j+1) convert straight into packed operand words.  The
+// operands go to LDS in lane order (one conflict-free 16-byte write per lane
+// and operand), double-buffered so one barrier per unit suffices.
+//
+// Every wave issues the same loads in the same order in every iteration
+// (the next unit's state and queries, before this unit's MFMAs; on the last
+// unit the loads repeat it): with no divergent control flow around the loads
+// the compiler's wait counts stay exact, and the prefetch really overlaps.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* __restrict__ q,
                                                                 const float* __restrict__ state,
@@ -260,8 +270,12 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
   static_assert(D <= 64 && Sh::GRP == 1, "sweep readout covers d = 32 and d = 64");
   constexpr int E = D * D + D;
   constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, R = Sh::R;
+  constexpr int NW = kBlock / kWave;
   constexpr int NF = KS * (NBK + 1) * 2;  // operands: [k-step][column block, z last][hi, lo]
-  using vecW = float __attribute__((ext_vector_type(W)));
+  constexpr int PAIRS = KS * NBK;         // (k-step, column block) pairs
+  constexpr int PW = PAIRS >= NW ? PAIRS / NW : 1;  // pairs per wave
+  static_assert(PAIRS % PW == 0 && NBK % PW == 0, "pair split");
+  using vecP = float __attribute__((ext_vector_type(PW)));
   __shared__ uint4 frag[2][NF][kWave];
 
   const int tid = threadIdx.x;
@@ -271,50 +285,59 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
   const int tok_a = 4 * (n & 3) + (n >> 2);
   auto fi = [](int s, int c, int p) { return (s * (NBK + 1) + c) * 2 + p; };
 
-  vecW sraw[8];
+  // this wave's pairs: k-step ps, column blocks pc0 .. pc0 + PW - 1
+  const bool producer = wave * PW < PAIRS;
+  const int p0 = producer ? wave * PW : 0;
+  const int ps = p0 / NBK, pc0 = p0 % NBK;
+
+  vecP sraw[8];
   f32x4 zraw[2];
-  // state rows of k-step `wave` (producer waves only)
   auto load_state = [&](int bh) {
-    if (wave < KS) {
-      const float* st = state + static_cast<size_t>(bh) * E;
+    const float* st = state + static_cast<size_t>(bh) * E;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        sraw[j] = *reinterpret_cast<const vecW*>(st + (32 * wave + 8 * g + j) * D + W * n);
-      zraw[0] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * wave + 8 * g);
-      zraw[1] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * wave + 8 * g + 4);
-    }
+    for (int j = 0; j < 8; ++j)
+      sraw[j] = *reinterpret_cast<const vecP*>(st + (32 * ps + 8 * g + j) * D + W * n + pc0);
+    zraw[0] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * ps + 8 * g);
+    zraw[1] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * ps + 8 * g + 4);
   };
   auto build = [&](int buf) {
-    if (wave < KS) {
+    if (!producer) return;
 #pragma unroll
-      for (int c = 0; c < NBK; ++c) {
-        uint32_t h[4], l[4];
+    for (int c = 0; c < PW; ++c) {
+      uint32_t h[4], l[4];
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) split_bf16x2(sraw[j][c], sraw[j + 1][c], &h[j / 2], &l[j / 2]);
-        frag[buf][fi(wave, c, 0)][lane] = make_uint4(h[0], h[1], h[2], h[3]);
-        frag[buf][fi(wave, c, 1)][lane] = make_uint4(l[0], l[1], l[2], l[3]);
-      }
+      for (int j = 0; j < 8; j += 2) split_bf16x2(sraw[j][c], sraw[j + 1][c], &h[j / 2], &l[j / 2]);
+      frag[buf][fi(ps, pc0 + c, 0)][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+      frag[buf][fi(ps, pc0 + c, 1)][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+    if (pc0 == 0) {
       uint32_t h[4], l[4];
       split_bf16x2(zraw[0][0], zraw[0][1], &h[0], &l[0]);
       split_bf16x2(zraw[0][2], zraw[0][3], &h[1], &l[1]);
       split_bf16x2(zraw[1][0], zraw[1][1], &h[2], &l[2]);
       split_bf16x2(zraw[1][2], zraw[1][3], &h[3], &l[3]);
-      frag[buf][fi(wave, NBK, 0)][lane] = make_uint4(h[0], h[1], h[2], h[3]);
-      frag[buf][fi(wave, NBK, 1)][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+      frag[buf][fi(ps, NBK, 0)][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+      frag[buf][fi(ps, NBK, 1)][lane] = make_uint4(l[0], l[1], l[2], l[3]);
     }
   };
+  // Query rows past the end of the head load row L - 1 instead: an MFMA
+  // output row depends only on its own A row, and those rows are never
+  // stored.  phi is applied where the operand is used.
   auto load_a = [&](uint4 (&a)[R][KS], int bh, int t0) {
     const uint4* qb = reinterpret_cast<const uint4*>(q + static_cast<size_t>(bh) * L * D);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int tok = t0 + 16 * r + tok_a;
+      const int tok = min(t0 + 16 * r + tok_a, L - 1);
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
-        a[r][s] = tok < L ? relu_bf16x8(load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g))
-                          : make_uint4(0, 0, 0, 0);
+      for (int s = 0; s < KS; ++s) a[r][s] = load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g);
     }
   };
-  auto consume = [&](int buf, const uint4 (&a)[R][KS], int bh, int t0) {
+  auto consume = [&](int buf, const uint4 (&qraw)[R][KS], int bh, int t0) {
+    uint4 a[R][KS];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[r][s] = relu_bf16x8(qraw[r][s]);
     f32x4 acc[R][NBK];
     f32x4 accz[R];
 #pragma unroll
@@ -374,7 +397,7 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
 
   // The unit index is uniform across the workgroup, so every wave takes the
   // same number of barriers; waves whose tile lies past the end of a head
-  // load zeros and store nothing.
+  // compute on clamped rows and store nothing.
   int unit = blockIdx.x;
   if (unit >= total_units) return;
   int bh = unit / units_per_head;
@@ -389,14 +412,12 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
     __syncthreads();
     const int next = unit + gridDim.x;
     const bool more = next < total_units;
-    int nbh = 0, nt0 = 0;
+    const int nu = more ? next : unit;
+    const int nbh = nu / units_per_head;
+    const int nt0 = ((nu - nbh * units_per_head) * 4 + wave) * Sh::TILE;
     uint4 an[R][KS];
-    if (more) {
-      nbh = next / units_per_head;
-      nt0 = ((next - nbh * units_per_head) * 4 + wave) * Sh::TILE;
-      load_state(nbh);
-      load_a(an, nbh, nt0);
-    }
+    load_state(nbh);
+    load_a(an, nbh, nt0);
     consume(buf, a, bh, t0);
     if (!more) break;
     unit = next;
