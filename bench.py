@@ -14,7 +14,13 @@ the library's stream inside the timed region; `cpu_baseline` times the fp64
 oracle on the same workload on the host.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --workload {chunk720p,global480p,global720p,stream480p,longhorizon}
     python bench.py --copy-calibration     # plain copy kernel for counter scaling
+
+The other workloads (one JSON line each, same fields) time the global form at
+the 480p and 720p latents, the 12-chunk 1-minute 480p stream and the 40-chunk
+d = 128 long-horizon stream (one step = the whole stream, state resident);
+their inputs are seeded normals drawn on the GPU.
 """
 
 import argparse
@@ -48,13 +54,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def bytes_alg(B, H, L, d, s_in=2, s_out=4):
-    """Algorithmic HBM bytes of one chunk call and of each stage."""
+def bytes_alg(B, H, L, d, s_in=2, s_out=4, with_state_in=True):
+    """Algorithmic HBM bytes of one call and of its KV and readout stages."""
     tok = B * H * L * d
     st = B * H * (d * d + d) * 4
     kv = 2 * tok * s_in                  # read K, V once
     readout = tok * (s_in + s_out) + st  # read Q, write O, read the updated state
-    call = 3 * tok * s_in + tok * s_out + 2 * st
+    call = 3 * tok * s_in + tok * s_out + (2 if with_state_in else 1) * st
     return call, kv, readout
 
 
@@ -116,6 +122,100 @@ def copy_calibration(steps):
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": steps}))
 
 
+OTHER = {
+    "global480p": 2,
+    "global720p": 3,
+    "stream480p": 4,
+    "longhorizon": 5,
+}
+
+
+def bench_other(args):
+    """One step = one global call, or one whole stream of chunk calls with the
+    state resident and reset at the start of the step."""
+    import torch
+
+    import block_causal_linear_amd as la
+    import workloads
+
+    w = workloads.WORKLOADS[OTHER[args.workload]]
+    B, H, L, d, C = w.B, w.H, w.L, w.d, w.chunks
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(1000 + w.cid)
+    log(f"drawing inputs on the GPU for {w.name} (B={B} H={H} L={L} d={d} chunks={C})")
+
+    def draw():
+        x = torch.randn((B, H, L, d), generator=gen, device=dev)
+        if w.scale != 1.0:
+            x.mul_(w.scale)
+        if w.outlier_frac > 0:
+            rows = torch.rand((B, H, L, 1), generator=gen, device=dev) < w.outlier_frac
+            x = torch.where(rows, x * w.outlier_scale, x)
+        return x.to(torch.bfloat16)
+
+    chunks = [tuple(draw() for _ in range(3)) for _ in range(C)]
+    out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
+    state = torch.empty((B, H, d * d + d), dtype=torch.float32, device=dev)
+    splits, rwg = la.plan(B, H, L, d, kv_splits=args.kv_splits)
+    log(f"plan: kv_splits={splits} readout_workgroups={rwg}")
+
+    # stage events on every `event_every`-th call (counted over all calls)
+    every = max(1, args.event_every)
+    steps = max(1, args.steps // C) if C > 1 else args.steps
+    evs = {c: la.StageEvents() for c in range(0, steps * C, every)}
+
+    def step(i=None):
+        base = None if i is None else i * C
+        if w.form == "global":
+            q, k, v = chunks[0]
+            la.global_forward(q, k, v, out=out, state_out=state, eps=workloads.EPS,
+                              kv_splits=args.kv_splits,
+                              stage_events=None if base is None else evs.get(base))
+            return
+        la.state_reset(state)
+        for n, (q, k, v) in enumerate(chunks):
+            la.chunk_forward(q, k, v, state, out=out, state_out=state, eps=workloads.EPS,
+                             kv_splits=args.kv_splits,
+                             stage_events=None if base is None else evs.get(base + n))
+
+    for _ in range(max(1, args.warmup // C)):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    stages = np.array([e.elapsed_ms() for e in evs.values()])
+    for e in evs.values():
+        e.close()
+    kv_ms, red_ms, ro_ms = (float(x) for x in stages.mean(axis=0))
+    call_b, kv_b, ro_b = bytes_alg(B, H, L, d, with_state_in=(w.form != "global"))
+    tokens = B * L * C
+    ro_kernel = f"readout_sweep_bf16<{d}>" if d <= 64 else f"readout_bf16<{d}>"
+    result = {
+        "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "form": w.form, "B": B, "H": H, "d": d, "L": L,
+                   "calls_per_step": C, "q_k_v": "bf16", "out": "f32", "state": "f32",
+                   "kv_splits": splits, "readout_workgroups": rwg},
+        "hbm_frac": call_b * C / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "us_per_call": ms * 1e3 / C,
+        "roofline": {"bound": "hbm", "kernel": ro_kernel,
+                     "achieved": ro_b / (ro_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": ro_b / (ro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_alg_per_launch": ro_b, "launch_us": ro_ms * 1e3},
+        "stages_us": {"kv_partial": kv_ms * 1e3, "state_reduce": red_ms * 1e3,
+                      "readout": ro_ms * 1e3, "event_samples": int(stages.shape[0])},
+        "kv_partial_GBs": kv_b / (kv_ms * 1e-3) / 1e9,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +224,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
+    ap.add_argument("--workload", default="chunk720p",
+                    choices=["chunk720p", "global480p", "global720p", "stream480p", "longhorizon"])
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-stage HIP events on every N-th timed step")
     ap.add_argument("--plain-steps", type=int, default=0,
@@ -143,6 +245,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
+        return
+    if args.workload != "chunk720p":
+        bench_other(args)
         return
 
     w = workloads.CHUNK_720P

@@ -20,50 +20,84 @@ namespace la {
 // The contraction runs over tokens, but K and V are token-major in HBM, so
 // an MFMA operand (8 consecutive tokens of one feature per lane) is a column
 // of the tile.  Each 64-token tile of K and V is loaded with coalesced 16-B
-// loads, phi is applied to K in registers (v_pk_max_i16), and the tile is
-// written to LDS token-major; operands are then gathered with 16-bit LDS
-// reads.  The 16-B unit index inside a token row is XOR-swizzled by the
-// row's 8-token group so the four lane groups of a wavefront (which read
-// rows 8 apart) land on different LDS banks.
+// loads (two tiles ahead, in registers), phi is applied to K in registers
+// (v_pk_max_i16), and the tile is written to LDS token-major.  Operands are
+// read back with the gfx950 transposing LDS read ds_read_b64_tr_b16: within
+// each 16-lane group, lane i receives element (i mod 4) of the 8-byte chunks
+// that lanes 4k + i/4 (k = 0..3) point at.  When lane j of the group points
+// at features f0 + 4 (j mod 4) .. +3 of token t0 + j/4, lane i receives
+// tokens t0 .. t0 + 3 of feature f0 + i; two such reads give the eight
+// consecutive tokens of an operand.  The 16-byte unit index inside a token
+// row is XOR-swizzled by 2 (t mod 4), so the four token rows one read
+// touches fall on different LDS banks.
 //
-// Work split in a workgroup: wave (wi, wj) owns the output quadrant
-// rows [wi*d/2, +d/2) x cols [wj*d/2, +d/2); waves with wj == 0 also
-// accumulate z with a second MFMA against an all-ones B operand.
+// Work split in a workgroup of WR x WC waves: wave (wi, wj) owns the output
+// block rows [wi d/WR, +d/WR) x cols [wj d/WC, +d/WC); waves with wj == 0
+// also accumulate z with a second MFMA against an all-ones B operand.
 
-template <int D>
+template <int D, int WR, int WC>
 struct KvTile {
+  static constexpr int NT = kWave * WR * WC;  // threads per workgroup
   static constexpr int TT = 64;               // tokens per tile
   static constexpr int UPR = D / 8;           // 16-byte units per token row
   static constexpr int UNITS = TT * UPR;      // units per tensor per tile
-  static constexpr int CPT = UNITS / kBlock;  // units per thread per tensor
-  static_assert(UNITS % kBlock == 0, "tile must split evenly over the workgroup");
+  static constexpr int CPT = UNITS / NT;      // units per thread per tensor
+  static_assert(UNITS % NT == 0, "tile must split evenly over the workgroup");
 };
+
+// Wave layouts: 2 x 2 at d <= 64, 4 x 4 (1024 threads) at d = 128.
+template <int D>
+struct KvWaves {
+  static constexpr int WR = D == 128 ? 4 : 2;
+  static constexpr int WC = D == 128 ? 4 : 2;
+};
+
+template <int D>
+constexpr int kv_threads() {
+  return KvTile<D, KvWaves<D>::WR, KvWaves<D>::WC>::NT;
+}
 
 template <int UPR>
 __device__ __forceinline__ int unit_swizzle(int t) {
-  return (((t >> 3) & 3) * 2) & (UPR - 1);
+  return ((t & 3) * 2) & (UPR - 1);
 }
 
-// Lane's MFMA operand: feature f of tokens ks + 8g + j, j = 0..7.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Lane's MFMA operand: feature f0 + (lane % 16) of tokens ks + 8g .. +7,
+// g = lane / 16, from a token-major swizzled tile.
 template <int UPR>
-__device__ __forceinline__ uint4 tile_column8(const uint16_t* tile, int ks, int f, int g) {
-  const int t = ks + 8 * g;
-  const int unit = (f >> 3) ^ unit_swizzle<UPR>(t);
-  const uint16_t* p = tile + (t * UPR + unit) * 8 + (f & 7);
-  uint32_t w[8];
+__device__ __forceinline__ uint4 tile_column8(const uint16_t* tile, int ks, int f0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int f = f0 + 4 * (j & 3);  // this lane's 4-feature chunk
+  uint4 r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = p[j * UPR * 8];
-  return make_uint4(pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7]));
+  for (int h = 0; h < 2; ++h) {
+    const int t = ks + 8 * g + 4 * h + (j >> 2);
+    const int unit = (f >> 3) ^ unit_swizzle<UPR>(t);
+    const uint16_t* p = tile + (t * UPR + unit) * 8 + (f & 7);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    const uint2 w = __builtin_bit_cast(uint2, v);
+    if (h == 0) {
+      r.x = w.x;
+      r.y = w.y;
+    } else {
+      r.z = w.x;
+      r.w = w.y;
+    }
+  }
+  return r;
 }
 
 template <int D>
-__global__ __launch_bounds__(kBlock) void kv_partial_bf16(const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, int L,
-                                                          int tps, const float* state_in,
-                                                          float* dst) {
-  using T = KvTile<D>;
-  constexpr int QD = D / 2;    // quadrant side
-  constexpr int NB = QD / 16;  // 16x16 blocks per quadrant side
+__global__ __launch_bounds__(kv_threads<D>()) void kv_partial_bf16(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int L, int tps,
+    const float* state_in, float* dst) {
+  constexpr int WR = KvWaves<D>::WR, WC = KvWaves<D>::WC;
+  using T = KvTile<D, WR, WC>;
+  constexpr int BR = D / WR, BC = D / WC;  // output block of one wave
+  constexpr int NR = BR / 16, NC = BC / 16;
   constexpr int E = D * D + D;
   __shared__ uint4 lds[2][2][T::UNITS];  // [buffer][K, V][unit]
 
@@ -78,16 +112,16 @@ __global__ __launch_bounds__(kBlock) void kv_partial_bf16(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wi = wave >> 1, wj = wave & 1;
+  const int wi = wave / WC, wj = wave % WC;
   const int n = lane & 15, g = lane >> 4;
 
-  f32x4 acc[NB][NB];
-  f32x4 accz[NB];
+  f32x4 acc[NR][NC];
+  f32x4 accz[NR];
 #pragma unroll
-  for (int r = 0; r < NB; ++r) {
+  for (int r = 0; r < NR; ++r) {
     accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NB; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 
@@ -98,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void kv_partial_bf16(const uint16_t* __rest
     const int base = t0 + tile * T::TT;
 #pragma unroll
     for (int i = 0; i < T::CPT; ++i) {
-      const int u = tid + kBlock * i;
+      const int u = tid + T::NT * i;
       const int t = u / T::UPR;
       if (base + t < t1) {
         const size_t idx = static_cast<size_t>(base) * T::UPR + u;
@@ -113,7 +147,7 @@ __global__ __launch_bounds__(kBlock) void kv_partial_bf16(const uint16_t* __rest
   auto lstore = [&](const uint4 (&rk)[T::CPT], const uint4 (&rv)[T::CPT], int buf) {
 #pragma unroll
     for (int i = 0; i < T::CPT; ++i) {
-      const int u = tid + kBlock * i;
+      const int u = tid + T::NT * i;
       const int t = u / T::UPR;
       const int c = u % T::UPR;
       const int s = t * T::UPR + (c ^ unit_swizzle<T::UPR>(t));
@@ -126,18 +160,18 @@ __global__ __launch_bounds__(kBlock) void kv_partial_bf16(const uint16_t* __rest
     const uint16_t* lv = reinterpret_cast<const uint16_t*>(lds[buf][1]);
 #pragma unroll
     for (int ks = 0; ks < T::TT; ks += 32) {
-      uint4 a[NB], b[NB];
+      uint4 a[NR], b[NC];
 #pragma unroll
-      for (int r = 0; r < NB; ++r) a[r] = tile_column8<T::UPR>(lk, ks, wi * QD + r * 16 + n, g);
+      for (int r = 0; r < NR; ++r) a[r] = tile_column8<T::UPR>(lk, ks, wi * BR + r * 16, lane);
 #pragma unroll
-      for (int c = 0; c < NB; ++c) b[c] = tile_column8<T::UPR>(lv, ks, wj * QD + c * 16 + n, g);
+      for (int c = 0; c < NC; ++c) b[c] = tile_column8<T::UPR>(lv, ks, wj * BC + c * 16, lane);
 #pragma unroll
-      for (int r = 0; r < NB; ++r)
+      for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int c = 0; c < NB; ++c) acc[r][c] = mfma_16x16x32(a[r], b[c], acc[r][c]);
+        for (int c = 0; c < NC; ++c) acc[r][c] = mfma_16x16x32(a[r], b[c], acc[r][c]);
       if (wj == 0) {
 #pragma unroll
-        for (int r = 0; r < NB; ++r) accz[r] = mfma_16x16x32(a[r], ones, accz[r]);
+        for (int r = 0; r < NR; ++r) accz[r] = mfma_16x16x32(a[r], ones, accz[r]);
       }
     }
   };
@@ -164,23 +198,23 @@ __global__ __launch_bounds__(kBlock) void kv_partial_bf16(const uint16_t* __rest
   float* o = dst + (splits > 1 ? bh * splits + split : bh) * static_cast<size_t>(E);
   const float* si = (splits == 1 && state_in != nullptr) ? state_in + bh * E : nullptr;
 #pragma unroll
-  for (int r = 0; r < NB; ++r)
+  for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int c = 0; c < NB; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ra = wi * QD + r * 16 + 4 * g + i;
-        const int cc = wj * QD + c * 16 + n;
+        const int ra = wi * BR + r * 16 + 4 * g + i;
+        const int cc = wj * BC + c * 16 + n;
         float x = acc[r][c][i];
         if (si) x = si[ra * D + cc] + x;
         o[ra * D + cc] = x;
       }
   if (wj == 0 && n == 0) {
 #pragma unroll
-    for (int r = 0; r < NB; ++r)
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ra = wi * QD + r * 16 + 4 * g + i;
+        const int ra = wi * BR + r * 16 + 4 * g + i;
         float x = accz[r][i];
         if (si) x = si[D * D + ra] + x;
         o[D * D + ra] = x;

@@ -17,11 +17,12 @@ namespace {
 constexpr int kAbiVersion = 1;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
-// MI355X (measured best at the 720p chunk: 16 splits x 32 heads).
+// MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
+// splits x 32 heads), one per compute unit at d = 128 (sixteen waves each).
 constexpr int kKvTargetWorkgroups = 512;
 // A split should carry at least this many tokens per (d + 1) so that its
 // partial (d*d + d floats) stays small next to the K/V bytes it reads.
-constexpr int kKvMinTokensPerFeature = 8;
+constexpr int kKvMinTokensPerFeature = 4;
 // Readout workgroups the planner aims for.  The sweep readout (bf16, d <= 64)
 // runs three waves per SIMD: 768 workgroups of four waves fill a 256-CU
 // MI355X once.  The per-head readout (d = 128, float32) gives each workgroup a
@@ -99,7 +100,8 @@ Plan make_plan(int B, int H, int L, int d, int in_dt, int out_dt, int request,
   if (request > 0) {
     s = request;
   } else {
-    s = (kKvTargetWorkgroups + bhc - 1) / bhc;
+    const long long target = d == 128 ? kKvTargetWorkgroups / 2 : kKvTargetWorkgroups;
+    s = (target + bhc - 1) / bhc;
     const long long by_size = L / (kKvMinTokensPerFeature * (d + 1));
     s = s < by_size ? s : by_size;
   }
@@ -127,7 +129,7 @@ int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int
               const float* state_in, float* dst, hipStream_t stream) {
   const dim3 grid(p.splits, H, B);
   if (in_dt == LA_BF16)
-    la::kv_partial_bf16<D><<<grid, la::kBlock, 0, stream>>>(
+    la::kv_partial_bf16<D><<<grid, la::kv_threads<D>(), 0, stream>>>(
         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), L, p.tps, state_in, dst);
   else
     la::kv_partial_f32<D><<<grid, la::kBlock, 0, stream>>>(
