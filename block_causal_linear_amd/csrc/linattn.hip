@@ -24,10 +24,11 @@ constexpr int kKvTargetWorkgroups = 512;
 // partial (d*d + d floats) stays small next to the K/V bytes it reads.
 constexpr int kKvMinTokensPerFeature = 4;
 // Readout workgroups the planner aims for.  The sweep readout (bf16, d <= 64)
-// runs three waves per SIMD: 768 workgroups of four waves fill a 256-CU
-// MI355X once.  The per-head readout (d = 128, float32) gives each workgroup a
-// contiguous token range of one head; 1024 was measured best at the 720p
-// shape among 512..4736.
+// runs three or four waves per SIMD: 768 workgroups of four waves were
+// measured best at the 720p shape.  The per-head readout (d = 128, float32)
+// gives each workgroup a contiguous token range of one head: 1024 workgroups
+// (float32), 512 at d = 128 (each stages a 64 KB state; measured at the
+// long-horizon shape, 512 and 256 beat 1024 by 25%).
 constexpr int kSweepWorkgroups = 768;
 constexpr int kReadoutTargetWorkgroups = 1024;
 
@@ -80,7 +81,9 @@ Plan make_plan(int B, int H, int L, int d, int in_dt, int out_dt, int request,
   } else {
     // workgroup tile: four waves x one wave tile (bf16 d = 128), or 128 tokens
     const int ro_unit = in_dt == LA_BF16 ? 4 * 32 : 128;
-    const long long target = readout_request > 0 ? readout_request : kReadoutTargetWorkgroups;
+    const long long target = readout_request > 0 ? readout_request
+                             : d == 128            ? kReadoutTargetWorkgroups / 2
+                                                   : kReadoutTargetWorkgroups;
     const long long per_head = (target + bhc - 1) / bhc;
     long long tpw = (L + per_head - 1) / per_head;
     if (tpw < 1) tpw = 1;
