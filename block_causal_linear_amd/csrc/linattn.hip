@@ -23,13 +23,15 @@ constexpr int kKvTargetWorkgroups = 512;
 // A split should carry at least this many tokens per (d + 1) so that its
 // partial (d*d + d floats) stays small next to the K/V bytes it reads.
 constexpr int kKvMinTokensPerFeature = 4;
-// Readout workgroups the planner aims for.  The sweep readout (bf16, d <= 64)
-// runs three or four waves per SIMD: 768 workgroups of four waves were
-// measured best at the 720p shape.  The per-head readout (d = 128, float32)
-// gives each workgroup a contiguous token range of one head: 1024 workgroups
-// (float32), 512 at d = 128 (each stages a 64 KB state; measured at the
-// long-horizon shape, 512 and 256 beat 1024 by 25%).
+// Readout workgroups the planner aims for.  The sweep readout (bf16 inputs)
+// runs three or four waves per SIMD at d <= 64: 768 workgroups of four waves
+// were measured best at the 720p shape.  The float32 readout gives each
+// workgroup a contiguous token range of one head (1024 workgroups, 512 at
+// d = 128 where each stages a 64 KB state).
 constexpr int kSweepWorkgroups = 768;
+// At d = 128 a sweep workgroup has eight waves and 144 KB of LDS: one per CU
+// (256 measured best at the long-horizon shape among 128..1024).
+constexpr int kSweepWorkgroups128 = 256;
 constexpr int kReadoutTargetWorkgroups = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -46,8 +48,8 @@ struct Plan {
   int splits;          // 0 when L == 0
   int tps;             // tokens per split
   int kv_tile;         // tokens per KV tile
-  bool sweep;          // readout_sweep_bf16 (else the per-head readout)
-  int readout_tpw;     // per-head readout: tokens per workgroup
+  bool sweep;          // readout_sweep_bf16 (bf16 inputs; else readout_f32)
+  int readout_tpw;     // readout_f32: tokens per workgroup
   int readout_wgs;     // readout workgroups in the grid
   int units_per_head;  // sweep readout: four-tile units per (b, h)
 };
@@ -68,19 +70,20 @@ Plan make_plan(int B, int H, int L, int d, int in_dt, int out_dt, int request,
   Plan p{};
   p.kv_tile = in_dt == LA_BF16 ? 64 : 16;
   const long long bhc = static_cast<long long>(B) * H;
-  p.sweep = in_dt == LA_BF16 && d <= 64;
+  p.sweep = in_dt == LA_BF16;
   if (p.sweep) {
-    constexpr int unit = 4 * 16 * LA_READOUT_ROWS;
+    const int unit = 4 * 16 * (d == 128 ? 2 : LA_READOUT_ROWS);
     p.units_per_head = (L + unit - 1) / unit;
-    long long wgs = readout_request > 0 ? readout_request : kSweepWorkgroups;
+    long long wgs = readout_request > 0 ? readout_request
+                    : d == 128          ? kSweepWorkgroups128
+                                        : kSweepWorkgroups;
     const long long most = bhc * p.units_per_head;
     if (wgs > most) wgs = most;
     if (wgs < 1) wgs = 1;
     p.readout_wgs = static_cast<int>(wgs);
     p.readout_tpw = 0;
   } else {
-    // workgroup tile: four waves x one wave tile (bf16 d = 128), or 128 tokens
-    const int ro_unit = in_dt == LA_BF16 ? 4 * 32 : 128;
+    const int ro_unit = 128;  // readout_f32 processes 32-token tiles
     const long long target = readout_request > 0 ? readout_request
                              : d == 128            ? kReadoutTargetWorkgroups / 2
                                                    : kReadoutTargetWorkgroups;
@@ -143,42 +146,34 @@ int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int
 template <int D>
 int launch_readout(const Plan& p, const void* q, int in_dt, int out_dt, int B, int H, int L,
                    const float* state, void* out, float eps, hipStream_t stream) {
-  if constexpr (D <= 64) {
-    if (p.sweep) {
-      const uint16_t* qq = static_cast<const uint16_t*>(q);
-      const int total = B * H * p.units_per_head;
-      if (out_dt == LA_BF16)
-        la::readout_sweep_bf16<D, true><<<p.readout_wgs, la::kBlock, 0, stream>>>(
-            qq, state, out, L, p.units_per_head, total, eps);
-      else
-        la::readout_sweep_bf16<D, false><<<p.readout_wgs, la::kBlock, 0, stream>>>(
-            qq, state, out, L, p.units_per_head, total, eps);
-      return launched();
-    }
-  }
-  const dim3 grid((L + p.readout_tpw - 1) / p.readout_tpw, H, B);
-  if (in_dt == LA_BF16) {
+  if (p.sweep) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const int total = B * H * p.units_per_head;
+    constexpr int nt = la::sweep_threads<D>();
     if (out_dt == LA_BF16)
-      la::readout_bf16<D, true><<<grid, la::kBlock, 0, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+      la::readout_sweep_bf16<D, true><<<p.readout_wgs, nt, 0, stream>>>(
+          qq, state, out, L, p.units_per_head, total, eps);
     else
-      la::readout_bf16<D, false><<<grid, la::kBlock, 0, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+      la::readout_sweep_bf16<D, false><<<p.readout_wgs, nt, 0, stream>>>(
+          qq, state, out, L, p.units_per_head, total, eps);
+    return launched();
+  }
+  // float32 queries: per-head workgroups over contiguous token ranges
+  const dim3 grid((L + p.readout_tpw - 1) / p.readout_tpw, H, B);
+  const float* qq = static_cast<const float*>(q);
+  constexpr size_t smem = la::readout_f32_smem<D>();
+  if (out_dt == LA_BF16) {
+    if (smem > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
+      return LA_E_HIP;
+    la::readout_f32<D, true><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
   } else {
-    const float* qq = static_cast<const float*>(q);
-    constexpr size_t smem = la::readout_f32_smem<D>();
-    if (out_dt == LA_BF16) {
-      if (smem > 65536 &&
-          hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
-        return LA_E_HIP;
-      la::readout_f32<D, true><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
-    } else {
-      if (smem > 65536 &&
-          hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
-        return LA_E_HIP;
-      la::readout_f32<D, false><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
-    }
+    if (smem > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
+      return LA_E_HIP;
+    la::readout_f32<D, false><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
   }
   return launched();
 }

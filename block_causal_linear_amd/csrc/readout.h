@@ -8,10 +8,6 @@
 
 #include "la_common.h"
 
-// Two waves per SIMD is the most that fits d = 64 and d = 128 without spills.
-#ifndef LA_READOUT_MIN_WAVES
-#define LA_READOUT_MIN_WAVES 2
-#endif
 // (Measured at the 720p chunk: plain loads and stores beat the
 // non-temporal forms, and two 16-token row blocks per wave tile beat four.)
 #ifndef LA_READOUT_STREAM_STORES
@@ -23,10 +19,6 @@
 // 16-token row blocks per wave tile at d <= 64.
 #ifndef LA_READOUT_ROWS
 #define LA_READOUT_ROWS 2
-#endif
-// Sweep readout: consecutive wave tiles of one head a wave takes per visit.
-#ifndef LA_SWEEP_RUN
-#define LA_SWEEP_RUN 1
 #endif
 
 namespace la {
@@ -50,10 +42,6 @@ namespace la {
 // W (4, or 2 when d = 32) values make one vector store.  Together these make
 // every store instruction of a wavefront write 4 consecutive tokens' rows
 // (1 KB at d = 64, float32) contiguously.
-//
-// The state is staged once per workgroup in LDS as S^T split into hi/lo
-// planes ([column block row][feature a], padded rows), so a B operand is a
-// single 16-byte LDS read.
 
 template <int D>
 struct ReadoutShape {
@@ -63,9 +51,7 @@ struct ReadoutShape {
   static constexpr int GRP = NBK / W;            // vector stores per token row
   static constexpr int R = (D == 128) ? 2 : LA_READOUT_ROWS;  // 16-token row blocks per wave tile
   static constexpr int TILE = 16 * R;            // tokens per wave tile
-  static constexpr int RS = D + 8;               // LDS row stride (bf16 elements)
   static constexpr int UPR = D / 8;              // 16-byte units per query row
-  static constexpr int MIN_WAVES = LA_READOUT_MIN_WAVES;  // occupancy target per SIMD
 };
 
 template <typename T>
@@ -85,202 +71,54 @@ __device__ __forceinline__ uint4 load_q(const uint4* p) {
 #endif
 }
 
-// LDS row of state column c (inverse of pi above).
+// Sweep readout: at d = 128 the output columns split into two 64-column
+// halves; waves 0-3 and 4-7 of a workgroup take the same four tiles, one
+// half each (the second read of a query row hits L2).
 template <int D>
-__device__ __forceinline__ int state_col_row(int c) {
-  constexpr int W = ReadoutShape<D>::W;
-  const int grp = c / (16 * W);
-  const int cc = c % (16 * W);
-  return 16 * (W * grp + cc % W) + cc / W;
+struct SweepShape {
+  static constexpr int NCH = D == 128 ? 2 : 1;          // column halves
+  static constexpr int NW = 4 * NCH;                    // waves per workgroup
+  static constexpr int NT = kWave * NW;                 // threads per workgroup
+  static constexpr int CB = ReadoutShape<D>::NBK / NCH;  // column blocks per half
+  static constexpr int MIN_WAVES = D == 128 ? 2 : 3;
+  // Operand buffers in LDS (two: one barrier per unit).  At d = 128 they take
+  // 144 KB, one eight-wave workgroup per CU; a single 72 KB buffer with two
+  // barriers per unit (two workgroups per CU) measured no faster.
+  static constexpr int NBUF = 2;
+};
+
+template <int D>
+constexpr int sweep_threads() {
+  return SweepShape<D>::NT;
+}
+
+template <int D>
+constexpr int sweep_min_waves() {
+  return SweepShape<D>::MIN_WAVES;
 }
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kBlock, ReadoutShape<D>::MIN_WAVES) void readout_bf16(const uint16_t* __restrict__ q,
-                                                       const float* __restrict__ state,
-                                                       void* __restrict__ out, int L, int tpw,
-                                                       float eps) {
+__global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void readout_sweep_bf16(
+    const uint16_t* __restrict__ q, const float* __restrict__ state, void* __restrict__ out, int L,
+    int units_per_head, int total_units, float eps) {
   using Sh = ReadoutShape<D>;
-  constexpr int E = D * D + D;
-  constexpr int RS = Sh::RS;
-  __shared__ __attribute__((aligned(16))) uint16_t s_hi[(D + 1) * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t s_lo[(D + 1) * RS];
-
-  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
-  const int tb = blockIdx.x * tpw;
-  const int te = min(L, tb + tpw);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int n = lane & 15, g = lane >> 4;
-
-  const float* st = state + bh * E;
-  for (int e = tid; e < D * D; e += kBlock) {
-    const int a = e / D, c = e % D;
-    const float x = st[e];
-    const uint16_t hi = to_bf16(x);
-    const uint16_t lo = to_bf16(x - from_bf16(hi));
-    const int row = state_col_row<D>(c);
-    s_hi[row * RS + a] = hi;
-    s_lo[row * RS + a] = lo;
-  }
-  for (int a = tid; a < D; a += kBlock) {
-    const float x = st[D * D + a];
-    const uint16_t hi = to_bf16(x);
-    s_hi[D * RS + a] = hi;
-    s_lo[D * RS + a] = to_bf16(x - from_bf16(hi));
-  }
-  __syncthreads();
-
-  const uint4* qb = reinterpret_cast<const uint4*>(q + bh * static_cast<size_t>(L) * D);
-  const int tok_a = 4 * (n & 3) + (n >> 2);  // token (within a row block) of A row n
-
-  // A operands of one wave tile: phi(q) rows.  Rows past the end of the
-  // range read row te - 1 instead (their outputs are never stored), so the
-  // loads carry no branch and no wait right after issue.
-  auto load_a = [&](uint4 (&a)[Sh::R][Sh::KS], int tile) {
-#pragma unroll
-    for (int r = 0; r < Sh::R; ++r) {
-      const int tok = min(tile + 16 * r + tok_a, te - 1);
-#pragma unroll
-      for (int s = 0; s < Sh::KS; ++s)
-        a[r][s] = load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g);
-    }
-  };
-
-  uint4 a[Sh::R][Sh::KS];
-  int tile = tb + wave * Sh::TILE;
-  if (tile < te) load_a(a, tile);
-  for (; tile < te; tile += 4 * Sh::TILE) {
-    // B operands are re-read from LDS every tile instead of living in 80
-    // registers for the kernel's lifetime; this keeps two waves per SIMD.
-    asm volatile("" ::: "memory");
-    // issue the next tile's loads before this tile's MFMAs and stores
-    uint4 an[Sh::R][Sh::KS];
-    const int next = tile + 4 * Sh::TILE;
-    if (next < te) load_a(an, next);
-
-#pragma unroll
-    for (int r = 0; r < Sh::R; ++r)
-#pragma unroll
-      for (int s = 0; s < Sh::KS; ++s) a[r][s] = relu_bf16x8(a[r][s]);
-    f32x4 acc[Sh::R][Sh::NBK];
-    f32x4 accz[Sh::R];
-#pragma unroll
-    for (int r = 0; r < Sh::R; ++r) {
-      accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < Sh::NBK; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int s = 0; s < Sh::KS; ++s) {
-      const int off = 8 * (4 * s + g);
-      const uint4 zh = *reinterpret_cast<const uint4*>(&s_hi[D * RS + off]);
-      const uint4 zl = *reinterpret_cast<const uint4*>(&s_lo[D * RS + off]);
-#pragma unroll
-      for (int r = 0; r < Sh::R; ++r) {
-        accz[r] = mfma_16x16x32(a[r][s], zh, accz[r]);
-        accz[r] = mfma_16x16x32(a[r][s], zl, accz[r]);
-      }
-#pragma unroll
-      for (int c = 0; c < Sh::NBK; ++c) {
-        const int row = 16 * c + n;
-        const uint4 bh16 = *reinterpret_cast<const uint4*>(&s_hi[row * RS + off]);
-        const uint4 bl16 = *reinterpret_cast<const uint4*>(&s_lo[row * RS + off]);
-#pragma unroll
-        for (int r = 0; r < Sh::R; ++r) {
-          acc[r][c] = mfma_16x16x32(a[r][s], bh16, acc[r][c]);
-          acc[r][c] = mfma_16x16x32(a[r][s], bl16, acc[r][c]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < Sh::R; ++r)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tile + 16 * r + 4 * i + g;
-        if (tok >= te) continue;
-        const float inv = fast_rcp(accz[r][i] + eps);
-        const size_t row0 = static_cast<size_t>(bh * L + tok) * D;
-#pragma unroll
-        for (int gr = 0; gr < Sh::GRP; ++gr) {
-          const int col = 16 * Sh::W * gr + Sh::W * n;
-          if constexpr (Sh::W == 4) {
-            const float o0 = acc[r][4 * gr + 0][i] * inv, o1 = acc[r][4 * gr + 1][i] * inv;
-            const float o2 = acc[r][4 * gr + 2][i] * inv, o3 = acc[r][4 * gr + 3][i] * inv;
-            if constexpr (OUT_BF16) {
-              const u32x2 pk = {pack2(to_bf16(o0), to_bf16(o1)), pack2(to_bf16(o2), to_bf16(o3))};
-              store_out(pk, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + row0 + col));
-            } else {
-              store_out(f32x4{o0, o1, o2, o3},
-                        reinterpret_cast<f32x4*>(static_cast<float*>(out) + row0 + col));
-            }
-          } else {
-            const float o0 = acc[r][2 * gr + 0][i] * inv, o1 = acc[r][2 * gr + 1][i] * inv;
-            if constexpr (OUT_BF16) {
-              store_out(pack2(to_bf16(o0), to_bf16(o1)),
-                        reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + row0 + col));
-            } else {
-              store_out(f32x2{o0, o1}, reinterpret_cast<f32x2*>(static_cast<float*>(out) + row0 + col));
-            }
-          }
-        }
-      }
-    if (next < te) {
-#pragma unroll
-      for (int r = 0; r < Sh::R; ++r)
-#pragma unroll
-        for (int s = 0; s < Sh::KS; ++s) a[r][s] = an[r][s];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Sweep schedule for d <= 64 (the bandwidth path).
-//
-// The output is two thirds of the readout's HBM traffic, and HBM write
-// bandwidth on MI355X depends on how many far-apart regions are written at
-// once: measured with this access pattern at the 720p shape, a single
-// window that the whole GPU sweeps through sustains ~5.8 TB/s, while one
-// contiguous range per workgroup (or per head) sustains ~5.0 TB/s.  So the
-// work is cut into units of four adjacent wave tiles (4 x 16R tokens of one
-// (b, h)), enumerated head-major, and workgroup k takes units k, k + G,
-// k + 2G, ...: at any moment the GPU works on G adjacent units.
-//
-// Consecutive units of a workgroup belong to different heads, so each unit
-// rebuilds the B operands (S and z as bf16 hi/lo pairs) from the float32
-// state in L2.  The d/32 x d/16 (k-step, column block) pairs are shared out
-// over the four waves (two each at d = 64): with the column placement pi
-// above, a wave's pairs are adjacent state columns, so lane (n, g) reads
-// S[32s + 8g + j][W n + c0 .. W n + c0 + PW - 1], j = 0..7, as one vector,
-// and rows (j, j+1) convert straight into packed operand words.  The
-// operands go to LDS in lane order (one conflict-free 16-byte write per lane
-// and operand), double-buffered so one barrier per unit suffices.
-//
-// Every wave issues the same loads in the same order in every iteration
-// (the next unit's state and queries, before this unit's MFMAs; on the last
-// unit the loads repeat it): with no divergent control flow around the loads
-// the compiler's wait counts stay exact, and the prefetch really overlaps.
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* __restrict__ q,
-                                                                const float* __restrict__ state,
-                                                                void* __restrict__ out, int L,
-                                                                int units_per_head, int total_units,
-                                                                float eps) {
-  using Sh = ReadoutShape<D>;
-  static_assert(D <= 64 && Sh::GRP == 1, "sweep readout covers d = 32 and d = 64");
+  using Sw = SweepShape<D>;
   constexpr int E = D * D + D;
   constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, R = Sh::R;
-  constexpr int NW = kBlock / kWave;
+  constexpr int NW = Sw::NW, CB = Sw::CB;
   constexpr int NF = KS * (NBK + 1) * 2;  // operands: [k-step][column block, z last][hi, lo]
   constexpr int PAIRS = KS * NBK;         // (k-step, column block) pairs
   constexpr int PW = PAIRS >= NW ? PAIRS / NW : 1;  // pairs per wave
-  static_assert(PAIRS % PW == 0 && NBK % PW == 0, "pair split");
+  static_assert(PAIRS % PW == 0 && NBK % PW == 0 && PW <= W && CB % W == 0, "pair split");
   using vecP = float __attribute__((ext_vector_type(PW)));
-  __shared__ uint4 frag[2][NF][kWave];
+  constexpr int NBUF = Sw::NBUF;
+  __shared__ uint4 frag[NBUF][NF][kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const int tw = wave % 4;   // tile of the unit
+  const int ch = wave / 4;   // column half
   const int n = lane & 15, g = lane >> 4;
   const int tok_a = 4 * (n & 3) + (n >> 2);
   auto fi = [](int s, int c, int p) { return (s * (NBK + 1) + c) * 2 + p; };
@@ -296,7 +134,8 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
     const float* st = state + static_cast<size_t>(bh) * E;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      sraw[j] = *reinterpret_cast<const vecP*>(st + (32 * ps + 8 * g + j) * D + W * n + pc0);
+      sraw[j] = *reinterpret_cast<const vecP*>(st + (32 * ps + 8 * g + j) * D + 16 * W * (pc0 / W) +
+                                                 W * n + pc0 % W);
     zraw[0] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * ps + 8 * g);
     zraw[1] = *reinterpret_cast<const f32x4*>(st + D * D + 32 * ps + 8 * g + 4);
   };
@@ -338,13 +177,13 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int s = 0; s < KS; ++s) a[r][s] = relu_bf16x8(qraw[r][s]);
-    f32x4 acc[R][NBK];
+    f32x4 acc[R][CB];
     f32x4 accz[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       accz[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < NBK; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < CB; ++c) acc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -355,8 +194,9 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
         accz[r] = mfma_16x16x32(a[r][s], zl, accz[r]);
       }
 #pragma unroll
-      for (int c = 0; c < NBK; ++c) {
-        const uint4 bh16 = frag[buf][fi(s, c, 0)][lane], bl16 = frag[buf][fi(s, c, 1)][lane];
+      for (int c = 0; c < CB; ++c) {
+        const int cg = ch * CB + c;
+        const uint4 bh16 = frag[buf][fi(s, cg, 0)][lane], bl16 = frag[buf][fi(s, cg, 1)][lane];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           acc[r][c] = mfma_16x16x32(a[r][s], bh16, acc[r][c]);
@@ -372,7 +212,7 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
         if (tok >= L) continue;
         const float inv = fast_rcp(accz[r][i] + eps);
         const size_t row0 = (static_cast<size_t>(bh) * L + tok) * D;
-        const int col = W * n;
+        const int col = 16 * W * (ch * CB / W) + W * n;
         if constexpr (W == 4) {
           const float o0 = acc[r][0][i] * inv, o1 = acc[r][1][i] * inv;
           const float o2 = acc[r][2][i] * inv, o3 = acc[r][3][i] * inv;
@@ -401,20 +241,22 @@ __global__ __launch_bounds__(kBlock, 3) void readout_sweep_bf16(const uint16_t* 
   int unit = blockIdx.x;
   if (unit >= total_units) return;
   int bh = unit / units_per_head;
-  int t0 = ((unit - bh * units_per_head) * 4 + wave) * Sh::TILE;
+  int t0 = ((unit - bh * units_per_head) * 4 + tw) * Sh::TILE;
   uint4 a[R][KS];
   load_state(bh);
   load_a(a, bh, t0);
   for (int i = 0;; ++i) {
-    const int buf = i & 1;
-    // buf was last read before the previous iteration's barrier
+    const int buf = NBUF == 2 ? (i & 1) : 0;
+    // With two buffers, buf was last read before the previous iteration's
+    // barrier; with one, wait until every wave has consumed the last unit.
+    if (NBUF == 1 && i > 0) __syncthreads();
     build(buf);
     __syncthreads();
     const int next = unit + gridDim.x;
     const bool more = next < total_units;
     const int nu = more ? next : unit;
     const int nbh = nu / units_per_head;
-    const int nt0 = ((nu - nbh * units_per_head) * 4 + wave) * Sh::TILE;
+    const int nt0 = ((nu - nbh * units_per_head) * 4 + tw) * Sh::TILE;
     uint4 an[R][KS];
     load_state(nbh);
     load_a(an, nbh, nt0);

@@ -121,7 +121,9 @@ def test_plan_shapes():
     assert la.plan(1, 32, 75600, 64)[1] == 768
     assert la.plan(1, 32, 75600, 64, readout_workgroups=300)[1] == 300
     assert la.plan(1, 1, 100, 64, readout_workgroups=300)[1] == 1
-    # d = 128 keeps per-head workgroups: 4*16 heads, 4096 tokens -> 8 per head
-    assert la.plan(4, 16, 4096, 128)[1] == 4 * 16 * 8
+    # d = 128 sweeps too: 256 eight-wave workgroups; float32 inputs keep
+    # per-head workgroups (512 at d = 128: 8 per head here)
+    assert la.plan(4, 16, 4096, 128)[1] == 256
+    assert la.plan(4, 16, 4096, 128, in_dtype=la.torch.float32)[1] == 4 * 16 * 8
     with pytest.raises(la.LinAttnError):
         la.plan(1, 1, 10, 48)
