@@ -127,6 +127,8 @@ OTHER = {
     "global720p": 3,
     "stream480p": 4,
     "longhorizon": 5,
+    "stream480p_onecall": 4,
+    "longhorizon_onecall": 5,
 }
 
 
@@ -153,18 +155,32 @@ def bench_other(args):
             x = torch.where(rows, x * w.outlier_scale, x)
         return x.to(torch.bfloat16)
 
-    chunks = [tuple(draw() for _ in range(3)) for _ in range(C)]
+    onecall = args.workload.endswith("_onecall")
+    if onecall:
+        # the whole stream as one sequence of C blocks, one la_blockcausal_forward per step
+        seq = tuple(torch.cat([draw() for _ in range(C)], dim=2) for _ in range(3))
+        out_seq = torch.empty((B, H, L * C, d), dtype=torch.float32, device=dev)
+        states = torch.empty((B, H, C, d * d + d), dtype=torch.float32, device=dev)
+        chunks = []
+    else:
+        chunks = [tuple(draw() for _ in range(3)) for _ in range(C)]
     out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
     state = torch.empty((B, H, d * d + d), dtype=torch.float32, device=dev)
     splits, rwg = la.plan(B, H, L, d, kv_splits=args.kv_splits)
-    log(f"plan: kv_splits={splits} readout_workgroups={rwg}")
+    log(f"plan (per chunk call): kv_splits={splits} readout_workgroups={rwg}")
 
     # stage events on every `event_every`-th call (counted over all calls)
     every = max(1, args.event_every)
     steps = max(1, args.steps // C) if C > 1 else args.steps
-    evs = {c: la.StageEvents() for c in range(0, steps * C, every)}
+    calls = 1 if onecall else C
+    evs = {c: la.StageEvents() for c in range(0, steps * calls, max(1, every // (C // calls)))}
 
     def step(i=None):
+        if onecall:
+            ev = None if i is None else evs.get(i)
+            la.blockcausal_forward(seq[0], seq[1], seq[2], L, out=out_seq, states=states,
+                                   eps=workloads.EPS, kv_splits=args.kv_splits, stage_events=ev)
+            return
         base = None if i is None else i * C
         if w.form == "global":
             q, k, v = chunks[0]
@@ -194,17 +210,21 @@ def bench_other(args):
         e.close()
     kv_ms, red_ms, ro_ms = (float(x) for x in stages.mean(axis=0))
     call_b, kv_b, ro_b = bytes_alg(B, H, L, d, with_state_in=(w.form != "global"))
+    if onecall:  # stage times cover all C blocks
+        kv_b, ro_b = kv_b * C, ro_b * C
     tokens = B * L * C
     ro_kernel = f"readout_sweep_bf16<{d}>" if d <= 64 else f"readout_bf16<{d}>"
     result = {
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "form": w.form, "B": B, "H": H, "d": d, "L": L,
-                   "calls_per_step": C, "q_k_v": "bf16", "out": "f32", "state": "f32",
+        "config": {"workload": w.name + ("-one-call" if onecall else ""), "form": w.form,
+                   "B": B, "H": H, "d": d, "L": L, "blocks_per_step": C,
+                   "calls_per_step": calls, "q_k_v": "bf16", "out": "f32", "state": "f32",
                    "kv_splits": splits, "readout_workgroups": rwg},
         "hbm_frac": call_b * C / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "us_per_call": ms * 1e3 / C,
+        "us_per_call": ms * 1e3 / calls,
+        "us_per_block": ms * 1e3 / C,
         "roofline": {"bound": "hbm", "kernel": ro_kernel,
                      "achieved": ro_b / (ro_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": ro_b / (ro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -225,7 +245,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--workload", default="chunk720p",
-                    choices=["chunk720p", "global480p", "global720p", "stream480p", "longhorizon"])
+                    choices=["chunk720p", "global480p", "global720p", "stream480p", "longhorizon",
+                             "stream480p_onecall", "longhorizon_onecall"])
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-stage HIP events on every N-th timed step")
     ap.add_argument("--plain-steps", type=int, default=0,

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "la_global_forward": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P],
     "la_global_forward_ex": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
                              ctypes.POINTER(LaunchOpts), _P],
+    "la_blockcausal_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
+    "la_blockcausal_forward_ex": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                  ctypes.POINTER(LaunchOpts), _P],
     "la_plan": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "la_status_string": [_I],
     "la_abi_version": [],
@@ -137,7 +140,7 @@ def _need(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
-def _prepare(q, k, v, out, out_dtype, state_out, B_H_d=None):
+def _prepare_out(q, k, v, out, out_dtype):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name)
         if t.dim() != 4:
@@ -148,12 +151,17 @@ def _prepare(q, k, v, out, out_dtype, state_out, B_H_d=None):
         raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on one device")
-    B, H, L, d = q.shape
     if out is None:
-        out = torch.empty((B, H, L, d), dtype=out_dtype, device=q.device)
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     _need(out, "out")
     if out.shape != q.shape or out.dtype not in _DTYPE or out.device != q.device:
         raise ValueError("out must be [B, H, L, d], float32 or bfloat16, on q's device")
+    return out
+
+
+def _prepare(q, k, v, out, out_dtype, state_out):
+    out = _prepare_out(q, k, v, out, out_dtype)
+    B, H, L, d = q.shape
     if state_out is None:
         state_out = torch.empty((B, H, d * d + d), dtype=torch.float32, device=q.device)
     _need(state_out, "state_out", torch.float32)
@@ -211,6 +219,44 @@ def global_forward(q, k, v, out=None, state_out=None, eps=DEFAULT_EPS,
         rc = L_.la_global_forward_ex(*args, ctypes.byref(o), _stream(q.device))
     _check(rc, "la_global_forward")
     return out, state_out
+
+
+def blockcausal_forward(q, k, v, T, state_in=None, out=None, states=None, eps=DEFAULT_EPS,
+                        out_dtype=torch.float32, kv_splits=0, readout_workgroups=0,
+                        stage_events=None):
+    """A whole sequence in the block-causal form: the N tokens of every (b, h)
+    cut into C = ceil(N / T) blocks of T tokens; block n's queries read
+    state_in + KV_1 + ... + KV_n.  Returns (out, states) with states
+    [B, H, C, d*d + d] the state after every block (states[:, :, -1] is the
+    state after the sequence).  state_in None means zeros."""
+    _need(q, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    T = int(T)
+    if T < 1:
+        raise ValueError("T must be >= 1")
+    C = -(-N // T) if N > 0 else 0
+    if states is None:
+        states = torch.empty((B, H, C, d * d + d), dtype=torch.float32, device=q.device)
+    _need(states, "states", torch.float32)
+    if tuple(states.shape) != (B, H, C, d * d + d) or states.device != q.device:
+        raise ValueError(f"states must be [{B}, {H}, {C}, {d * d + d}] on q's device")
+    out = _prepare_out(q, k, v, out, out_dtype)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32)
+        if tuple(state_in.shape) != (B, H, d * d + d) or state_in.device != q.device:
+            raise ValueError("state_in must be [B, H, d*d + d] on q's device")
+    o = _opts(kv_splits, readout_workgroups, stage_events)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out), _ptr(states),
+            B, H, N, T, d, _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps))
+    L_ = lib()
+    if o is None:
+        rc = L_.la_blockcausal_forward(*args, _stream(q.device))
+    else:
+        rc = L_.la_blockcausal_forward_ex(*args, ctypes.byref(o), _stream(q.device))
+    _check(rc, "la_blockcausal_forward")
+    return out, states
 
 
 def plan(B, H, L, d, in_dtype=torch.bfloat16, out_dtype=torch.float32, kv_splits=0,

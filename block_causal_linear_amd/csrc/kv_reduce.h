@@ -5,9 +5,11 @@
 // "Sabit Bellekli KV önbelleğe alma mekanizması"), which is what lets many
 // workgroups share one head's tokens.
 //
-// With one split the kernel writes S_out = S_in + P and z_out = z_in + p
-// straight into the state; with more, it writes P_s, p_s to a partials
-// buffer [B][H][splits][d*d + d] that state_reduce sums in a fixed order.
+// A sequence may be cut into several blocks (the whole-sequence block-causal
+// call); every (block, split) pair gets its own partial in a buffer
+// [B][H][blocks][splits][d*d + d] that state_reduce / state_scan sum in a
+// fixed order.  With one block and one split the kernel writes
+// S_out = S_in + P and z_out = z_in + p straight into the state.
 #pragma once
 
 #include "la_common.h"
@@ -90,10 +92,15 @@ __device__ __forceinline__ uint4 tile_column8(const uint16_t* tile, int ks, int 
   return r;
 }
 
+// Grid: (blocks x splits, H, B).  Block c covers tokens [c T, min((c+1) T, N))
+// of every (b, h) sequence of N tokens; split s of it covers tps tokens.  The
+// result for (b, h, c, s) goes to dst[((b H + h) C + c) splits + s]; with a
+// single block and a single split, dst is the state itself and state_in (if
+// any) is added.
 template <int D>
 __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_bf16(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int L, int tps,
-    const float* state_in, float* dst) {
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int TB, int splits,
+    int tps, const float* state_in, float* dst) {
   constexpr int WR = KvWaves<D>::WR, WC = KvWaves<D>::WC;
   using T = KvTile<D, WR, WC>;
   constexpr int BR = D / WR, BC = D / WC;  // output block of one wave
@@ -101,13 +108,16 @@ __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_bf16(
   constexpr int E = D * D + D;
   __shared__ uint4 lds[2][2][T::UNITS];  // [buffer][K, V][unit]
 
-  const int split = blockIdx.x;
-  const int splits = gridDim.x;
+  const int nblk = gridDim.x / splits;
+  const int blk = blockIdx.x / splits;
+  const int split = blockIdx.x - blk * splits;
   const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
-  const int t0 = split * tps;
-  const int t1 = min(L, t0 + tps);
-  const uint4* kb = reinterpret_cast<const uint4*>(k + bh * static_cast<size_t>(L) * D);
-  const uint4* vb = reinterpret_cast<const uint4*>(v + bh * static_cast<size_t>(L) * D);
+  const int c0 = blk * TB;
+  const int c1 = min(N, c0 + TB);
+  const int t0 = c0 + split * tps;
+  const int t1 = min(c1, t0 + tps);
+  const uint4* kb = reinterpret_cast<const uint4*>(k + bh * static_cast<size_t>(N) * D);
+  const uint4* vb = reinterpret_cast<const uint4*>(v + bh * static_cast<size_t>(N) * D);
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -195,8 +205,9 @@ __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_bf16(
     }
   }
 
-  float* o = dst + (splits > 1 ? bh * splits + split : bh) * static_cast<size_t>(E);
-  const float* si = (splits == 1 && state_in != nullptr) ? state_in + bh * E : nullptr;
+  const bool direct = nblk == 1 && splits == 1;
+  float* o = dst + ((bh * nblk + blk) * splits + split) * static_cast<size_t>(E);
+  const float* si = (direct && state_in != nullptr) ? state_in + bh * E : nullptr;
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
@@ -227,9 +238,9 @@ __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_bf16(
 // for exactness checks and small problems; bfloat16 is the bandwidth path).
 template <int D>
 __global__ __launch_bounds__(kBlock) void kv_partial_f32(const float* __restrict__ k,
-                                                         const float* __restrict__ v, int L, int tps,
-                                                         const float* state_in,
-                                                         float* dst) {
+                                                         const float* __restrict__ v, int N, int T,
+                                                         int splits, int tps,
+                                                         const float* state_in, float* dst) {
   constexpr int TT = 16;
   constexpr int E = D * D + D;
   constexpr int PER = D * D / kBlock;
@@ -237,13 +248,16 @@ __global__ __launch_bounds__(kBlock) void kv_partial_f32(const float* __restrict
   __shared__ float sk[TT * D];
   __shared__ float sv[TT * D];
 
-  const int split = blockIdx.x;
-  const int splits = gridDim.x;
+  const int nblk = gridDim.x / splits;
+  const int blk = blockIdx.x / splits;
+  const int split = blockIdx.x - blk * splits;
   const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
-  const int t0 = split * tps;
-  const int t1 = min(L, t0 + tps);
-  const float* kb = k + bh * static_cast<size_t>(L) * D;
-  const float* vb = v + bh * static_cast<size_t>(L) * D;
+  const int c0 = blk * T;
+  const int c1 = min(N, c0 + T);
+  const int t0 = c0 + split * tps;
+  const int t1 = min(c1, t0 + tps);
+  const float* kb = k + bh * static_cast<size_t>(N) * D;
+  const float* vb = v + bh * static_cast<size_t>(N) * D;
   const int tid = threadIdx.x;
 
   float acc[PER];
@@ -274,8 +288,9 @@ __global__ __launch_bounds__(kBlock) void kv_partial_f32(const float* __restrict
     __syncthreads();
   }
 
-  float* o = dst + (splits > 1 ? bh * splits + split : bh) * static_cast<size_t>(E);
-  const float* si = (splits == 1 && state_in != nullptr) ? state_in + bh * E : nullptr;
+  const bool direct = nblk == 1 && splits == 1;
+  float* o = dst + ((bh * nblk + blk) * splits + split) * static_cast<size_t>(E);
+  const float* si = (direct && state_in != nullptr) ? state_in + bh * E : nullptr;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = tid + kBlock * i;

@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/linattn.h: argument checks,
-// launch planning, and the three launches of a forward call
-// (KV reduction -> split reduce + state add -> readout) on the caller's
-// stream.  Nothing here allocates device memory or synchronises.
+// launch planning, and the three launches of a forward call (KV reduction ->
+// split reduce + state add, or the prefix over blocks -> readout) on the
+// caller's stream.  Nothing here allocates device memory or synchronises.
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -14,7 +14,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -45,81 +45,90 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 int elem_size(int dt) { return dt == LA_BF16 ? 2 : 4; }
 
 struct Plan {
-  int splits;          // 0 when L == 0
+  int nblk;            // blocks of T tokens (0 when N == 0)
+  int T;               // tokens per block (the last may be shorter)
+  int splits;          // token splits per block for the KV reduction
   int tps;             // tokens per split
   int kv_tile;         // tokens per KV tile
+  bool direct;         // one block, one split: the KV kernel writes the state
+  bool in_place;       // several blocks, one split: partials live in `states`
   bool sweep;          // readout_sweep_bf16 (bf16 inputs; else readout_f32)
   int readout_tpw;     // readout_f32: tokens per workgroup
   int readout_wgs;     // readout workgroups in the grid
-  int units_per_head;  // sweep readout: four-tile units per (b, h)
+  int units_per_block; // sweep readout: four-tile units per block
 };
 
-int check_shape(int B, int H, int L, int d, int in_dt, int out_dt) {
-  if (B <= 0 || H <= 0 || L < 0) return LA_E_INVAL;
+int check_shape(int B, int H, int N, int d, int in_dt, int out_dt) {
+  if (B <= 0 || H <= 0 || N < 0) return LA_E_INVAL;
   if (B > 65535 || H > 65535) return LA_E_INVAL;
   if (d != 32 && d != 64 && d != 128) return LA_E_UNSUPPORTED;
   if ((in_dt != LA_F32 && in_dt != LA_BF16) || (out_dt != LA_F32 && out_dt != LA_BF16))
     return LA_E_UNSUPPORTED;
   // keep every per-head element index inside 31 bits
-  if (static_cast<long long>(L) * d >= (1LL << 31)) return LA_E_INVAL;
+  if (static_cast<long long>(N) * d >= (1LL << 31)) return LA_E_INVAL;
   return LA_OK;
 }
 
-Plan make_plan(int B, int H, int L, int d, int in_dt, int out_dt, int request,
+// N tokens per (b, h) in blocks of T (T >= N: one block).
+Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int request,
                int readout_request) {
   Plan p{};
   p.kv_tile = in_dt == LA_BF16 ? 64 : 16;
-  const long long bhc = static_cast<long long>(B) * H;
+  p.T = T < N ? T : N;
+  p.nblk = N == 0 ? 0 : (N + p.T - 1) / p.T;
   p.sweep = in_dt == LA_BF16;
-  if (p.sweep) {
-    const int unit = 4 * 16 * (d == 128 ? 2 : LA_READOUT_ROWS);
-    p.units_per_head = (L + unit - 1) / unit;
-    long long wgs = readout_request > 0 ? readout_request
-                    : d == 128          ? kSweepWorkgroups128
-                                        : kSweepWorkgroups;
-    const long long most = bhc * p.units_per_head;
-    if (wgs > most) wgs = most;
-    if (wgs < 1) wgs = 1;
-    p.readout_wgs = static_cast<int>(wgs);
-    p.readout_tpw = 0;
-  } else {
-    const int ro_unit = 128;  // readout_f32 processes 32-token tiles
-    const long long target = readout_request > 0 ? readout_request
-                             : d == 128            ? kReadoutTargetWorkgroups / 2
-                                                   : kReadoutTargetWorkgroups;
-    const long long per_head = (target + bhc - 1) / bhc;
-    long long tpw = (L + per_head - 1) / per_head;
-    if (tpw < 1) tpw = 1;
-    tpw = (tpw + ro_unit - 1) / ro_unit * ro_unit;
-    p.readout_tpw = static_cast<int>(tpw);
-    p.readout_wgs = static_cast<int>(((L + tpw - 1) / tpw) * bhc);
-    p.units_per_head = 0;
-  }
-  if (L == 0) {
-    p.splits = 0;
-    p.tps = 0;
-    p.readout_wgs = 0;
-    return p;
-  }
-  const int ntiles = (L + p.kv_tile - 1) / p.kv_tile;
+  if (N == 0) return p;
+  const long long bhc = static_cast<long long>(B) * H;
+  const long long pairs = bhc * p.nblk;  // (b, h, block) pairs
+  const int Tb = p.T;                    // tokens in a full block
+
+  // KV splits per block
+  const int ntiles = (Tb + p.kv_tile - 1) / p.kv_tile;
   long long s;
   if (request > 0) {
     s = request;
   } else {
     const long long target = d == 128 ? kKvTargetWorkgroups / 2 : kKvTargetWorkgroups;
-    s = (target + bhc - 1) / bhc;
-    const long long by_size = L / (kKvMinTokensPerFeature * (d + 1));
+    s = (target + pairs - 1) / pairs;
+    const long long by_size = Tb / (kKvMinTokensPerFeature * (d + 1));
     s = s < by_size ? s : by_size;
   }
   if (s > ntiles) s = ntiles;
-  // the partials live in `out`: splits * (d*d + d) * 4 bytes per (b, h)
-  const long long cap = static_cast<long long>(L) * d * elem_size(out_dt) /
-                        (static_cast<long long>(d * d + d) * 4);
+  // more than one split needs the partials in `out`: splits * (d*d + d) * 4
+  // bytes per (b, h, block)
+  const long long cap = static_cast<long long>(N) * d * elem_size(out_dt) /
+                        (static_cast<long long>(p.nblk) * (d * d + d) * 4);
   if (s > cap) s = cap;
   if (s < 1) s = 1;
-  const int per = static_cast<int>((L + s - 1) / s);
+  const int per = static_cast<int>((Tb + s - 1) / s);
   p.tps = (per + p.kv_tile - 1) / p.kv_tile * p.kv_tile;
-  p.splits = (L + p.tps - 1) / p.tps;
+  p.splits = (Tb + p.tps - 1) / p.tps;
+  p.direct = p.nblk == 1 && p.splits == 1;
+  p.in_place = p.nblk > 1 && p.splits == 1;
+
+  // readout
+  if (p.sweep) {
+    const int unit = 4 * 16 * (d == 128 ? 2 : LA_READOUT_ROWS);
+    p.units_per_block = (Tb + unit - 1) / unit;
+    long long wgs = readout_request > 0 ? readout_request
+                    : d == 128          ? kSweepWorkgroups128
+                                        : kSweepWorkgroups;
+    const long long most = pairs * p.units_per_block;
+    if (wgs > most) wgs = most;
+    if (wgs < 1) wgs = 1;
+    p.readout_wgs = static_cast<int>(wgs);
+  } else {
+    const int ro_unit = 128;  // readout_f32 processes 32-token tiles
+    const long long target = readout_request > 0 ? readout_request
+                             : d == 128            ? kReadoutTargetWorkgroups / 2
+                                                   : kReadoutTargetWorkgroups;
+    const long long per_block = (target + pairs - 1) / pairs;
+    long long tpw = (Tb + per_block - 1) / per_block;
+    if (tpw < 1) tpw = 1;
+    tpw = (tpw + ro_unit - 1) / ro_unit * ro_unit;
+    p.readout_tpw = static_cast<int>(tpw);
+    p.readout_wgs = static_cast<int>(((Tb + tpw - 1) / tpw) * pairs);
+  }
   return p;
 }
 
@@ -131,35 +140,37 @@ int record(const la_launch_opts* o, int i, hipStream_t stream) {
 int launched() { return hipGetLastError() == hipSuccess ? LA_OK : LA_E_HIP; }
 
 template <int D>
-int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int H, int L,
+int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int H, int N,
               const float* state_in, float* dst, hipStream_t stream) {
-  const dim3 grid(p.splits, H, B);
+  const dim3 grid(p.nblk * p.splits, H, B);
   if (in_dt == LA_BF16)
     la::kv_partial_bf16<D><<<grid, la::kv_threads<D>(), 0, stream>>>(
-        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), L, p.tps, state_in, dst);
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, p.T, p.splits, p.tps,
+        state_in, dst);
   else
     la::kv_partial_f32<D><<<grid, la::kBlock, 0, stream>>>(
-        static_cast<const float*>(k), static_cast<const float*>(v), L, p.tps, state_in, dst);
+        static_cast<const float*>(k), static_cast<const float*>(v), N, p.T, p.splits, p.tps,
+        state_in, dst);
   return launched();
 }
 
 template <int D>
-int launch_readout(const Plan& p, const void* q, int in_dt, int out_dt, int B, int H, int L,
-                   const float* state, void* out, float eps, hipStream_t stream) {
+int launch_readout(const Plan& p, const void* q, int out_dt, int B, int H, int N,
+                   const float* states, void* out, float eps, hipStream_t stream) {
   if (p.sweep) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
-    const int total = B * H * p.units_per_head;
+    const int total = B * H * p.nblk * p.units_per_block;
     constexpr int nt = la::sweep_threads<D>();
     if (out_dt == LA_BF16)
       la::readout_sweep_bf16<D, true><<<p.readout_wgs, nt, 0, stream>>>(
-          qq, state, out, L, p.units_per_head, total, eps);
+          qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
     else
       la::readout_sweep_bf16<D, false><<<p.readout_wgs, nt, 0, stream>>>(
-          qq, state, out, L, p.units_per_head, total, eps);
+          qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
     return launched();
   }
-  // float32 queries: per-head workgroups over contiguous token ranges
-  const dim3 grid((L + p.readout_tpw - 1) / p.readout_tpw, H, B);
+  // float32 queries: workgroups over contiguous token ranges of one block
+  const dim3 grid(p.nblk * ((p.T + p.readout_tpw - 1) / p.readout_tpw), H, B);
   const float* qq = static_cast<const float*>(q);
   constexpr size_t smem = la::readout_f32_smem<D>();
   if (out_dt == LA_BF16) {
@@ -167,82 +178,105 @@ int launch_readout(const Plan& p, const void* q, int in_dt, int out_dt, int B, i
         hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
       return LA_E_HIP;
-    la::readout_f32<D, true><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+    la::readout_f32<D, true><<<grid, la::kBlock, smem, stream>>>(qq, states, out, N, p.T, p.nblk,
+                                                                 p.readout_tpw, eps);
   } else {
     if (smem > 65536 &&
         hipFuncSetAttribute(reinterpret_cast<const void*>(&la::readout_f32<D, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, smem) != hipSuccess)
       return LA_E_HIP;
-    la::readout_f32<D, false><<<grid, la::kBlock, smem, stream>>>(qq, state, out, L, p.readout_tpw, eps);
+    la::readout_f32<D, false><<<grid, la::kBlock, smem, stream>>>(qq, states, out, N, p.T, p.nblk,
+                                                                  p.readout_tpw, eps);
   }
   return launched();
 }
 
+// The three stages for any number of blocks.  `states` holds nblk states per
+// (b, h) (one for the chunk and global calls).
 template <int D>
 int run(const Plan& p, const void* q, const void* k, const void* v, const float* state_in,
-        void* out, float* state_out, int B, int H, int L, int in_dt, int out_dt, float eps,
+        void* out, float* states, int B, int H, int N, int in_dt, int out_dt, float eps,
         const la_launch_opts* opts, hipStream_t stream) {
   constexpr int E = D * D + D;
   const int n4 = E / 4;
-  const dim3 red_grid((n4 + la::kWave - 1) / la::kWave, H, B);
   int rc;
   if ((rc = record(opts, 0, stream)) != LA_OK) return rc;
-  float* partials = static_cast<float*>(out);
-  if (p.splits >= 1) {
-    float* dst = p.splits == 1 ? state_out : partials;
-    if ((rc = launch_kv<D>(p, k, v, in_dt, B, H, L, state_in, dst, stream)) != LA_OK) return rc;
+  float* partials = p.direct || p.in_place ? states : static_cast<float*>(out);
+  if (p.nblk >= 1) {
+    if ((rc = launch_kv<D>(p, k, v, in_dt, B, H, N, state_in, partials, stream)) != LA_OK)
+      return rc;
   }
   if ((rc = record(opts, 1, stream)) != LA_OK) return rc;
-  if (p.splits != 1) {
-    la::state_reduce<<<red_grid, la::kBlock, 0, stream>>>(
-        reinterpret_cast<const float4*>(partials), p.splits, n4,
-        reinterpret_cast<const float4*>(state_in), reinterpret_cast<float4*>(state_out));
+  if (p.nblk <= 1 && !p.direct) {
+    // one block (or an empty chunk): partial sums plus S_in
+    const dim3 grid((n4 + la::kWave - 1) / la::kWave, H, B);
+    la::state_reduce<<<grid, la::kBlock, 0, stream>>>(
+        reinterpret_cast<const float4*>(partials), p.nblk == 1 ? p.splits : 0, n4,
+        reinterpret_cast<const float4*>(state_in), reinterpret_cast<float4*>(states));
+    if ((rc = launched()) != LA_OK) return rc;
+  } else if (p.nblk > 1) {
+    const dim3 grid((n4 + la::kBlock - 1) / la::kBlock, H, B);
+    la::state_scan<<<grid, la::kBlock, 0, stream>>>(
+        reinterpret_cast<const float4*>(partials), p.nblk, p.splits, n4,
+        reinterpret_cast<const float4*>(state_in), reinterpret_cast<float4*>(states));
     if ((rc = launched()) != LA_OK) return rc;
   }
   if ((rc = record(opts, 2, stream)) != LA_OK) return rc;
-  if (L > 0) {
-    if ((rc = launch_readout<D>(p, q, in_dt, out_dt, B, H, L, state_out, out, eps, stream)) != LA_OK)
+  if (N > 0) {
+    if ((rc = launch_readout<D>(p, q, out_dt, B, H, N, states, out, eps, stream)) != LA_OK)
       return rc;
   }
   return record(opts, 3, stream);
 }
 
-int forward(const void* q, const void* k, const void* v, const float* state_in, bool chunk,
-            void* out, float* state_out, int B, int H, int L, int d, int in_dt, int out_dt,
-            float eps, const la_launch_opts* opts, hipStream_t stream) {
-  int rc = check_shape(B, H, L, d, in_dt, out_dt);
+// Checks shared by every forward call, then the launches.  `need_state_in`:
+// the chunk call requires it; the global and block-causal calls take NULL as
+// zero.  `states_blocks`: number of states `states` holds per (b, h).
+int forward(const void* q, const void* k, const void* v, const float* state_in,
+            bool need_state_in, bool blockcausal, void* out, float* states, int B, int H, int N,
+            int T, int d, int in_dt, int out_dt, float eps, const la_launch_opts* opts,
+            hipStream_t stream) {
+  int rc = check_shape(B, H, N, d, in_dt, out_dt);
   if (rc != LA_OK) return rc;
+  if (T <= 0) return LA_E_INVAL;
   if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
-  if (state_out == nullptr || (chunk && state_in == nullptr)) return LA_E_INVAL;
-  if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr)) return LA_E_INVAL;
-  const void* ptrs[] = {q, k, v, out, state_in, state_out};
-  for (const void* p : ptrs)
-    if (p != nullptr && !aligned16(p)) return LA_E_ALIGN;
+  if (states == nullptr || (need_state_in && state_in == nullptr)) return LA_E_INVAL;
+  if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr)) return LA_E_INVAL;
+  const void* ptrs[] = {q, k, v, out, state_in, states};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return LA_E_ALIGN;
 
+  const int nblk = N == 0 ? 1 : (N + (T < N ? T : N) - 1) / (T < N ? T : N);
   const size_t bh = static_cast<size_t>(B) * H;
-  const size_t in_bytes = bh * L * d * elem_size(in_dt);
-  const size_t out_bytes = bh * L * d * elem_size(out_dt);
+  const size_t in_bytes = bh * N * d * elem_size(in_dt);
+  const size_t out_bytes = bh * N * d * elem_size(out_dt);
   const size_t st_bytes = bh * (static_cast<size_t>(d) * d + d) * sizeof(float);
-  if (L > 0) {
+  const size_t sts_bytes = st_bytes * nblk;
+  if (N > 0) {
     const void* ins[] = {q, k, v};
-    for (const void* p : ins)
-      if (overlaps(out, out_bytes, p, in_bytes) || overlaps(state_out, st_bytes, p, in_bytes))
+    for (const void* ptr : ins)
+      if (overlaps(out, out_bytes, ptr, in_bytes) || overlaps(states, sts_bytes, ptr, in_bytes))
         return LA_E_ALIAS;
-    if (overlaps(out, out_bytes, state_out, st_bytes) ||
+    if (overlaps(out, out_bytes, states, sts_bytes) ||
         overlaps(out, out_bytes, state_in, st_bytes))
       return LA_E_ALIAS;
   }
-  if (state_in != state_out && overlaps(state_in, st_bytes, state_out, st_bytes)) return LA_E_ALIAS;
+  // one block: state_in may be the state itself (in-place commit)
+  if (nblk == 1 ? (state_in != states && overlaps(state_in, st_bytes, states, sts_bytes))
+                : overlaps(state_in, st_bytes, states, sts_bytes))
+    return LA_E_ALIAS;
 
-  const Plan p = make_plan(B, H, L, d, in_dt, out_dt, opts ? opts->kv_splits : 0,
+  // a block-causal sequence of no tokens has no blocks and no states
+  if (blockcausal && N == 0) return LA_OK;
+  const Plan p = make_plan(B, H, N, T, d, in_dt, out_dt, opts ? opts->kv_splits : 0,
                            opts ? opts->readout_workgroups : 0);
   switch (d) {
     case 32:
-      return run<32>(p, q, k, v, state_in, out, state_out, B, H, L, in_dt, out_dt, eps, opts, stream);
+      return run<32>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, opts, stream);
     case 64:
-      return run<64>(p, q, k, v, state_in, out, state_out, B, H, L, in_dt, out_dt, eps, opts, stream);
+      return run<64>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, opts, stream);
     default:
-      return run<128>(p, q, k, v, state_in, out, state_out, B, H, L, in_dt, out_dt, eps, opts, stream);
+      return run<128>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, opts, stream);
   }
 }
 
@@ -266,28 +300,43 @@ int la_state_reset(float* state, int B, int H, int d, hipStream_t stream) {
 int la_chunk_forward(const void* q, const void* k, const void* v, const float* state_in, void* out,
                      float* state_out, int B, int H, int L, int d, int in_dt, int out_dt, float eps,
                      hipStream_t stream) {
-  return forward(q, k, v, state_in, true, out, state_out, B, H, L, d, in_dt, out_dt, eps, nullptr,
-                 stream);
+  return forward(q, k, v, state_in, true, false, out, state_out, B, H, L, L > 0 ? L : 1, d, in_dt, out_dt,
+                 eps, nullptr, stream);
 }
 
 int la_chunk_forward_ex(const void* q, const void* k, const void* v, const float* state_in,
                         void* out, float* state_out, int B, int H, int L, int d, int in_dt,
                         int out_dt, float eps, const la_launch_opts* opts, hipStream_t stream) {
-  return forward(q, k, v, state_in, true, out, state_out, B, H, L, d, in_dt, out_dt, eps, opts,
-                 stream);
+  return forward(q, k, v, state_in, true, false, out, state_out, B, H, L, L > 0 ? L : 1, d, in_dt, out_dt,
+                 eps, opts, stream);
 }
 
 int la_global_forward(const void* q, const void* k, const void* v, void* out, float* state_out,
                       int B, int H, int N, int d, int in_dt, int out_dt, float eps,
                       hipStream_t stream) {
-  return forward(q, k, v, nullptr, false, out, state_out, B, H, N, d, in_dt, out_dt, eps, nullptr,
-                 stream);
+  return forward(q, k, v, nullptr, false, false, out, state_out, B, H, N, N > 0 ? N : 1, d, in_dt, out_dt,
+                 eps, nullptr, stream);
 }
 
 int la_global_forward_ex(const void* q, const void* k, const void* v, void* out, float* state_out,
                          int B, int H, int N, int d, int in_dt, int out_dt, float eps,
                          const la_launch_opts* opts, hipStream_t stream) {
-  return forward(q, k, v, nullptr, false, out, state_out, B, H, N, d, in_dt, out_dt, eps, opts,
+  return forward(q, k, v, nullptr, false, false, out, state_out, B, H, N, N > 0 ? N : 1, d, in_dt, out_dt,
+                 eps, opts, stream);
+}
+
+int la_blockcausal_forward(const void* q, const void* k, const void* v, const float* state_in,
+                           void* out, float* states, int B, int H, int N, int T, int d, int in_dt,
+                           int out_dt, float eps, hipStream_t stream) {
+  return forward(q, k, v, state_in, false, true, out, states, B, H, N, T, d, in_dt, out_dt, eps, nullptr,
+                 stream);
+}
+
+int la_blockcausal_forward_ex(const void* q, const void* k, const void* v, const float* state_in,
+                              void* out, float* states, int B, int H, int N, int T, int d,
+                              int in_dt, int out_dt, float eps, const la_launch_opts* opts,
+                              hipStream_t stream) {
+  return forward(q, k, v, state_in, false, true, out, states, B, H, N, T, d, in_dt, out_dt, eps, opts,
                  stream);
 }
 
@@ -296,9 +345,9 @@ int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_req
   const int rc = check_shape(B, H, L, d, in_dt, out_dt);
   if (rc != LA_OK) return rc;
   if (kv_splits == nullptr || readout_workgroups == nullptr) return LA_E_INVAL;
-  const Plan p = make_plan(B, H, L, d, in_dt, out_dt, kv_splits_request,
+  const Plan p = make_plan(B, H, L, L > 0 ? L : 1, d, in_dt, out_dt, kv_splits_request,
                            readout_workgroups_request);
-  *kv_splits = p.splits;
+  *kv_splits = p.nblk == 0 ? 0 : p.splits;
   *readout_workgroups = p.readout_wgs;
   return LA_OK;
 }

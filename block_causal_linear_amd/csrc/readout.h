@@ -97,10 +97,13 @@ constexpr int sweep_min_waves() {
   return SweepShape<D>::MIN_WAVES;
 }
 
+// A sequence of N tokens per (b, h) may be cut into blocks of T tokens, each
+// read against its own state states[(b H + h) nblk + c] (the whole-sequence
+// block-causal call); units never straddle a block.  One block: T = N.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void readout_sweep_bf16(
-    const uint16_t* __restrict__ q, const float* __restrict__ state, void* __restrict__ out, int L,
-    int units_per_head, int total_units, float eps) {
+    const uint16_t* __restrict__ q, const float* __restrict__ state, void* __restrict__ out, int N,
+    int T, int nblk, int units_per_block, int total_units, float eps) {
   using Sh = ReadoutShape<D>;
   using Sw = SweepShape<D>;
   constexpr int E = D * D + D;
@@ -130,8 +133,8 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
 
   vecP sraw[8];
   f32x4 zraw[2];
-  auto load_state = [&](int bh) {
-    const float* st = state + static_cast<size_t>(bh) * E;
+  auto load_state = [&](int sb) {  // sb = (b H + h) nblk + block
+    const float* st = state + static_cast<size_t>(sb) * E;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       sraw[j] = *reinterpret_cast<const vecP*>(st + (32 * ps + 8 * g + j) * D + 16 * W * (pc0 / W) +
@@ -159,19 +162,19 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
       frag[buf][fi(ps, NBK, 1)][lane] = make_uint4(l[0], l[1], l[2], l[3]);
     }
   };
-  // Query rows past the end of the head load row L - 1 instead: an MFMA
+  // Query rows past the end of the block load its last row instead: an MFMA
   // output row depends only on its own A row, and those rows are never
   // stored.  phi is applied where the operand is used.
-  auto load_a = [&](uint4 (&a)[R][KS], int bh, int t0) {
-    const uint4* qb = reinterpret_cast<const uint4*>(q + static_cast<size_t>(bh) * L * D);
+  auto load_a = [&](uint4 (&a)[R][KS], int bh, int t0, int te) {
+    const uint4* qb = reinterpret_cast<const uint4*>(q + static_cast<size_t>(bh) * N * D);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int tok = min(t0 + 16 * r + tok_a, L - 1);
+      const int tok = min(t0 + 16 * r + tok_a, te - 1);
 #pragma unroll
       for (int s = 0; s < KS; ++s) a[r][s] = load_q(qb + static_cast<size_t>(tok) * Sh::UPR + 4 * s + g);
     }
   };
-  auto consume = [&](int buf, const uint4 (&qraw)[R][KS], int bh, int t0) {
+  auto consume = [&](int buf, const uint4 (&qraw)[R][KS], int bh, int t0, int te) {
     uint4 a[R][KS];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -209,9 +212,9 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * r + 4 * i + g;
-        if (tok >= L) continue;
+        if (tok >= te) continue;
         const float inv = fast_rcp(accz[r][i] + eps);
-        const size_t row0 = (static_cast<size_t>(bh) * L + tok) * D;
+        const size_t row0 = (static_cast<size_t>(bh) * N + tok) * D;
         const int col = 16 * W * (ch * CB / W) + W * n;
         if constexpr (W == 4) {
           const float o0 = acc[r][0][i] * inv, o1 = acc[r][1][i] * inv;
@@ -238,13 +241,23 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
   // The unit index is uniform across the workgroup, so every wave takes the
   // same number of barriers; waves whose tile lies past the end of a head
   // compute on clamped rows and store nothing.
+  // unit -> (b, h), block, tile of this wave, end of the block
+  auto locate = [&](int u, int& bh, int& sb, int& t0, int& te) {
+    const int upb = units_per_block;
+    bh = u / (nblk * upb);
+    const int rem = u - bh * nblk * upb;
+    const int blk = rem / upb;
+    sb = bh * nblk + blk;
+    t0 = blk * T + ((rem - blk * upb) * 4 + tw) * Sh::TILE;
+    te = min(N, (blk + 1) * T);
+  };
   int unit = blockIdx.x;
   if (unit >= total_units) return;
-  int bh = unit / units_per_head;
-  int t0 = ((unit - bh * units_per_head) * 4 + tw) * Sh::TILE;
+  int bh, sb, t0, te;
+  locate(unit, bh, sb, t0, te);
   uint4 a[R][KS];
-  load_state(bh);
-  load_a(a, bh, t0);
+  load_state(sb);
+  load_a(a, bh, t0, te);
   for (int i = 0;; ++i) {
     const int buf = NBUF == 2 ? (i & 1) : 0;
     // With two buffers, buf was last read before the previous iteration's
@@ -255,16 +268,17 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
     const int next = unit + gridDim.x;
     const bool more = next < total_units;
     const int nu = more ? next : unit;
-    const int nbh = nu / units_per_head;
-    const int nt0 = ((nu - nbh * units_per_head) * 4 + tw) * Sh::TILE;
+    int nbh, nsb, nt0, nte;
+    locate(nu, nbh, nsb, nt0, nte);
     uint4 an[R][KS];
-    load_state(nbh);
-    load_a(an, nbh, nt0);
-    consume(buf, a, bh, t0);
+    load_state(nsb);
+    load_a(an, nbh, nt0, nte);
+    consume(buf, a, bh, t0, te);
     if (!more) break;
     unit = next;
     bh = nbh;
     t0 = nt0;
+    te = nte;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -276,11 +290,13 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
 // float32 queries: plain VALU.  The state sits in LDS; each thread owns
 // (token, column) outputs of a 32-token tile; the denominators are formed
 // once per token.
+// Grid: (blocks x workgroups per block, H, B); workgroup x of block c reads
+// tokens [c T + x tpw, ...) of the block against states[(b H + h) nblk + c].
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(kBlock) void readout_f32(const float* __restrict__ q,
                                                       const float* __restrict__ state,
-                                                      void* __restrict__ out, int L, int tpw,
-                                                      float eps) {
+                                                      void* __restrict__ out, int N, int T,
+                                                      int nblk, int tpw, float eps) {
   constexpr int TT = 32;
   constexpr int E = D * D + D;
   extern __shared__ float smem[];
@@ -289,12 +305,14 @@ __global__ __launch_bounds__(kBlock) void readout_f32(const float* __restrict__ 
   float* sden = sq + TT * D;    // TT
 
   const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
-  const int tb = blockIdx.x * tpw;
-  const int te = min(L, tb + tpw);
+  const int per = gridDim.x / nblk;
+  const int blk = blockIdx.x / per;
+  const int tb = blk * T + (blockIdx.x - blk * per) * tpw;
+  const int te = min(min(N, (blk + 1) * T), tb + tpw);
   const int tid = threadIdx.x;
-  const float* st = state + bh * E;
+  const float* st = state + (bh * nblk + blk) * E;
   for (int e = tid; e < E; e += kBlock) sS[e] = st[e];
-  const float* qb = q + bh * static_cast<size_t>(L) * D;
+  const float* qb = q + bh * static_cast<size_t>(N) * D;
 
   for (int base = tb; base < te; base += TT) {
     __syncthreads();
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(kBlock) void readout_f32(const float* __restrict__ 
       float num = 0.f;
       for (int a = 0; a < D; ++a) num = fmaf(sq[t * D + a], sS[a * D + c], num);
       const float o = num / sden[t];
-      const size_t idx = (bh * L + base + t) * static_cast<size_t>(D) + c;
+      const size_t idx = (bh * N + base + t) * static_cast<size_t>(D) + c;
       if constexpr (OUT_BF16)
         static_cast<uint16_t*>(out)[idx] = to_bf16(o);
       else

@@ -68,6 +68,54 @@ __global__ __launch_bounds__(kBlock) void state_reduce(const float4* __restrict_
   state_out[idx] = t;
 }
 
+// Inclusive prefix over the blocks of a whole sequence: for block c,
+//   S_c = S_{c-1} + sum_s P_{c,s},  S_{-1} = S_in (or 0),
+// written to states[B][H][blocks][d*d + d].  One thread per float4 of one
+// (b, h) state walks the blocks in order; the loads of four blocks' splits
+// are issued together.  Each block's partials are summed in split order and
+// then added to the running state (a fixed order: repeated runs are bitwise
+// identical; against one la_chunk_forward per block only the float32
+// summation order differs).  state_in must not overlap states; partials may
+// be states itself (one split per block: each element is read before the
+// same thread writes it).
+__global__ __launch_bounds__(kBlock) void state_scan(const float4* partials,
+                                                     int nblk, int splits, int n4,
+                                                     const float4* __restrict__ state_in,
+                                                     float4* states) {
+  const int e = blockIdx.x * kBlock + threadIdx.x;
+  if (e >= n4) return;
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  auto add = [](float4& a, const float4& x) {
+    a.x += x.x;
+    a.y += x.y;
+    a.z += x.z;
+    a.w += x.w;
+  };
+  float4 run = state_in != nullptr ? state_in[bh * n4 + e] : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4* p = partials + bh * static_cast<size_t>(nblk) * splits * n4 + e;
+  float4* out = states + bh * static_cast<size_t>(nblk) * n4 + e;
+  constexpr int U = 4;
+  for (int c0 = 0; c0 < nblk; c0 += U) {
+    float4 kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (c0 + u < nblk)
+        for (int s = 0; s < splits; ++s)
+          add(kv[u], p[(static_cast<size_t>(c0 + u) * splits + s) * n4]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c0 + u >= nblk) break;
+      run.x = run.x + kv[u].x;
+      run.y = run.y + kv[u].y;
+      run.z = run.z + kv[u].z;
+      run.w = run.w + kv[u].w;
+      out[static_cast<size_t>(c0 + u) * n4] = run;
+    }
+  }
+}
+
 // Zero fill (used instead of a memset so that callers may graph-capture it).
 __global__ __launch_bounds__(kBlock) void fill_zero(float4* __restrict__ p, size_t n4) {
   const size_t stride = static_cast<size_t>(gridDim.x) * kBlock;

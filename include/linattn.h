@@ -113,10 +113,36 @@ int la_global_forward(const void* q, const void* k, const void* v,
                       float eps, hipStream_t stream);
 
 /*
+ * la_blockcausal_forward - a whole sequence in the block-causal form, in one
+ * call (the form a block-wise autoregressive model is trained with; [TR]:
+ * the video is cut into blocks, block n reads KVsum of blocks 1..n-1 plus
+ * its own KV, and the computation splits along token order).  The N tokens
+ * of every (b, h) are cut into C = ceil(N / T) blocks of T tokens (the last
+ * may be shorter); block n's queries read S_in + KV_1 + ... + KV_n.  The
+ * result equals C calls of la_chunk_forward in order with the state carried
+ * (up to float32 summation order).
+ *   q, k, v   : [B][H][N][d] in_dt, read.
+ *   state_in  : [B][H][d*d+d] float32, read; NULL means zeros.  Must not
+ *               overlap `states`.
+ *   out       : [B][H][N][d] out_dt, written (and used as scratch).
+ *   states    : [B][H][C][d*d+d] float32, written: the state after every
+ *               block; states[..][C-1] is the state after the sequence.
+ *   T         : tokens per block, >= 1 (T >= N: one block, the global form
+ *               plus state_in).
+ * N = 0 is allowed and does nothing.  Errors as for la_chunk_forward
+ * (T <= 0 gives LA_E_INVAL).
+ */
+int la_blockcausal_forward(const void* q, const void* k, const void* v,
+                           const float* state_in, void* out, float* states,
+                           int B, int H, int N, int T, int d, int in_dt, int out_dt,
+                           float eps, hipStream_t stream);
+
+/*
  * Launch options for the _ex variants (same computation, same rules):
- *   kv_splits     : token splits per (b, h) for the KV reduction; 0 lets the
- *                   library choose.  A request is clamped to [1, the number
- *                   of 64-token tiles] and to what the scratch in `out` holds.
+ *   kv_splits     : token splits per (b, h) and block for the KV reduction; 0
+ *                   lets the library choose.  A request is clamped to [1,
+ *                   the number of 64-token tiles] and to what the scratch in
+ *                   `out` holds.
  *                   Results differ between split counts only by float32
  *                   summation order.
  *   readout_workgroups: workgroups of the readout grid; 0 lets the library
@@ -125,8 +151,9 @@ int la_global_forward(const void* q, const void* k, const void* v,
  *                   clamped to one wave per tile; otherwise it is rounded to
  *                   whole workgroups per (b, h).  Results do not depend on it.
  *   stage_events  : NULL, or 4 caller-created events recorded on `stream`
- *                   before the KV reduction, before the split reduce, before
- *                   the readout, and after the readout (for timing).
+ *                   before the KV reduction, before the split reduce (or the
+ *                   prefix over blocks), before the readout, and after the
+ *                   readout (for timing).
  */
 typedef struct la_launch_opts {
   int kv_splits;
@@ -143,6 +170,11 @@ int la_global_forward_ex(const void* q, const void* k, const void* v,
                          void* out, float* state_out,
                          int B, int H, int N, int d, int in_dt, int out_dt,
                          float eps, const la_launch_opts* opts, hipStream_t stream);
+
+int la_blockcausal_forward_ex(const void* q, const void* k, const void* v,
+                              const float* state_in, void* out, float* states,
+                              int B, int H, int N, int T, int d, int in_dt, int out_dt,
+                              float eps, const la_launch_opts* opts, hipStream_t stream);
 
 /*
  * la_plan - the launch shape a forward call with these arguments (and the

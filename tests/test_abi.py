@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 1
+    assert la.abi_version() == 2
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -96,6 +96,33 @@ def test_chunk_rejects(kw, code):
 ])
 def test_global_rejects(kw, code):
     assert glob(**kw) == code
+
+
+def bc(q=A, k=2 * A, v=3 * A, si=4 * A, out=5 * A, sts=6 * A, B=1, H=2, N=640, T=64, d=64,
+       idt=BF16, odt=F32, eps=1e-6):
+    return la.lib().la_blockcausal_forward(q, k, v, si, out, sts, B, H, N, T, d, idt, odt, eps,
+                                           None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), la.LA_E_INVAL),
+    (dict(T=-3), la.LA_E_INVAL),
+    (dict(N=-1), la.LA_E_INVAL),
+    (dict(sts=None), la.LA_E_INVAL),
+    (dict(d=96), la.LA_E_UNSUPPORTED),
+    (dict(si=4 * A + 8), la.LA_E_ALIGN),
+    (dict(si=6 * A + 16640 * 3), la.LA_E_ALIAS),   # state_in inside states (block 3 of head 0)
+    (dict(si=6 * A), la.LA_E_ALIAS),               # with several blocks even equal is illegal
+    (dict(out=6 * A + 64), la.LA_E_ALIAS),         # out overlaps states
+    (dict(sts=3 * A + 1024), la.LA_E_ALIAS),       # states inside v
+])
+def test_blockcausal_rejects(kw, code):
+    assert bc(**kw) == code
+
+
+def test_blockcausal_empty_is_a_no_op():
+    # N = 0: no blocks, nothing is written or launched (fake pointers are fine)
+    assert bc(N=0, q=None, k=None, v=None, out=None) == la.LA_OK
 
 
 def test_state_reset_rejects():

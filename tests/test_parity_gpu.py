@@ -302,3 +302,134 @@ def test_binding_rejects_bad_buffers():
         la.chunk_forward(x, x, x, st, out=out, state_out=out.view(-1)[: d * d + d].view(1, 1, -1),
                          eps=EPS)
     assert e.value.status == la.LA_E_ALIAS
+
+
+# ---------------------------------------------------------------------------
+# whole-sequence block-causal call (one call for all blocks)
+
+
+def _prefix_ref(Q, K, V, T, S_in, z_in):
+    """Oracle route that takes every block's KV first, prefix-sums them and
+    then reads each block's queries (oracle.prefix_forward), plus S_in."""
+    N = Q.shape[2]
+    bounds = list(range(0, N, T)) + [N]
+    O, S_pre, z_pre = oracle.prefix_forward(Q, K, V, bounds, EPS)
+    if S_in is not None:
+        # a non-zero initial state adds to every prefix; re-read the queries
+        S_pre = S_pre + S_in[None]
+        z_pre = z_pre + z_in[None]
+        for n in range(len(bounds) - 1):
+            a, b = bounds[n], bounds[n + 1]
+            O[:, :, a:b] = oracle.readout(Q[:, :, a:b], S_pre[n], z_pre[n], EPS)
+    return O, S_pre, z_pre
+
+
+def _states_err(got, S_pre, z_pre):
+    """max normwise error over blocks of a [B, H, C, d*d + d] states tensor."""
+    worst = 0.0
+    for n in range(S_pre.shape[0]):
+        es, ez = state_err(got[:, :, n], S_pre[n], z_pre[n])
+        worst = max(worst, es, ez)
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d,N,T", [(64, 1000, 64), (64, 2085, 500), (32, 777, 7), (128, 1300, 256),
+                                   (64, 300, 1), (64, 640, 640), (64, 500, 900), (128, 100, 33)])
+def test_blockcausal_small(dtype, d, N, T):
+    B, H = 2, 3
+    Q, K, V = workloads.random_qkv(2000 + N + T, B, H, N, d, dtype=dtype)
+    S_in, z_in = workloads.random_state(N + 7, B, H, d)
+    S_in, z_in = S_in.astype(np.float64), z_in.astype(np.float64)
+    O_ref, S_pre, z_pre = _prefix_ref(Q, K, V, T, S_in, z_in)
+    st_in = torch.from_numpy(state_np(S_in, z_in)).cuda()
+    out, states = la.blockcausal_forward(dev(Q, dtype), dev(K, dtype), dev(V, dtype), T,
+                                         state_in=st_in, eps=EPS)
+    torch.cuda.synchronize()
+    eo = out_err(host(out), O_ref)
+    es = _states_err(host(states), S_pre, z_pre)
+    report(f"blockcausal {dtype} d={d} N={N} T={T}", out=eo, states=es)
+    assert eo <= TOL[dtype] and es <= TOL[dtype], (eo, es)
+    assert torch.equal(st_in.cpu(), torch.from_numpy(state_np(S_in, z_in)))  # state_in untouched
+
+
+def test_blockcausal_matches_chunk_calls():
+    """One block-causal call == the same blocks through la_chunk_forward with
+    the state carried (float32 summation order aside); zero initial state."""
+    B, H, N, T, d = 1, 4, 5000, 1024, 64
+    Q, K, V = workloads.random_qkv(31, B, H, N, d)
+    q, k, v = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    out, states = la.blockcausal_forward(q, k, v, T, eps=EPS)
+    st = la.new_state(B, H, d)
+    for n, a in enumerate(range(0, N, T)):
+        b = min(N, a + T)
+        o, st = la.chunk_forward(q[:, :, a:b].contiguous(), k[:, :, a:b].contiguous(),
+                                 v[:, :, a:b].contiguous(), st, state_out=st, eps=EPS)
+        torch.cuda.synchronize()
+        assert out_err(host(out[:, :, a:b]), host(o)) < 1e-5, n
+        assert out_err(host(states[:, :, n]).reshape(B, H, -1, 1),
+                       host(st).reshape(B, H, -1, 1)) < 1e-5, n
+    # repeated runs are bitwise identical
+    out2, states2 = la.blockcausal_forward(q, k, v, T, eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(states, states2)
+
+
+def test_blockcausal_480p_1min_one_call():
+    """The 1-minute 480p stream (12 blocks x 32,760 tokens, 16 heads) in one
+    call, checked block by block against the prefix route."""
+    w = workloads.WORKLOADS[4]
+    N, T = w.L * w.chunks, w.L
+    q = torch.empty((w.B, w.H, N, w.d), dtype=torch.bfloat16, device="cuda")
+    k, v = torch.empty_like(q), torch.empty_like(q)
+    blocks = []
+    for n in range(w.chunks):
+        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
+        sl = slice(n * T, (n + 1) * T)
+        q[:, :, sl], k[:, :, sl], v[:, :, sl] = dev(Qn, "bf16"), dev(Kn, "bf16"), dev(Vn, "bf16")
+        blocks.append((Qn, Kn, Vn))
+    out, states = la.blockcausal_forward(q, k, v, T, eps=EPS)
+    torch.cuda.synchronize()
+    KVs, ks, worst = [], [], [0.0, 0.0]
+    for n, (Qn, Kn, Vn) in enumerate(blocks):
+        KV, kk = oracle.kv_of_block(Kn, Vn)
+        KVs.append(KV)
+        ks.append(kk)
+        S = np.sum(np.stack(KVs), axis=0)
+        z = np.sum(np.stack(ks), axis=0)
+        O_ref = oracle.readout(Qn, S, z, EPS)
+        eo = out_err(host(out[:, :, n * T:(n + 1) * T]), O_ref)
+        es = max(state_err(host(states[:, :, n]), S, z))
+        report(f"480p one-call block {n}", out=eo, state=es)
+        worst = [max(worst[0], eo), max(worst[1], es)]
+    assert max(worst) <= TOL["bf16"], worst
+
+
+def test_blockcausal_long_horizon_d128_one_call():
+    """The 40-block d = 128 long-horizon sequence (B=4, H=16, 163,840 tokens)
+    in one call: every block's state, and the outputs of every fourth block
+    and the last, against the fp64 carried state."""
+    w = workloads.WORKLOADS[5]
+    N, T = w.L * w.chunks, w.L
+    q = torch.empty((w.B, w.H, N, w.d), dtype=torch.bfloat16, device="cuda")
+    k, v = torch.empty_like(q), torch.empty_like(q)
+    for n in range(w.chunks):
+        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
+        sl = slice(n * T, (n + 1) * T)
+        q[:, :, sl], k[:, :, sl], v[:, :, sl] = dev(Qn, "bf16"), dev(Kn, "bf16"), dev(Vn, "bf16")
+    out, states = la.blockcausal_forward(q, k, v, T, eps=EPS)
+    torch.cuda.synchronize()
+    S = np.zeros((w.B, w.H, w.d, w.d))
+    z = np.zeros((w.B, w.H, w.d))
+    worst = 0.0
+    for n in range(w.chunks):
+        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
+        KV, kk = oracle.kv_of_block(Kn, Vn)
+        S, z = S + KV, z + kk
+        es = max(state_err(host(states[:, :, n]), S, z))
+        eo = 0.0
+        if n % 4 == 0 or n == w.chunks - 1:
+            eo = out_err(host(out[:, :, n * T:(n + 1) * T]), oracle.readout(Qn, S, z, EPS))
+        report(f"long-horizon one-call block {n}", out=eo, state=es)
+        worst = max(worst, eo, es)
+    assert worst <= TOL["bf16"], worst
