@@ -430,6 +430,8 @@ def test_blockcausal_long_horizon_d128_one_call():
         eo = 0.0
         if n % 4 == 0 or n == w.chunks - 1:
             eo = out_err(host(out[:, :, n * T:(n + 1) * T]), oracle.readout(Qn, S, z, EPS))
-        report(f"long-horizon one-call block {n}", out=eo, state=es)
+            report(f"long-horizon one-call block {n}", out=eo, state=es)
+        else:
+            report(f"long-horizon one-call block {n}", state=es)
         worst = max(worst, eo, es)
     assert worst <= TOL["bf16"], worst
