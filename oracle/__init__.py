@@ -39,6 +39,12 @@ the HIP library implements):
   ([TR]: each block uses KVsum plus its *own* KV).  Token j is visible to
   query i iff block(j) <= block(i).
 
+Gradients (``readout_backward``, ``kv_backward``, ``blockcausal_backward``)
+are the chain rule applied to the forward definition above, nothing more:
+the pages train the model with the same attention ([EN] abstract; [TR]:
+block-causal attention in training) but print no gradient formula.  The
+derivative of max(x, 0) is taken as 0 at x = 0.
+
 Layout: every tensor is a numpy array [B, H, T, d]; a state is a pair
 (S [B, H, d, d], z [B, H, d]) with S[a, c] = sum_t phi(k_t)[a] v_t[c].
 All arithmetic is float64 (or exact rationals in ``quadratic_exact``).
@@ -59,6 +65,9 @@ __all__ = [
     "quadratic_forward",
     "quadratic_exact",
     "zero_state",
+    "readout_backward",
+    "kv_backward",
+    "blockcausal_backward",
 ]
 
 
@@ -208,3 +217,105 @@ def quadratic_exact(q, k, v, block_id, eps):
                 acc[c] += w * Fraction(v[j][c])
         out.append([acc[c] / (wsum + eps) for c in range(d)])
     return out
+
+
+# --------------------------------------------------------------------------
+# Gradients.  For a loss L with dO = dL/dO and (optionally) dL/dS_n, dL/dz_n
+# for the state after every block, the chain rule through the definitions
+# above gives everything below; no step is fused or reordered beyond it.
+
+
+def readout_backward(Q, S, z, dO, eps):
+    """Gradients of ``readout`` w.r.t. its queries and its state.
+
+    With num_i = phi(q_i)^T S, den_i = phi(q_i) . z + eps, o_i = num_i / den_i:
+      dnum_i = do_i / den_i,   dden_i = -(do_i . o_i) / den_i
+      dphi(q_i) = S dnum_i + dden_i z,   dq_i = dphi(q_i) * [q_i > 0]
+      dS = sum_i phi(q_i) dnum_i^T,      dz = sum_i dden_i phi(q_i)
+    Returns (dQ, dS, dz).
+    """
+    fQ = phi(Q)
+    dO = _f64(dO)
+    S = _f64(S)
+    z = _f64(z)
+    den = np.matmul(fQ, z[..., :, None]) + float(eps)          # [B,H,T,1]
+    O = np.matmul(fQ, S) / den
+    dnum = dO / den
+    dden = -np.sum(dO * O, axis=-1, keepdims=True) / den       # [B,H,T,1]
+    dfQ = np.matmul(dnum, np.swapaxes(S, -1, -2)) + dden * z[..., None, :]
+    dQ = np.where(_f64(Q) > 0.0, dfQ, 0.0)
+    fQt = np.swapaxes(fQ, -1, -2)
+    dS = np.matmul(fQt, dnum)
+    dz = np.matmul(fQt, dden)[..., 0]
+    return dQ, dS, dz
+
+
+def kv_backward(K, V, dKV, dk):
+    """Gradients of ``kv_of_block`` given dL/dKV ([B,H,d,d]) and dL/dk
+    ([B,H,d]).  KV = sum_j phi(k_j) v_j^T and k = sum_j phi(k_j), so
+      dphi(k_j) = dKV v_j + dk,   dk_j = dphi(k_j) * [k_j > 0],
+      dv_j = dKV^T phi(k_j).
+    Returns (dK, dV)."""
+    fK = phi(K)
+    V = _f64(V)
+    dKV = _f64(dKV)
+    dfK = np.matmul(V, np.swapaxes(dKV, -1, -2)) + _f64(dk)[..., None, :]
+    dK = np.where(_f64(K) > 0.0, dfK, 0.0)
+    dV = np.matmul(fK, dKV)
+    return dK, dV
+
+
+def _suffix_sums(xs):
+    """[x_0, ..., x_{C-1}] -> [sum_{m >= n} x_m for n in 0..C-1]."""
+    out = [None] * len(xs)
+    acc = None
+    for n in range(len(xs) - 1, -1, -1):
+        acc = xs[n] if acc is None else acc + xs[n]
+        out[n] = acc
+    return out
+
+
+def blockcausal_backward(Q, K, V, bounds, dO, eps, S0=None, z0=None, dS=None, dz=None):
+    """Gradients of the block-causal form over a whole sequence.
+
+    The forward: S_n = S0 + KV_1 + ... + KV_n (and z_n likewise) for the
+    blocks given by ``bounds`` (as in ``prefix_forward``), and block n's
+    queries read (S_n, z_n) ([TR]: KVsum plus the block's own KV).  Since
+    KV_m enters S_n for every n >= m, its gradient is the suffix sum
+      R_m = sum_{n >= m} (dL/dS_n),
+    where dL/dS_n collects block n's readout gradient plus the caller's
+    dS[n] (the gradient of the state output after block n, zero if None).
+    dL/dS0 = R_1 because S0 enters every S_n.
+
+    Q, K, V, dO: [B,H,T,d].  S0 [B,H,d,d], z0 [B,H,d] (None: zeros).
+    dS [C,B,H,d,d], dz [C,B,H,d] or None.
+    Returns (dQ, dK, dV, dS0, dz0).
+    """
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    B, H, T, d = Q.shape
+    C = len(bounds) - 1
+    if S0 is None:
+        S0, z0 = zero_state(B, H, d)
+    S, z = _f64(S0), _f64(z0)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(Q)
+    dV = np.zeros_like(Q)
+    GS, Gz = [], []
+    for n in range(C):
+        a, b = bounds[n], bounds[n + 1]
+        KV, k = kv_of_block(K[:, :, a:b], V[:, :, a:b])
+        S, z = S + KV, z + k
+        dQn, dSn, dzn = readout_backward(Q[:, :, a:b], S, z, dO[:, :, a:b], eps)
+        dQ[:, :, a:b] = dQn
+        if dS is not None:
+            dSn = dSn + _f64(dS[n])
+            dzn = dzn + _f64(dz[n])
+        GS.append(dSn)
+        Gz.append(dzn)
+    RS, Rz = _suffix_sums(GS), _suffix_sums(Gz)
+    for n in range(C):
+        a, b = bounds[n], bounds[n + 1]
+        dK[:, :, a:b], dV[:, :, a:b] = kv_backward(K[:, :, a:b], V[:, :, a:b], RS[n], Rz[n])
+    if C == 0:
+        return dQ, dK, dV, np.zeros((B, H, d, d)), np.zeros((B, H, d))
+    return dQ, dK, dV, RS[0], Rz[0]
