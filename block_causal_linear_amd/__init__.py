@@ -9,7 +9,8 @@ rejected, an exception is raised.
 
 Shapes: q, k, v and out are [B, H, L, d]; a state is [B, H, d*d + d] float32
 (S[a, c] at a*d + c, then z).  d is 32, 64 or 128; q/k/v are float32 or
-bfloat16; out is float32 (default) or bfloat16.
+bfloat16; out is float32 (default) or bfloat16.  The backward calls take
+dO in float32 or bfloat16 and return dq, dk, dv in that type.
 """
 
 import ctypes
@@ -43,6 +44,7 @@ _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_Z = ctypes.c_size_t
 
 _SIGNATURES = {
     "la_state_reset": [_P, _I, _I, _I, _P],
@@ -55,6 +57,15 @@ _SIGNATURES = {
     "la_blockcausal_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "la_blockcausal_forward_ex": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                   ctypes.POINTER(LaunchOpts), _P],
+    "la_backward_workspace_size": [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)],
+    "la_blockcausal_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                _I, _I, _F, _P, _Z, _P],
+    "la_blockcausal_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                   _I, _I, _I, _F, _P, _Z, ctypes.POINTER(LaunchOpts), _P],
+    "la_chunk_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
+                          _P, _Z, _P],
+    "la_global_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
+                           _P],
     "la_plan": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "la_status_string": [_I],
     "la_abi_version": [],
@@ -257,6 +268,132 @@ def blockcausal_forward(q, k, v, T, state_in=None, out=None, states=None, eps=DE
         rc = L_.la_blockcausal_forward_ex(*args, ctypes.byref(o), _stream(q.device))
     _check(rc, "la_blockcausal_forward")
     return out, states
+
+
+def backward_workspace_size(B, H, N, T, d, in_dtype=torch.bfloat16):
+    """Bytes of workspace a backward call needs (T = N for the chunk and
+    global calls)."""
+    z = ctypes.c_size_t()
+    _check(lib().la_backward_workspace_size(B, H, N, max(int(T), 1), d, _DTYPE[in_dtype],
+                                            ctypes.byref(z)), "la_backward_workspace_size")
+    return z.value
+
+
+def _prepare_grads(q, k, v, dout, dq, dk, dv):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, N, d]")
+    _need(dout, "dout")
+    if not (q.shape == k.shape == v.shape == dout.shape):
+        raise ValueError("q, k, v, dout shapes differ")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPE:
+        raise TypeError("q, k, v must share one dtype, float32 or bfloat16")
+    if dout.dtype not in _DTYPE or dout.device != q.device:
+        raise TypeError("dout must be float32 or bfloat16 on q's device")
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty(q.shape, dtype=dout.dtype, device=q.device)
+        _need(t, name, dout.dtype)
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must be [B, H, N, d] on q's device")
+        grads.append(t)
+    return grads
+
+
+def _workspace(workspace, need, device):
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds fewer than {need} bytes")
+    return workspace
+
+
+def _state_like(t, shape, name, device):
+    _need(t, name, torch.float32)
+    if tuple(t.shape) != tuple(shape) or t.device != device:
+        raise ValueError(f"{name} must be {list(shape)} on q's device")
+
+
+def blockcausal_backward(q, k, v, states, dout, T, dstates=None, want_dstate_in=False,
+                         eps=DEFAULT_EPS, dq=None, dk=None, dv=None, dstate_in=None,
+                         workspace=None, kv_splits=0, readout_workgroups=0,
+                         stage_events=None):
+    """Gradients of blockcausal_forward(q, k, v, T, ...) for the upstream
+    gradient dout (and dstates, the gradient of the returned states, or
+    None).  `states` is what the forward returned.  Returns
+    (dq, dk, dv, dstate_in) with dstate_in the gradient of the forward's
+    state_in ([B, H, d*d + d], or None unless asked for)."""
+    dq, dk, dv = _prepare_grads(q, k, v, dout, dq, dk, dv)
+    B, H, N, d = q.shape
+    T = int(T)
+    if T < 1:
+        raise ValueError("T must be >= 1")
+    C = -(-N // T) if N > 0 else 0
+    _state_like(states, (B, H, C, d * d + d), "states", q.device)
+    if dstates is not None:
+        _state_like(dstates, (B, H, C, d * d + d), "dstates", q.device)
+    if want_dstate_in and dstate_in is None:
+        dstate_in = torch.empty((B, H, d * d + d), dtype=torch.float32, device=q.device)
+    if dstate_in is not None:
+        _state_like(dstate_in, (B, H, d * d + d), "dstate_in", q.device)
+    need = backward_workspace_size(B, H, N, T, d, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    o = _opts(kv_splits, readout_workgroups, stage_events)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(states), _ptr(dout), _ptr(dstates), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dstate_in), B, H, N, T, d, _DTYPE[q.dtype],
+            _DTYPE[dout.dtype], float(eps), _ptr(workspace), ws_bytes)
+    L_ = lib()
+    if o is None:
+        rc = L_.la_blockcausal_backward(*args, _stream(q.device))
+    else:
+        rc = L_.la_blockcausal_backward_ex(*args, ctypes.byref(o), _stream(q.device))
+    _check(rc, "la_blockcausal_backward")
+    return dq, dk, dv, dstate_in
+
+
+def chunk_backward(q, k, v, state_out, dout, dstate_out=None, want_dstate_in=True,
+                   eps=DEFAULT_EPS, dq=None, dk=None, dv=None, dstate_in=None, workspace=None):
+    """Gradients of chunk_forward(q, k, v, state_in) -> (out, state_out) for
+    the upstream gradients dout and dstate_out (None: zero).  Returns
+    (dq, dk, dv, dstate_in)."""
+    dq, dk, dv = _prepare_grads(q, k, v, dout, dq, dk, dv)
+    B, H, L, d = q.shape
+    _state_like(state_out, (B, H, d * d + d), "state_out", q.device)
+    if dstate_out is not None:
+        _state_like(dstate_out, (B, H, d * d + d), "dstate_out", q.device)
+    if want_dstate_in and dstate_in is None:
+        dstate_in = torch.empty((B, H, d * d + d), dtype=torch.float32, device=q.device)
+    if dstate_in is not None:
+        _state_like(dstate_in, (B, H, d * d + d), "dstate_in", q.device)
+    need = backward_workspace_size(B, H, L, L, d, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().la_chunk_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state_out), _ptr(dout), _ptr(dstate_out), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(dstate_in), B, H, L, d, _DTYPE[q.dtype], _DTYPE[dout.dtype],
+        float(eps), _ptr(workspace), ws_bytes, _stream(q.device)), "la_chunk_backward")
+    return dq, dk, dv, dstate_in
+
+
+def global_backward(q, k, v, state, dout, eps=DEFAULT_EPS, dq=None, dk=None, dv=None,
+                    workspace=None):
+    """Gradients of global_forward(q, k, v) -> (out, state) for the upstream
+    gradient dout.  Returns (dq, dk, dv)."""
+    dq, dk, dv = _prepare_grads(q, k, v, dout, dq, dk, dv)
+    B, H, N, d = q.shape
+    _state_like(state, (B, H, d * d + d), "state", q.device)
+    need = backward_workspace_size(B, H, N, N, d, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().la_global_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, N, d, _DTYPE[q.dtype], _DTYPE[dout.dtype], float(eps), _ptr(workspace), ws_bytes,
+        _stream(q.device)), "la_global_backward")
+    return dq, dk, dv
 
 
 def plan(B, H, L, d, in_dtype=torch.bfloat16, out_dtype=torch.float32, kv_splits=0,

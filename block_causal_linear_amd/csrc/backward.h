@@ -1,0 +1,696 @@
+// Gradients of the block-causal form (the global form is one block), for
+// training with the same attention the model samples with ("SANA-Video:
+// Efficient Video Generation with Block Linear Diffusion Transformer",
+// abstract; "Nvidia, MIT ve diğerleri video yapay zeka devrimini
+// başlattı", section "Sabit Bellekli KV önbelleğe alma mekanizması").
+//
+// The forward, per (b, h): S_n = S_0 + KV_1 + ... + KV_n (z_n likewise) and
+// o_i = phi(q_i)^T S_n / (phi(q_i) . z_n + eps) for the queries of block n.
+// For an upstream gradient dO (and optionally dS_n, dz_n on every block's
+// state) the chain rule gives, with den_i = phi(q_i) . z_n + eps:
+//   w_i    = S_n do_i                      (d)
+//   t_i    = phi(q_i) . w_i                (= do_i . num_i)
+//   dq_i   = (w_i - (t_i / den_i) z_n) / den_i * [q_i > 0]
+//   G_n    = sum_i phi(q_i) (do_i / den_i)^T,  g_n = sum_i (-t_i / den_i^2) phi(q_i)
+//   R_m    = sum_{n >= m} (G_n + dS_n),        r_m likewise (suffix over blocks)
+//   dk_j   = (R_m v_j + r_m) * [k_j > 0],      dv_j = R_m^T phi(k_j)
+//   dS_0   = R_1,  dz_0 = r_1.
+// The derivative of max(x, 0) is taken as 0 at x = 0.
+//
+// Three launches: bwd_query (dQ and the per-split partials of (G_n, g_n)),
+// state_suffix_scan (R_m from the partials), bwd_key (dK, dV).
+#pragma once
+
+#include "la_common.h"
+#include "kv_reduce.h"
+
+namespace la {
+
+template <int D>
+struct BwdShape {
+  static constexpr int KS = D / 32;            // 32-feature k-steps
+  static constexpr int NBK = D / 16;           // 16-column accumulator blocks
+  static constexpr int W = D == 32 ? 2 : 4;    // values per vector store
+  static constexpr int GRP = NBK / W;          // vector stores per token row
+  static constexpr int UPR = D / 8;            // 16-byte units per bf16 token row
+  static constexpr int TT = 64;                // tokens per tile: 16 per wave
+  static constexpr int NT = 4 * kWave;         // four waves
+  static constexpr int BR = D / 2;             // G block of one wave (2 x 2 waves)
+  static constexpr int NR = BR / 16;
+  static constexpr int NF = KS * NBK * 2;      // operand fragments of one d x d matrix
+};
+
+// Accumulator column n of block nb holds feature 16 W (nb / W) + W n + nb % W
+// (the readout's placement): each lane owns W consecutive features per
+// group, so one vector store per (token, group) writes them, and the 16
+// lanes of a row group cover 16 W consecutive features.
+template <int D>
+__device__ __forceinline__ int bwd_col(int nb, int n) {
+  constexpr int W = BwdShape<D>::W;
+  return 16 * W * (nb / W) + W * n + nb % W;
+}
+
+// MFMA B operand "rows of X": B[k = c][n] = X[bwd_col(nb, n)][32 s + c] for
+// the products sum_c X[a][c] y[c] with y in the A operand (tokens x c).
+// frag[(s NBK + nb) 2 + {hi, lo}][lane]; the four waves share the work.
+template <int D>
+__device__ void build_row_frags(const float* X, uint4 (*frag)[kWave], int wave, int lane) {
+  using Sh = BwdShape<D>;
+  const int n = lane & 15, g = lane >> 4;
+  for (int p = wave; p < Sh::KS * Sh::NBK; p += 4) {
+    const int s = p / Sh::NBK, nb = p % Sh::NBK;
+    const float* src = X + bwd_col<D>(nb, n) * D + 32 * s + 8 * g;
+    const float4 x0 = *reinterpret_cast<const float4*>(src);
+    const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+    uint32_t h[4], l[4];
+    split_bf16x2(x0.x, x0.y, &h[0], &l[0]);
+    split_bf16x2(x0.z, x0.w, &h[1], &l[1]);
+    split_bf16x2(x1.x, x1.y, &h[2], &l[2]);
+    split_bf16x2(x1.z, x1.w, &h[3], &l[3]);
+    frag[2 * p][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+    frag[2 * p + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+}
+
+// MFMA B operand "columns of X": B[k = a][n] = X[32 s + a][bwd_col(nb, n)]
+// for the products sum_a x[a] X[a][c] with x in the A operand (tokens x a).
+template <int D>
+__device__ void build_col_frags(const float* X, uint4 (*frag)[kWave], int wave, int lane) {
+  using Sh = BwdShape<D>;
+  const int n = lane & 15, g = lane >> 4;
+  for (int p = wave; p < Sh::KS * Sh::NBK; p += 4) {
+    const int s = p / Sh::NBK, nb = p % Sh::NBK;
+    const float* src = X + (32 * s + 8 * g) * D + bwd_col<D>(nb, n);
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = src[j * D];
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) split_bf16x2(x[j], x[j + 1], &h[j / 2], &l[j / 2]);
+    frag[2 * p][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+    frag[2 * p + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+}
+
+// W bfloat16 values of one token row (features f .. f + W - 1) as floats.
+template <int W>
+__device__ __forceinline__ void load_row_w(const uint16_t* p, float (&x)[W]) {
+  if constexpr (W == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  } else {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    x[0] = __uint_as_float(u << 16);
+    x[1] = __uint_as_float(u & 0xFFFF0000u);
+  }
+}
+
+// W values to one token row of a gradient (float32 or bfloat16).
+template <int W, bool BF16>
+__device__ __forceinline__ void store_row_w(void* base, size_t idx, const float (&x)[W]) {
+  if constexpr (BF16) {
+    uint16_t* p = static_cast<uint16_t*>(base) + idx;
+    if constexpr (W == 4) {
+      *reinterpret_cast<u32x2*>(p) = u32x2{pack2(to_bf16(x[0]), to_bf16(x[1])),
+                                           pack2(to_bf16(x[2]), to_bf16(x[3]))};
+    } else {
+      *reinterpret_cast<uint32_t*>(p) = pack2(to_bf16(x[0]), to_bf16(x[1]));
+    }
+  } else {
+    float* p = static_cast<float*>(base) + idx;
+    if constexpr (W == 4) {
+      *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    } else {
+      *reinterpret_cast<f32x2*>(p) = f32x2{x[0], x[1]};
+    }
+  }
+}
+
+// Eight consecutive dO values of one token (float32 or bfloat16 in HBM).
+template <bool BF16>
+struct DoRow;
+template <>
+struct DoRow<false> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const void* base, size_t elem) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    a = p[0];
+    b = p[1];
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+template <>
+struct DoRow<true> {
+  uint4 u;
+  __device__ __forceinline__ void load(const void* base, size_t elem) {
+    u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __uint_as_float(w[j] << 16);
+      x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// bwd_query_bf16: dQ and the partials of (G_n, g_n), bfloat16 queries.
+//
+// Grid (blocks x splits, H, B), as the KV reduction: workgroup (c, s) covers
+// a contiguous token range of block c and writes its partial to
+// dst[((b H + h) C + c) splits + s] (d*d floats of G, then d of g).
+//
+// Per 64-token tile, four waves:
+//  1. wave w takes tokens 16 w .. 16 w + 15 as MFMA rows (A row m holds token
+//     4 (m % 4) + m / 4, so each store instruction writes 4 consecutive
+//     token rows): den from phi(Q) against z, w_i from dO (bf16 hi/lo) against
+//     S (hi/lo, "rows of S"); in the epilogue t_i is a 16-lane sum, dq is
+//     formed and stored, and 1/den, dden go to LDS; phi(Q) rows go to an LDS
+//     tile (token-major, swizzled as in the KV reduction);
+//  2. after a barrier each lane scales its dO by 1/den and writes dnum as a
+//     bf16 hi/lo pair into two more LDS tiles;
+//  3. after a barrier the waves accumulate G (2 x 2 blocks of d/2 x d/2) over
+//     the tile's tokens with transposing LDS reads, as the KV reduction
+//     does; waves in block column 0 also accumulate g against dden.
+// The phi(Q) tile and the per-token scalars are double-buffered: a wave
+// writes tile i + 1's only after the barrier of step 1 of tile i, which every
+// wave reaches after its step 3 of tile i - 1.
+template <int D, bool GO_BF16>
+__global__ __launch_bounds__(256) void bwd_query_bf16(const uint16_t* __restrict__ q,
+                                                      const void* __restrict__ dout,
+                                                      const float* __restrict__ states,
+                                                      void* __restrict__ dq, int N, int TB,
+                                                      int splits, int tps, float eps,
+                                                      float* __restrict__ dst) {
+  using Sh = BwdShape<D>;
+  constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, GRP = Sh::GRP, UPR = Sh::UPR;
+  constexpr int TT = Sh::TT, BR = Sh::BR, NR = Sh::NR;
+  constexpr int E = D * D + D;
+  constexpr int UNITS = TT * UPR;
+  __shared__ uint4 sfrag[Sh::NF][kWave];  // rows of S, hi/lo
+  __shared__ uint4 zfrag[KS * 2][kWave];  // z in every column, hi/lo
+  __shared__ uint4 qt[2][UNITS];          // phi(Q) tile, two buffers
+  __shared__ uint4 dnh[UNITS], dnl[UNITS];
+  __shared__ float srd[2][TT], sdd[2][TT];
+
+  const int nblk = gridDim.x / splits;
+  const int blk = blockIdx.x / splits;
+  const int split = blockIdx.x - blk * splits;
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const int c0 = blk * TB;
+  const int c1 = min(N, c0 + TB);
+  const int t0 = c0 + split * tps;
+  const int t1 = min(c1, t0 + tps);
+  const float* st = states + (bh * nblk + blk) * E;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  const int sig = 4 * (n & 3) + (n >> 2);
+  const int wi = wave >> 1, wj = wave & 1;
+
+  build_row_frags<D>(st, sfrag, wave, lane);
+  if (wave < KS) {
+    const float* zp = st + D * D + 32 * wave + 8 * g;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) split_bf16x2(zp[j], zp[j + 1], &h[j / 2], &l[j / 2]);
+    zfrag[2 * wave][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+    zfrag[2 * wave + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+  }
+  float zc[NBK];
+#pragma unroll
+  for (int nb = 0; nb < NBK; ++nb) zc[nb] = st[D * D + bwd_col<D>(nb, n)];
+
+  f32x4 accG[NR][NR], accg[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    accg[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NR; ++c) accG[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+
+  const uint4* qb = reinterpret_cast<const uint4*>(q + bh * static_cast<size_t>(N) * D);
+  const uint16_t* qrow = q + bh * static_cast<size_t>(N) * D;
+  const size_t row0 = bh * static_cast<size_t>(N);
+  uint4 qa[KS];
+  DoRow<GO_BF16> da[KS];
+  // Rows past the range load its last row; they are zeroed where used.
+  auto gload = [&](int it) {
+    const int tc = min(t0 + it * TT + 16 * wave + sig, t1 - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qa[s] = qb[static_cast<size_t>(tc) * UPR + 4 * s + g];
+      da[s].load(dout, (row0 + tc) * D + 32 * s + 8 * g);
+    }
+  };
+
+  const int ntiles = t1 > t0 ? (t1 - t0 + TT - 1) / TT : 0;
+  if (ntiles > 0) gload(0);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int ta = 16 * wave + sig;  // this lane's A row within the tile
+    const bool va = t0 + it * TT + ta < t1;
+    uint4 qp[KS];
+    float dv[KS][8];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qp[s] = va ? relu_bf16x8(qa[s]) : make_uint4(0, 0, 0, 0);
+      da[s].get(dv[s]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dv[s][j] = va ? dv[s][j] : 0.f;
+    }
+    if (it + 1 < ntiles) gload(it + 1);
+
+    // 1. phi(Q) rows to the tile; den and w on MFMA
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qt[buf][ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta))] = qp[s];
+    f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 accw[NBK];
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) accw[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      accz = mfma_16x16x32(qp[s], zfrag[2 * s][lane], accz);
+      accz = mfma_16x16x32(qp[s], zfrag[2 * s + 1][lane], accz);
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) split_bf16x2(dv[s][j], dv[s][j + 1], &h[j / 2], &l[j / 2]);
+      const uint4 ah = make_uint4(h[0], h[1], h[2], h[3]);
+      const uint4 al = make_uint4(l[0], l[1], l[2], l[3]);
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) {
+        const uint4 bh16 = sfrag[2 * (s * NBK + nb)][lane];
+        const uint4 bl16 = sfrag[2 * (s * NBK + nb) + 1][lane];
+        accw[nb] = mfma_16x16x32(ah, bh16, accw[nb]);
+        accw[nb] = mfma_16x16x32(ah, bl16, accw[nb]);
+        if constexpr (!GO_BF16) accw[nb] = mfma_16x16x32(al, bh16, accw[nb]);
+      }
+    }
+    // epilogue: rows 4 g + i hold tokens 4 i + g of the wave's sixteen
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = 16 * wave + 4 * i + g;
+      const int tok = t0 + it * TT + tt;
+      const int tc = min(tok, t1 - 1);
+      float qf[NBK];
+#pragma unroll
+      for (int gr = 0; gr < GRP; ++gr) {
+        float x[W];
+        load_row_w<W>(qrow + static_cast<size_t>(tc) * D + 16 * W * gr + W * n, x);
+#pragma unroll
+        for (int e = 0; e < W; ++e) qf[gr * W + e] = x[e];
+      }
+      float t = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) t = fmaf(fmaxf(qf[nb], 0.f), accw[nb][i], t);
+      t += __shfl_xor(t, 1, 16);
+      t += __shfl_xor(t, 2, 16);
+      t += __shfl_xor(t, 4, 16);
+      t += __shfl_xor(t, 8, 16);
+      // rows past the range have phi(q) = 0 and dO = 0; rd = 0 keeps them
+      // exactly zero even when eps = 0
+      const float rd = tok < t1 ? fast_rcp(accz[i] + eps) : 0.f;
+      const float c = t * rd;
+      if (tok < t1) {
+#pragma unroll
+        for (int gr = 0; gr < GRP; ++gr) {
+          float x[W];
+#pragma unroll
+          for (int e = 0; e < W; ++e) {
+            const int nb = gr * W + e;
+            const float gq = (accw[nb][i] - c * zc[nb]) * rd;
+            x[e] = qf[nb] > 0.f ? gq : 0.f;
+          }
+          store_row_w<W, GO_BF16>(dq, (row0 + tok) * D + 16 * W * gr + W * n, x);
+        }
+      }
+      if (n == 0) {
+        srd[buf][tt] = rd;
+        sdd[buf][tt] = -c * rd;
+      }
+    }
+    __syncthreads();
+
+    // 2. dnum = dO / den as a bf16 hi/lo pair, token-major
+    {
+      const float rd = srd[buf][ta];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2)
+          split_bf16x2(dv[s][j] * rd, dv[s][j + 1] * rd, &h[j / 2], &l[j / 2]);
+        const int u = ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta));
+        dnh[u] = make_uint4(h[0], h[1], h[2], h[3]);
+        dnl[u] = make_uint4(l[0], l[1], l[2], l[3]);
+      }
+    }
+    __syncthreads();
+
+    // 3. G += phi(Q)^T dnum, g += phi(Q)^T dden over the tile's tokens
+    const uint16_t* lq = reinterpret_cast<const uint16_t*>(qt[buf]);
+    const uint16_t* lh = reinterpret_cast<const uint16_t*>(dnh);
+    const uint16_t* ll = reinterpret_cast<const uint16_t*>(dnl);
+#pragma unroll
+    for (int ks = 0; ks < TT; ks += 32) {
+      uint4 a[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) a[r] = tile_column8<UPR>(lq, ks, wi * BR + 16 * r, lane);
+#pragma unroll
+      for (int c = 0; c < NR; ++c) {
+        const uint4 bh16 = tile_column8<UPR>(lh, ks, wj * BR + 16 * c, lane);
+        const uint4 bl16 = tile_column8<UPR>(ll, ks, wj * BR + 16 * c, lane);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          accG[r][c] = mfma_16x16x32(a[r], bh16, accG[r][c]);
+          accG[r][c] = mfma_16x16x32(a[r], bl16, accG[r][c]);
+        }
+      }
+      if (wj == 0) {
+        uint4 ddh = make_uint4(0, 0, 0, 0), ddl = make_uint4(0, 0, 0, 0);
+        if (n == 0) {
+          const float* p = &sdd[buf][ks + 8 * g];
+          uint32_t h[4], l[4];
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) split_bf16x2(p[j], p[j + 1], &h[j / 2], &l[j / 2]);
+          ddh = make_uint4(h[0], h[1], h[2], h[3]);
+          ddl = make_uint4(l[0], l[1], l[2], l[3]);
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          accg[r] = mfma_16x16x32(a[r], ddh, accg[r]);
+          accg[r] = mfma_16x16x32(a[r], ddl, accg[r]);
+        }
+      }
+    }
+  }
+
+  float* o = dst + ((bh * nblk + blk) * splits + split) * static_cast<size_t>(E);
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int c = 0; c < NR; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[(wi * BR + 16 * r + 4 * g + i) * D + wj * BR + 16 * c + n] = accG[r][c][i];
+  if (wj == 0 && n == 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[D * D + wi * BR + 16 * r + 4 * g + i] = accg[r][i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_key_bf16: dK and dV, bfloat16 keys and values.  Grid (blocks x splits,
+// H, B); workgroup (c, s) reads R_c ("rows of R" and "columns of R" operand
+// sets, built once into LDS) and covers a contiguous token range of block c.
+// Each wave takes 16 tokens per step as MFMA rows:
+//   dphi(k) = v R^T + r  (A = v, B = rows of R),
+//   dv      = phi(k) R   (A = phi(k), B = columns of R),
+// and stores both with the readout's 4-token-row store pattern.  No barrier
+// inside the loop.
+template <int D, bool GO_BF16>
+__global__ __launch_bounds__(256) void bwd_key_bf16(const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v,
+                                                    const float* __restrict__ R,
+                                                    void* __restrict__ dk, void* __restrict__ dv,
+                                                    int N, int TB, int splits, int tps) {
+  using Sh = BwdShape<D>;
+  constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, GRP = Sh::GRP, UPR = Sh::UPR;
+  constexpr int E = D * D + D;
+  __shared__ uint4 rrow[Sh::NF][kWave];
+  __shared__ uint4 rcol[Sh::NF][kWave];
+
+  const int nblk = gridDim.x / splits;
+  const int blk = blockIdx.x / splits;
+  const int split = blockIdx.x - blk * splits;
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const int c0 = blk * TB;
+  const int c1 = min(N, c0 + TB);
+  const int t0 = c0 + split * tps;
+  const int t1 = min(c1, t0 + tps);
+  if (t1 <= t0) return;
+  const float* rs = R + (bh * nblk + blk) * E;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  const int sig = 4 * (n & 3) + (n >> 2);
+
+  build_row_frags<D>(rs, rrow, wave, lane);
+  build_col_frags<D>(rs, rcol, wave, lane);
+  float rc[NBK];
+#pragma unroll
+  for (int nb = 0; nb < NBK; ++nb) rc[nb] = rs[D * D + bwd_col<D>(nb, n)];
+  __syncthreads();
+
+  const size_t row0 = bh * static_cast<size_t>(N);
+  const uint4* kb = reinterpret_cast<const uint4*>(k + row0 * D);
+  const uint4* vb = reinterpret_cast<const uint4*>(v + row0 * D);
+  const uint16_t* krow = k + row0 * D;
+  uint4 ka[KS], va[KS];
+  // this wave's 16-token steps: t0 + 16 (4 i + wave), i = 0, 1, ...
+  const int nsteps = (t1 - t0 + 15) / 16;
+  auto gload = [&](int step) {
+    const int tc = min(t0 + 16 * step + sig, t1 - 1);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      ka[s] = kb[static_cast<size_t>(tc) * UPR + 4 * s + g];
+      va[s] = vb[static_cast<size_t>(tc) * UPR + 4 * s + g];
+    }
+  };
+  if (wave < nsteps) gload(wave);
+  for (int step = wave; step < nsteps; step += 4) {
+    const bool valid = t0 + 16 * step + sig < t1;
+    uint4 kp[KS], vv[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kp[s] = valid ? relu_bf16x8(ka[s]) : make_uint4(0, 0, 0, 0);
+      vv[s] = valid ? va[s] : make_uint4(0, 0, 0, 0);
+    }
+    if (step + 4 < nsteps) gload(step + 4);
+    f32x4 acck[NBK], accv[NBK];
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) {
+      acck[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      accv[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) {
+        const int f = 2 * (s * NBK + nb);
+        acck[nb] = mfma_16x16x32(vv[s], rrow[f][lane], acck[nb]);
+        acck[nb] = mfma_16x16x32(vv[s], rrow[f + 1][lane], acck[nb]);
+        accv[nb] = mfma_16x16x32(kp[s], rcol[f][lane], accv[nb]);
+        accv[nb] = mfma_16x16x32(kp[s], rcol[f + 1][lane], accv[nb]);
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = t0 + 16 * step + 4 * i + g;
+      if (tok >= t1) continue;
+#pragma unroll
+      for (int gr = 0; gr < GRP; ++gr) {
+        float kf[W], xk[W], xv[W];
+        const int col = 16 * W * gr + W * n;
+        load_row_w<W>(krow + static_cast<size_t>(tok) * D + col, kf);
+#pragma unroll
+        for (int e = 0; e < W; ++e) {
+          const int nb = gr * W + e;
+          xk[e] = kf[e] > 0.f ? acck[nb][i] + rc[nb] : 0.f;
+          xv[e] = accv[nb][i];
+        }
+        store_row_w<W, GO_BF16>(dk, (row0 + tok) * D + col, xk);
+        store_row_w<W, GO_BF16>(dv, (row0 + tok) * D + col, xv);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 inputs: plain VALU versions of the two kernels above (the float32
+// path is for exactness checks and small problems).  Same grids and outputs.
+template <int D, bool GO_BF16>
+__global__ __launch_bounds__(kBlock) void bwd_query_f32(const float* __restrict__ q,
+                                                        const void* __restrict__ dout,
+                                                        const float* __restrict__ states,
+                                                        void* __restrict__ dq, int N, int TB,
+                                                        int splits, int tps, float eps,
+                                                        float* __restrict__ dst) {
+  constexpr int TT = 16;
+  constexpr int E = D * D + D;
+  constexpr int PER = D * D / kBlock;
+  static_assert(D * D % kBlock == 0 && D <= kBlock, "shape");
+  extern __shared__ float smem[];
+  float* sS = smem;              // E
+  float* sq = sS + E;            // TT x D: phi(q)
+  float* sd = sq + TT * D;       // TT x D: dO, then dnum
+  float* sw = sd + TT * D;       // TT x D: w
+  float* srd = sw + TT * D;      // TT: 1/den
+  float* sc = srd + TT;          // TT: t / den
+
+  const int nblk = gridDim.x / splits;
+  const int blk = blockIdx.x / splits;
+  const int split = blockIdx.x - blk * splits;
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const int c0 = blk * TB;
+  const int c1 = min(N, c0 + TB);
+  const int t0 = c0 + split * tps;
+  const int t1 = min(c1, t0 + tps);
+  const int tid = threadIdx.x;
+  const float* st = states + (bh * nblk + blk) * E;
+  for (int e = tid; e < E; e += kBlock) sS[e] = st[e];
+  const size_t row0 = bh * static_cast<size_t>(N);
+
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  float accz = 0.f;
+
+  for (int base = t0; base < t1; base += TT) {
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kBlock) {
+      const int t = e / D;
+      float x = 0.f, y = 0.f;
+      if (base + t < t1) {
+        const size_t idx = (row0 + base) * D + e;
+        x = q[idx];
+        y = GO_BF16 ? from_bf16(static_cast<const uint16_t*>(dout)[idx])
+                    : static_cast<const float*>(dout)[idx];
+      }
+      sq[e] = x > 0.f ? x : 0.f;
+      sd[e] = y;
+    }
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kBlock) {
+      const int t = e / D, a = e % D;
+      float w = 0.f;
+      for (int c = 0; c < D; ++c) w = fmaf(sS[a * D + c], sd[t * D + c], w);
+      sw[e] = w;
+    }
+    __syncthreads();
+    if (tid < TT) {
+      float den = 0.f, t = 0.f;
+      for (int a = 0; a < D; ++a) {
+        den = fmaf(sq[tid * D + a], sS[D * D + a], den);
+        t = fmaf(sq[tid * D + a], sw[tid * D + a], t);
+      }
+      const float rd = base + tid < t1 ? 1.f / (den + eps) : 0.f;
+      srd[tid] = rd;
+      sc[tid] = t * rd;
+    }
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kBlock) {
+      const int t = e / D, a = e % D;
+      const float rd = srd[t];
+      if (base + t < t1) {
+        const float gq = sq[e] > 0.f ? (sw[e] - sc[t] * sS[D * D + a]) * rd : 0.f;
+        const size_t idx = (row0 + base) * D + e;
+        if constexpr (GO_BF16)
+          static_cast<uint16_t*>(dq)[idx] = to_bf16(gq);
+        else
+          static_cast<float*>(dq)[idx] = gq;
+      }
+      sd[e] *= rd;  // dnum
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + kBlock * i;
+      const int a = e / D, c = e % D;
+      float x = acc[i];
+      for (int t = 0; t < TT; ++t) x = fmaf(sq[t * D + a], sd[t * D + c], x);
+      acc[i] = x;
+    }
+    if (tid < D)
+      for (int t = 0; t < TT; ++t) accz = fmaf(-sc[t] * srd[t], sq[t * D + tid], accz);
+  }
+
+  float* o = dst + ((bh * nblk + blk) * splits + split) * static_cast<size_t>(E);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[tid + kBlock * i] = acc[i];
+  if (tid < D) o[D * D + tid] = accz;
+}
+
+template <int D>
+constexpr size_t bwd_query_f32_smem() {
+  return sizeof(float) * (D * D + D + 3 * 16 * D + 2 * 16);
+}
+
+template <int D, bool GO_BF16>
+__global__ __launch_bounds__(kBlock) void bwd_key_f32(const float* __restrict__ k,
+                                                      const float* __restrict__ v,
+                                                      const float* __restrict__ R,
+                                                      void* __restrict__ dk, void* __restrict__ dv,
+                                                      int N, int TB, int splits, int tps) {
+  constexpr int TT = 16;
+  constexpr int E = D * D + D;
+  extern __shared__ float smem[];
+  float* sR = smem;            // E
+  float* sk = sR + E;          // TT x D: k (raw)
+  float* sv = sk + TT * D;     // TT x D: v
+
+  const int nblk = gridDim.x / splits;
+  const int blk = blockIdx.x / splits;
+  const int split = blockIdx.x - blk * splits;
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  const int c0 = blk * TB;
+  const int c1 = min(N, c0 + TB);
+  const int t0 = c0 + split * tps;
+  const int t1 = min(c1, t0 + tps);
+  const int tid = threadIdx.x;
+  const float* rs = R + (bh * nblk + blk) * E;
+  for (int e = tid; e < E; e += kBlock) sR[e] = rs[e];
+  const size_t row0 = bh * static_cast<size_t>(N);
+
+  for (int base = t0; base < t1; base += TT) {
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kBlock) {
+      const int t = e / D;
+      float x = 0.f, y = 0.f;
+      if (base + t < t1) {
+        x = k[(row0 + base) * D + e];
+        y = v[(row0 + base) * D + e];
+      }
+      sk[e] = x;
+      sv[e] = y;
+    }
+    __syncthreads();
+    for (int e = tid; e < TT * D; e += kBlock) {
+      const int t = e / D, a = e % D;
+      if (base + t >= t1) continue;
+      float gk = sR[D * D + a], gv = 0.f;
+      for (int c = 0; c < D; ++c) gk = fmaf(sR[a * D + c], sv[t * D + c], gk);
+      for (int b = 0; b < D; ++b) gv = fmaf(fmaxf(sk[t * D + b], 0.f), sR[b * D + a], gv);
+      gk = sk[e] > 0.f ? gk : 0.f;
+      const size_t idx = (row0 + base) * D + e;
+      if constexpr (GO_BF16) {
+        static_cast<uint16_t*>(dk)[idx] = to_bf16(gk);
+        static_cast<uint16_t*>(dv)[idx] = to_bf16(gv);
+      } else {
+        static_cast<float*>(dk)[idx] = gk;
+        static_cast<float*>(dv)[idx] = gv;
+      }
+    }
+  }
+}
+
+template <int D>
+constexpr size_t bwd_key_f32_smem() {
+  return sizeof(float) * (D * D + D + 2 * 16 * D);
+}
+
+}  // namespace la

@@ -1,7 +1,9 @@
 // Host side of the C ABI declared in include/linattn.h: argument checks,
 // launch planning, and the three launches of a forward call (KV reduction ->
-// split reduce + state add, or the prefix over blocks -> readout) on the
-// caller's stream.  Nothing here allocates device memory or synchronises.
+// split reduce + state add, or the prefix over blocks -> readout) or of a
+// backward call (query gradients + partial state gradients -> suffix over
+// blocks -> key and value gradients) on the caller's stream.  Nothing here
+// allocates device memory or synchronises.
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -11,10 +13,11 @@
 #include "kv_reduce.h"
 #include "readout.h"
 #include "state_update.h"
+#include "backward.h"
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -33,6 +36,12 @@ constexpr int kSweepWorkgroups = 768;
 // (256 measured best at the long-horizon shape among 128..1024).
 constexpr int kSweepWorkgroups128 = 256;
 constexpr int kReadoutTargetWorkgroups = 1024;
+// Backward workgroups the planner aims for: the query-gradient kernel (four
+// waves, 53 KB of LDS at d = 64: three per CU) and the key-gradient kernel
+// (four waves, 32 KB).  At d = 128 both hold 128-137 KB of LDS: one per CU.
+constexpr int kBwdQueryTargetWorkgroups = 768;
+constexpr int kBwdKeyTargetWorkgroups = 1024;
+constexpr int kBwdTargetWorkgroups128 = 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -229,6 +238,225 @@ int run(const Plan& p, const void* q, const void* k, const void* v, const float*
   return record(opts, 3, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Backward.  Workspace layout: R [B][H][blocks][d*d + d] float32 (the suffix
+// sums), then, when the query kernel uses more than one split per block,
+// its partials [B][H][blocks][splits][d*d + d].
+struct BwdPlan {
+  int nblk;        // blocks (0 when N == 0)
+  int T;           // tokens per block
+  int qsplits;     // query-gradient workgroups per block
+  int qtps;        // tokens per query-gradient workgroup
+  int ksplits;     // key-gradient workgroups per block
+  int ktps;        // tokens per key-gradient workgroup
+  size_t ws_bytes; // workspace the plan needs
+};
+
+// ws_avail: the caller's workspace size (SIZE_MAX when planning the size).
+BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest, int krequest,
+                      size_t ws_avail) {
+  BwdPlan p{};
+  p.T = T < N ? T : N;
+  p.nblk = N == 0 ? 0 : (N + p.T - 1) / p.T;
+  if (N == 0) return p;
+  const int tile = in_dt == LA_BF16 ? 64 : 16;
+  const long long pairs = static_cast<long long>(B) * H * p.nblk;
+  const size_t st = static_cast<size_t>(d) * d + d;
+  const size_t r_bytes = static_cast<size_t>(pairs) * st * sizeof(float);
+  const int Tb = p.T;
+  const int ntiles = (Tb + tile - 1) / tile;
+
+  long long s;
+  if (qrequest > 0) {
+    s = qrequest;
+  } else {
+    const long long target = d == 128 ? kBwdTargetWorkgroups128 : kBwdQueryTargetWorkgroups;
+    s = (target + pairs - 1) / pairs;
+    const long long by_size = Tb / (kKvMinTokensPerFeature * (d + 1));
+    s = s < by_size ? s : by_size;
+  }
+  if (s > ntiles) s = ntiles;
+  if (s > 1 && ws_avail != SIZE_MAX) {
+    // splits + 1 state-sized slots per (b, h, block)
+    const size_t slots = ws_avail / r_bytes;
+    const long long most = slots > 1 ? static_cast<long long>(slots - 1) : 1;
+    if (s > most) s = most;
+  }
+  if (s < 1) s = 1;
+  int per = static_cast<int>((Tb + s - 1) / s);
+  p.qtps = (per + tile - 1) / tile * tile;
+  p.qsplits = (Tb + p.qtps - 1) / p.qtps;
+  p.ws_bytes = p.qsplits > 1 ? r_bytes * (p.qsplits + 1) : r_bytes;
+
+  long long kw;
+  if (krequest > 0) {
+    kw = (krequest + pairs - 1) / pairs;
+  } else {
+    const long long target = d == 128 ? kBwdTargetWorkgroups128 : kBwdKeyTargetWorkgroups;
+    kw = (target + pairs - 1) / pairs;
+  }
+  if (kw > ntiles) kw = ntiles;
+  if (kw < 1) kw = 1;
+  per = static_cast<int>((Tb + kw - 1) / kw);
+  p.ktps = (per + tile - 1) / tile * tile;
+  p.ksplits = (Tb + p.ktps - 1) / p.ktps;
+  return p;
+}
+
+template <typename Kern>
+int allow_smem(Kern* kern, size_t smem) {
+  if (smem <= 65536) return LA_OK;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(smem)) == hipSuccess
+             ? LA_OK
+             : LA_E_HIP;
+}
+
+template <int D, bool GO_BF16>
+int launch_bwd_query(const BwdPlan& p, const void* q, const void* dout, const float* states,
+                     void* dq, int in_dt, int B, int H, int N, float eps, float* dst,
+                     hipStream_t stream) {
+  const dim3 grid(p.nblk * p.qsplits, H, B);
+  if (in_dt == LA_BF16) {
+    la::bwd_query_bf16<D, GO_BF16><<<grid, la::BwdShape<D>::NT, 0, stream>>>(
+        static_cast<const uint16_t*>(q), dout, states, dq, N, p.T, p.qsplits, p.qtps, eps, dst);
+  } else {
+    constexpr size_t smem = la::bwd_query_f32_smem<D>();
+    const int rc = allow_smem(&la::bwd_query_f32<D, GO_BF16>, smem);
+    if (rc != LA_OK) return rc;
+    la::bwd_query_f32<D, GO_BF16><<<grid, la::kBlock, smem, stream>>>(
+        static_cast<const float*>(q), dout, states, dq, N, p.T, p.qsplits, p.qtps, eps, dst);
+  }
+  return launched();
+}
+
+template <int D, bool GO_BF16>
+int launch_bwd_key(const BwdPlan& p, const void* k, const void* v, const float* R, void* dk,
+                   void* dv, int in_dt, int B, int H, int N, hipStream_t stream) {
+  const dim3 grid(p.nblk * p.ksplits, H, B);
+  if (in_dt == LA_BF16) {
+    la::bwd_key_bf16<D, GO_BF16><<<grid, la::BwdShape<D>::NT, 0, stream>>>(
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), R, dk, dv, N, p.T,
+        p.ksplits, p.ktps);
+  } else {
+    constexpr size_t smem = la::bwd_key_f32_smem<D>();
+    const int rc = allow_smem(&la::bwd_key_f32<D, GO_BF16>, smem);
+    if (rc != LA_OK) return rc;
+    la::bwd_key_f32<D, GO_BF16><<<grid, la::kBlock, smem, stream>>>(
+        static_cast<const float*>(k), static_cast<const float*>(v), R, dk, dv, N, p.T, p.ksplits,
+        p.ktps);
+  }
+  return launched();
+}
+
+template <int D, bool GO_BF16>
+int run_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const float* states,
+            const void* dout, const float* dstates, void* dq, void* dk, void* dv,
+            float* dstate_in, int B, int H, int N, int in_dt, float eps, void* workspace,
+            const la_launch_opts* opts, hipStream_t stream) {
+  constexpr int E = D * D + D;
+  const int n4 = E / 4;
+  float* R = static_cast<float*>(workspace);
+  float* partials = p.qsplits > 1 ? R + static_cast<size_t>(B) * H * p.nblk * E : R;
+  int rc;
+  if ((rc = record(opts, 0, stream)) != LA_OK) return rc;
+  if ((rc = launch_bwd_query<D, GO_BF16>(p, q, dout, states, dq, in_dt, B, H, N, eps, partials,
+                                         stream)) != LA_OK)
+    return rc;
+  if ((rc = record(opts, 1, stream)) != LA_OK) return rc;
+  const dim3 grid((n4 + la::kBlock - 1) / la::kBlock, H, B);
+  la::state_suffix_scan<<<grid, la::kBlock, 0, stream>>>(
+      reinterpret_cast<const float4*>(partials), p.nblk, p.qsplits, n4,
+      reinterpret_cast<const float4*>(dstates), reinterpret_cast<float4*>(R),
+      reinterpret_cast<float4*>(dstate_in));
+  if ((rc = launched()) != LA_OK) return rc;
+  if ((rc = record(opts, 2, stream)) != LA_OK) return rc;
+  if ((rc = launch_bwd_key<D, GO_BF16>(p, k, v, R, dk, dv, in_dt, B, H, N, stream)) != LA_OK)
+    return rc;
+  return record(opts, 3, stream);
+}
+
+// Checks shared by every backward call, then the launches.  The sequence of
+// N tokens per (b, h) is cut into blocks of T (one block: T >= N); `states`
+// holds the forward's state after every block.  `empty_block`: the chunk
+// call with L = 0 (one block of no tokens, so dstate_in = dstates).
+int backward(const void* q, const void* k, const void* v, const float* states, const void* dout,
+             const float* dstates, void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
+             int N, int T, int d, int in_dt, int grad_dt, float eps, void* workspace,
+             size_t workspace_bytes, bool empty_block, const la_launch_opts* opts,
+             hipStream_t stream) {
+  int rc = check_shape(B, H, N, d, in_dt, grad_dt);
+  if (rc != LA_OK) return rc;
+  if (T <= 0) return LA_E_INVAL;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
+  if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || states == nullptr ||
+                dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr))
+    return LA_E_INVAL;
+  if (empty_block && states == nullptr) return LA_E_INVAL;
+  const void* ptrs[] = {q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, workspace};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return LA_E_ALIGN;
+
+  const int nblk = N == 0 ? (empty_block ? 1 : 0) : (N + (T < N ? T : N) - 1) / (T < N ? T : N);
+  const size_t bh = static_cast<size_t>(B) * H;
+  const size_t st = (static_cast<size_t>(d) * d + d) * sizeof(float);
+  const size_t in_bytes = bh * N * d * elem_size(in_dt);
+  const size_t g_bytes = bh * N * d * elem_size(grad_dt);
+  BwdPlan p = empty_block
+                  ? make_bwd_plan(B, H, 1, 1, d, in_dt, 1, 1, SIZE_MAX)
+                  : make_bwd_plan(B, H, N, T, d, in_dt, opts ? opts->kv_splits : 0,
+                                  opts ? opts->readout_workgroups : 0, workspace_bytes);
+  if (empty_block) {
+    p.T = 1;  // one block of no tokens: every workgroup's range is empty
+  }
+  const size_t need = nblk == 0 ? 0 : p.ws_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LA_E_INVAL;
+
+  // outputs against inputs and against each other
+  struct Buf {
+    const void* p;
+    size_t n;
+  };
+  const Buf ins[] = {{q, in_bytes}, {k, in_bytes}, {v, in_bytes}, {states, st * bh * nblk},
+                     {dout, g_bytes}, {dstates, st * bh * nblk}};
+  const Buf outs[] = {{dq, g_bytes}, {dk, g_bytes}, {dv, g_bytes}, {dstate_in, st * bh},
+                      {workspace, need}};
+  for (const Buf& o : outs) {
+    for (const Buf& i : ins)
+      if (overlaps(o.p, o.n, i.p, i.n)) return LA_E_ALIAS;
+    for (const Buf& o2 : outs)
+      if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return LA_E_ALIAS;
+  }
+
+  if (nblk == 0) {
+    if (dstate_in != nullptr) {
+      const size_t n4 = bh * (static_cast<size_t>(d) * d + d) / 4;
+      size_t blocks = (n4 + la::kBlock - 1) / la::kBlock;
+      if (blocks > 4096) blocks = 4096;
+      la::fill_zero<<<static_cast<unsigned>(blocks), la::kBlock, 0, stream>>>(
+          reinterpret_cast<float4*>(dstate_in), n4);
+      return launched();
+    }
+    return LA_OK;
+  }
+  const bool gb = grad_dt == LA_BF16;
+#define LA_RUN_BWD(DD)                                                                          \
+  return gb ? run_bwd<DD, true>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, \
+                                N, in_dt, eps, workspace, opts, stream)                         \
+            : run_bwd<DD, false>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H,\
+                                 N, in_dt, eps, workspace, opts, stream)
+  switch (d) {
+    case 32:
+      LA_RUN_BWD(32);
+    case 64:
+      LA_RUN_BWD(64);
+    default:
+      LA_RUN_BWD(128);
+  }
+#undef LA_RUN_BWD
+}
+
 // Checks shared by every forward call, then the launches.  `need_state_in`:
 // the chunk call requires it; the global and block-causal calls take NULL as
 // zero.  `states_blocks`: number of states `states` holds per (b, h).
@@ -350,6 +578,53 @@ int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_req
   *kv_splits = p.nblk == 0 ? 0 : p.splits;
   *readout_workgroups = p.readout_wgs;
   return LA_OK;
+}
+
+int la_backward_workspace_size(int B, int H, int N, int T, int d, int in_dt, size_t* bytes) {
+  const int rc = check_shape(B, H, N, d, in_dt, LA_F32);
+  if (rc != LA_OK) return rc;
+  if (T <= 0 || bytes == nullptr) return LA_E_INVAL;
+  const BwdPlan p = N == 0 ? make_bwd_plan(B, H, 1, 1, d, in_dt, 1, 1, SIZE_MAX)
+                           : make_bwd_plan(B, H, N, T, d, in_dt, 0, 0, SIZE_MAX);
+  *bytes = p.ws_bytes;
+  return LA_OK;
+}
+
+int la_blockcausal_backward(const void* q, const void* k, const void* v, const float* states,
+                            const void* dout, const float* dstates, void* dq, void* dk, void* dv,
+                            float* dstate_in, int B, int H, int N, int T, int d, int in_dt,
+                            int grad_dt, float eps, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return backward(q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, N, T, d, in_dt,
+                  grad_dt, eps, workspace, workspace_bytes, false, nullptr, stream);
+}
+
+int la_blockcausal_backward_ex(const void* q, const void* k, const void* v, const float* states,
+                               const void* dout, const float* dstates, void* dq, void* dk,
+                               void* dv, float* dstate_in, int B, int H, int N, int T, int d,
+                               int in_dt, int grad_dt, float eps, void* workspace,
+                               size_t workspace_bytes, const la_launch_opts* opts,
+                               hipStream_t stream) {
+  return backward(q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, N, T, d, in_dt,
+                  grad_dt, eps, workspace, workspace_bytes, false, opts, stream);
+}
+
+int la_chunk_backward(const void* q, const void* k, const void* v, const float* state_out,
+                      const void* dout, const float* dstate_out, void* dq, void* dk, void* dv,
+                      float* dstate_in, int B, int H, int L, int d, int in_dt, int grad_dt,
+                      float eps, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (state_out == nullptr) return LA_E_INVAL;
+  return backward(q, k, v, state_out, dout, dstate_out, dq, dk, dv, dstate_in, B, H, L,
+                  L > 0 ? L : 1, d, in_dt, grad_dt, eps, workspace, workspace_bytes, L == 0,
+                  nullptr, stream);
+}
+
+int la_global_backward(const void* q, const void* k, const void* v, const float* state,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                       int in_dt, int grad_dt, float eps, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  return backward(q, k, v, state, dout, nullptr, dq, dk, dv, nullptr, B, H, N, N > 0 ? N : 1, d,
+                  in_dt, grad_dt, eps, workspace, workspace_bytes, false, nullptr, stream);
 }
 
 const char* la_status_string(int status) {

@@ -116,6 +116,42 @@ __global__ __launch_bounds__(kBlock) void state_scan(const float4* partials,
   }
 }
 
+// Suffix over the blocks of a sequence, for the gradients:
+//   R_c = R_{c+1} + sum_s P_{c,s} + dS_c,  c = C-1 .. 0,  R_C = 0,
+// written to R[B][H][blocks][d*d + d]; dS (the gradients of the states
+// after every block) may be null; d_in, if not null, receives R_0 (the
+// gradient of the state before the first block).  One thread per float4 of
+// one (b, h) walks the blocks backwards; splits are summed in order, so
+// repeated runs are bitwise identical.  partials may be R itself (one split
+// per block): each element is read before the same thread writes it.
+__global__ __launch_bounds__(kBlock) void state_suffix_scan(const float4* partials, int nblk,
+                                                            int splits, int n4,
+                                                            const float4* __restrict__ dS,
+                                                            float4* R,
+                                                            float4* __restrict__ d_in) {
+  const int e = blockIdx.x * kBlock + threadIdx.x;
+  if (e >= n4) return;
+  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
+  auto add = [](float4& a, const float4& x) {
+    a.x += x.x;
+    a.y += x.y;
+    a.z += x.z;
+    a.w += x.w;
+  };
+  const float4* p = partials + bh * static_cast<size_t>(nblk) * splits * n4 + e;
+  const float4* ds = dS != nullptr ? dS + bh * static_cast<size_t>(nblk) * n4 + e : nullptr;
+  float4* out = R + bh * static_cast<size_t>(nblk) * n4 + e;
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c = nblk - 1; c >= 0; --c) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < splits; ++s) add(x, p[(static_cast<size_t>(c) * splits + s) * n4]);
+    if (ds != nullptr) add(x, ds[static_cast<size_t>(c) * n4]);
+    add(run, x);
+    out[static_cast<size_t>(c) * n4] = run;
+  }
+  if (d_in != nullptr) d_in[bh * n4 + e] = run;
+}
+
 // Zero fill (used instead of a memset so that callers may graph-capture it).
 __global__ __launch_bounds__(kBlock) void fill_zero(float4* __restrict__ p, size_t n4) {
   const size_t stride = static_cast<size_t>(gridDim.x) * kBlock;

@@ -58,6 +58,7 @@
 #define LINATTN_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -175,6 +176,85 @@ int la_blockcausal_forward_ex(const void* q, const void* k, const void* v,
                               const float* state_in, void* out, float* states,
                               int B, int H, int N, int T, int d, int in_dt, int out_dt,
                               float eps, const la_launch_opts* opts, hipStream_t stream);
+
+/*
+ * Gradients (training uses the same attention: [EN] abstract; [TR] trains
+ * with block-causal attention over the blocks of a video).  For a loss L,
+ * given dO = dL/dO and optionally dL/dS_n, dL/dz_n for the state after every
+ * block, the backward calls return dL/dQ, dL/dK, dL/dV and optionally the
+ * gradient of the state before the first block.  They are the chain rule of
+ * the forward above (den_i = phi(q_i) . z_n + eps, S_n the state block n's
+ * queries read):
+ *   dq_i = (S_n do_i - (t_i / den_i) z_n) / den_i * [q_i > 0],
+ *          t_i = phi(q_i) . (S_n do_i)
+ *   R_m  = sum over blocks n >= m of ( sum_{i in n} phi(q_i) do_i^T / den_i + dL/dS_n )
+ *   r_m  = sum over blocks n >= m of ( -sum_{i in n} t_i / den_i^2 phi(q_i) + dL/dz_n )
+ *   dk_j = (R_m v_j + r_m) * [k_j > 0],   dv_j = R_m^T phi(k_j)   (j in block m)
+ *   dS_in = R_1, dz_in = r_1
+ * with [x > 0] the derivative of max(x, 0), taken as 0 at 0.
+ *
+ * Common arguments:
+ *   q, k, v    : the forward's inputs, [B][H][N][d] in_dt, read.
+ *   dout       : dL/dO, [B][H][N][d] grad_dt, read.
+ *   dq, dk, dv : [B][H][N][d] grad_dt, written.
+ *   grad_dt    : LA_F32 or LA_BF16, the type of dout and of dq, dk, dv.
+ *   workspace  : device memory of at least la_backward_workspace_size() bytes
+ *                (caller-owned, contents need not be initialised, clobbered).
+ * Outputs (dq, dk, dv, dstate_in, workspace) must not overlap each other or
+ * any input (LA_E_ALIAS); inputs may overlap each other.  A workspace that is
+ * NULL or too small gives LA_E_INVAL.  Other errors as for the forward calls.
+ * Results are bitwise reproducible run to run.
+ */
+
+/* Bytes of workspace a backward call with these arguments needs (T as for
+ * la_blockcausal_backward; L or N for the chunk and global calls). */
+int la_backward_workspace_size(int B, int H, int N, int T, int d, int in_dt, size_t* bytes);
+
+/*
+ * la_blockcausal_backward - gradients of la_blockcausal_forward.
+ *   states    : [B][H][C][d*d+d] float32, read: the forward's `states`.
+ *   dstates   : [B][H][C][d*d+d] float32, read, or NULL (zero): dL/dS_n, dL/dz_n.
+ *   dstate_in : [B][H][d*d+d] float32, written (NULL: not wanted): the gradient
+ *               of the forward's state_in (R_1, r_1).
+ * N = 0 writes zeros to dstate_in (if given) and nothing else.
+ */
+int la_blockcausal_backward(const void* q, const void* k, const void* v, const float* states,
+                            const void* dout, const float* dstates, void* dq, void* dk, void* dv,
+                            float* dstate_in, int B, int H, int N, int T, int d, int in_dt,
+                            int grad_dt, float eps, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* As above, with launch options: kv_splits = workgroups per block of the
+ * query-gradient kernel (clamped as the forward's, and to the workspace),
+ * readout_workgroups = workgroups of the key-gradient kernel, stage_events =
+ * 4 events around its three kernels. */
+int la_blockcausal_backward_ex(const void* q, const void* k, const void* v, const float* states,
+                               const void* dout, const float* dstates, void* dq, void* dk,
+                               void* dv, float* dstate_in, int B, int H, int N, int T, int d,
+                               int in_dt, int grad_dt, float eps, void* workspace,
+                               size_t workspace_bytes, const la_launch_opts* opts,
+                               hipStream_t stream);
+
+/*
+ * la_chunk_backward - gradients of one la_chunk_forward call.
+ *   state_out  : the forward's state_out (the state the queries read), read.
+ *   dstate_out : dL/d state_out, [B][H][d*d+d] float32, read, or NULL (zero).
+ *   dstate_in  : dL/d state_in, written, or NULL.
+ * L = 0: dstate_in = dstate_out (or zeros); q, k, v, dout, dq, dk, dv may be NULL.
+ */
+int la_chunk_backward(const void* q, const void* k, const void* v, const float* state_out,
+                      const void* dout, const float* dstate_out, void* dq, void* dk, void* dv,
+                      float* dstate_in, int B, int H, int L, int d, int in_dt, int grad_dt,
+                      float eps, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * la_global_backward - gradients of la_global_forward (no state gradient).
+ *   state : the forward's state_out (the global S, z), read.
+ */
+int la_global_backward(const void* q, const void* k, const void* v, const float* state,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                       int in_dt, int grad_dt, float eps, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * la_plan - the launch shape a forward call with these arguments (and the

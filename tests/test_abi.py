@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 2
+    assert la.abi_version() == 3
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -154,3 +154,59 @@ def test_plan_shapes():
     assert la.plan(4, 16, 4096, 128, in_dtype=la.torch.float32)[1] == 4 * 16 * 8
     with pytest.raises(la.LinAttnError):
         la.plan(1, 1, 10, 48)
+
+
+def bwd(q=A, k=2 * A, v=3 * A, sts=4 * A, do=5 * A, dsts=None, dq=6 * A, dk=7 * A, dv=8 * A,
+        dsi=None, B=1, H=2, N=640, T=64, d=64, idt=BF16, gdt=F32, eps=1e-6, ws=9 * A,
+        wsb=1 << 20):
+    return la.lib().la_blockcausal_backward(q, k, v, sts, do, dsts, dq, dk, dv, dsi, B, H, N, T,
+                                            d, idt, gdt, eps, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), la.LA_E_INVAL),
+    (dict(N=-2), la.LA_E_INVAL),
+    (dict(eps=-1e-3), la.LA_E_INVAL),
+    (dict(d=48), la.LA_E_UNSUPPORTED),
+    (dict(gdt=5), la.LA_E_UNSUPPORTED),
+    (dict(idt=2), la.LA_E_UNSUPPORTED),
+    (dict(q=None), la.LA_E_INVAL),
+    (dict(do=None), la.LA_E_INVAL),
+    (dict(sts=None), la.LA_E_INVAL),
+    (dict(dv=None), la.LA_E_INVAL),
+    (dict(ws=None), la.LA_E_INVAL),                # workspace needed
+    (dict(wsb=1024), la.LA_E_INVAL),               # workspace too small
+    (dict(dq=6 * A + 8), la.LA_E_ALIGN),
+    (dict(ws=9 * A + 4), la.LA_E_ALIGN),
+    (dict(dq=A), la.LA_E_ALIAS),                   # dq == q
+    (dict(dk=5 * A + 512), la.LA_E_ALIAS),         # dk inside dout
+    (dict(dv=7 * A + 64), la.LA_E_ALIAS),          # dv overlaps dk
+    (dict(ws=8 * A + 4096), la.LA_E_ALIAS),        # workspace overlaps dv
+    (dict(dsi=4 * A + 16640), la.LA_E_ALIAS),      # dstate_in inside states
+    (dict(dsi=9 * A), la.LA_E_ALIAS),              # dstate_in inside the workspace
+])
+def test_backward_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_backward_entry_points_reject():
+    L_ = la.lib()
+    # the chunk call needs state_out; the global call rejects a bad d
+    assert L_.la_chunk_backward(A, 2 * A, 3 * A, None, 5 * A, None, 6 * A, 7 * A, 8 * A, None,
+                                1, 2, 64, 64, BF16, F32, 1e-6, 9 * A, 1 << 20, None) == la.LA_E_INVAL
+    assert L_.la_global_backward(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 1, 2, 64,
+                                 40, BF16, F32, 1e-6, 9 * A, 1 << 20, None) == la.LA_E_UNSUPPORTED
+    # no tokens and no state gradient wanted: nothing to do, nothing launched
+    assert bwd(N=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None, ws=None,
+               wsb=0) == la.LA_OK
+
+
+def test_backward_workspace_size():
+    E = 64 * 64 + 64
+    # one short block: one query split, the workspace holds R only
+    assert la.backward_workspace_size(1, 1, 100, 100, 64) == E * 4
+    # the 720p chunk: 24 query splits per head -> R plus 24 partials per head
+    assert la.backward_workspace_size(1, 32, 75600, 75600, 64) == 32 * E * 4 * 25
+    # config-5 shape in one call: 40 blocks x 64 heads, one split each
+    E2 = 128 * 128 + 128
+    assert la.backward_workspace_size(4, 16, 40 * 4096, 4096, 128) == 4 * 16 * 40 * E2 * 4

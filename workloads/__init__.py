@@ -27,6 +27,8 @@ import numpy as np
 EPS = float(np.float32(1e-6))
 
 Q_ID, K_ID, V_ID, MASK_ID = 0, 1, 2, 3
+# upstream gradients for the backward tests: dL/dO, dL/d(block states)
+DO_ID, DSTATE_ID = 4, 5
 
 
 @dataclass(frozen=True)
@@ -123,3 +125,18 @@ def random_state(seed, B, H, d, tokens=1000):
     S = (g.standard_normal((B, H, d, d)) * np.sqrt(tokens / 2.0)).astype(np.float32)
     z = (np.abs(g.standard_normal((B, H, d))) * 0.1 + 0.4) * tokens
     return S, z.astype(np.float32)
+
+
+def random_grads(seed, B, H, N, d, dtype="f32", chunk=0, scale=1.0):
+    """An upstream gradient dL/dO [B, H, N, d] ~ N(0, 1) * scale, rounded to
+    the gradient's storage precision (tensor id 4 of the seed's streams)."""
+    return draw(seed, DO_ID, chunk, (B, H, N, d), dtype=dtype, scale=scale)
+
+
+def random_state_grads(seed, B, H, C, d, scale=1e-4):
+    """Gradients of C block states: (dS [C, B, H, d, d], dz [C, B, H, d]),
+    N(0, 1) * scale in float32 (tensor id 5)."""
+    g = _rng(seed, DSTATE_ID, 0)
+    dS = (g.standard_normal((C, B, H, d, d)) * scale).astype(np.float32)
+    dz = (g.standard_normal((C, B, H, d)) * scale).astype(np.float32)
+    return dS, dz
