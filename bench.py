@@ -213,7 +213,7 @@ def bench_other(args):
     if onecall:  # stage times cover all C blocks
         kv_b, ro_b = kv_b * C, ro_b * C
     tokens = B * L * C
-    ro_kernel = f"readout_sweep_bf16<{d}>" if d <= 64 else f"readout_bf16<{d}>"
+    ro_kernel = f"readout_sweep_bf16<{d}>"
     result = {
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -236,6 +236,111 @@ def bench_other(args):
     print(json.dumps(result), flush=True)
 
 
+BACKWARD = {
+    "bwd_chunk720p": 3,
+    "bwd_stream480p_onecall": 4,
+    "bwd_longhorizon_onecall": 5,
+}
+
+
+def bwd_bytes(B, H, N, d, C, s_in=2, s_g=4):
+    """Algorithmic bytes of one backward call (float32 gradients):
+    query kernel: read Q, dO and the C block states, write dQ;
+    key kernel: read K, V and the C suffix states, write dK, dV;
+    the whole call: Q, K, V, dO, states (+ one state gradient) in, dQ, dK,
+    dV (+ one state gradient) out."""
+    th = B * H * N * d
+    st = B * H * C * (d * d + d) * 4
+    query = th * (s_in + 2 * s_g) + st
+    key = th * (2 * s_in + 2 * s_g) + st
+    call = th * (3 * s_in + 4 * s_g) + st + 2 * B * H * (d * d + d) * 4
+    return call, query, key
+
+
+def bench_backward(args):
+    """One step = one backward call over resident inputs and forward states
+    (the 720p chunk with gradients on its state, or a whole stream in one
+    la_blockcausal_backward)."""
+    import torch
+
+    import block_causal_linear_amd as la
+    import workloads
+
+    w = workloads.CHUNK_720P if args.workload == "bwd_chunk720p" else \
+        workloads.WORKLOADS[BACKWARD[args.workload]]
+    chunked = args.workload == "bwd_chunk720p"
+    B, H, d = w.B, w.H, w.d
+    C = 1 if chunked else w.chunks
+    T = w.L
+    N = T * C
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(2000 + w.cid)
+    log(f"drawing inputs on the GPU for the backward of {w.name} (B={B} H={H} N={N} T={T} d={d})")
+
+    def draw(dtype=torch.bfloat16, scale=w.scale):
+        x = torch.randn((B, H, N, d), generator=gen, device=dev)
+        if scale != 1.0:
+            x.mul_(scale)
+        return x.to(dtype)
+
+    q, k, v = draw(), draw(), draw()
+    dout = draw(torch.float32, 1.0)
+    state_in = None
+    if chunked:
+        _, state_in = la.global_forward(draw(), draw(), draw(), eps=workloads.EPS)
+    _, states = la.blockcausal_forward(q, k, v, T, state_in=state_in, eps=workloads.EPS)
+    dstates = torch.randn(states.shape, generator=gen, device=dev).mul_(1e-5) if chunked else None
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
+    dsi = torch.empty((B, H, d * d + d), dtype=torch.float32, device=dev) if chunked else None
+    ws = torch.empty(la.backward_workspace_size(B, H, N, T, d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        la.blockcausal_backward(q, k, v, states, dout, T, dstates=dstates, eps=workloads.EPS,
+                                dq=dq, dk=dk, dv=dv, dstate_in=dsi, workspace=ws,
+                                kv_splits=args.kv_splits, stage_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    every = max(1, args.event_every)
+    evs = {i: la.StageEvents() for i in range(0, args.steps, every)}
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs.get(i))
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stages = np.array([e.elapsed_ms() for e in evs.values()])
+    for e in evs.values():
+        e.close()
+    q_ms, scan_ms, k_ms = (float(x) for x in stages.mean(axis=0))
+    call_b, q_b, k_b = bwd_bytes(B, H, N, d, C)
+    result = {
+        "metric": "latent tokens/sec + % peak HBM BW, block-causal linear attn backward",
+        "value": B * N / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + (" backward" if chunked else "-one-call backward"),
+                   "B": B, "H": H, "d": d, "N": N, "T": T, "blocks": C, "q_k_v": "bf16",
+                   "grads": "f32", "state_grads": chunked},
+        "hbm_frac": call_b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "us_per_block": ms * 1e3 / C,
+        "roofline": {"bound": "hbm", "kernel": f"bwd_key_bf16<{d}>",
+                     "achieved": k_b / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": k_b / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_alg_per_launch": k_b, "launch_us": k_ms * 1e3},
+        "stages_us": {"bwd_query": q_ms * 1e3, "suffix_scan": scan_ms * 1e3,
+                      "bwd_key": k_ms * 1e3, "event_samples": int(stages.shape[0])},
+        "bwd_query_GBs": q_b / (q_ms * 1e-3) / 1e9,
+        "bwd_key_GBs": k_b / (k_ms * 1e-3) / 1e9,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,7 +351,7 @@ def main():
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--workload", default="chunk720p",
                     choices=["chunk720p", "global480p", "global720p", "stream480p", "longhorizon",
-                             "stream480p_onecall", "longhorizon_onecall"])
+                             "stream480p_onecall", "longhorizon_onecall"] + list(BACKWARD))
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-stage HIP events on every N-th timed step")
     ap.add_argument("--plain-steps", type=int, default=0,
@@ -266,6 +371,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
+        return
+    if args.workload in BACKWARD:
+        bench_backward(args)
         return
     if args.workload != "chunk720p":
         bench_other(args)

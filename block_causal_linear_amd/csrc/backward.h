@@ -92,19 +92,37 @@ __device__ void build_col_frags(const float* X, uint4 (*frag)[kWave], int wave, 
   }
 }
 
-// W bfloat16 values of one token row (features f .. f + W - 1) as floats.
-template <int W>
-__device__ __forceinline__ void load_row_w(const uint16_t* p, float (&x)[W]) {
-  if constexpr (W == 4) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    x[0] = __uint_as_float(u.x << 16);
-    x[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    x[2] = __uint_as_float(u.y << 16);
-    x[3] = __uint_as_float(u.y & 0xFFFF0000u);
-  } else {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
-    x[0] = __uint_as_float(u << 16);
-    x[1] = __uint_as_float(u & 0xFFFF0000u);
+// Eight bfloat16 values, all zero except element c (0 <= c < 8), which is
+// 1.0; all zero for any other c.
+__device__ __forceinline__ uint4 onehot_bf16x8(int c) {
+  const uint32_t one = (c & 1) ? 0x3F800000u : 0x00003F80u;
+  const int w = c >> 1;
+  return make_uint4(w == 0 ? one : 0u, w == 1 ? one : 0u, w == 2 ? one : 0u, w == 3 ? one : 0u);
+}
+
+// The wave's A-operand rows (16 tokens x d features, bf16, lane (n, g) holding
+// row n, features 32 s + 8 g .. + 7) re-expressed in the accumulator layout:
+// x[nb][i] = A[4 g + i][bwd_col(nb, n)].  Each is an MFMA against a one-hot
+// B operand, so every output is one product with 1.0 plus zeros: exact.
+// This gives the epilogue the inputs' values where it needs them without
+// reading them from memory a second time.
+template <int D>
+__device__ __forceinline__ void rows_to_acc(const uint4 (&a)[BwdShape<D>::KS],
+                                            f32x4 (&x)[BwdShape<D>::NBK], int lane) {
+  using Sh = BwdShape<D>;
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int nb = 0; nb < Sh::NBK; ++nb) {
+    x[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int f = bwd_col<D>(nb, n);
+    // features of block nb: 16 W (nb / W) + [0, 16 W), i.e. k-steps s0 .. s1
+    constexpr int SPAN = 16 * Sh::W / 32;
+    const int s0 = (16 * Sh::W * (nb / Sh::W)) / 32;
+#pragma unroll
+    for (int e = 0; e < SPAN; ++e) {
+      const int s = s0 + e;
+      x[nb] = mfma_16x16x32(a[s], onehot_bf16x8(f - 32 * s - 8 * g), x[nb]);
+    }
   }
 }
 
@@ -162,19 +180,44 @@ struct DoRow<true> {
 };
 
 // ---------------------------------------------------------------------------
-// bwd_query_bf16: dQ and the partials of (G_n, g_n), bfloat16 queries.
-//
-// Grid (blocks x splits, H, B), as the KV reduction: workgroup (c, s) covers
-// a contiguous token range of block c and writes its partial to
-// dst[((b H + h) C + c) splits + s] (d*d floats of G, then d of g).
+// Work items of the two bf16 kernels.  Block c of (b, h) is cut into S
+// items; item (b, h, c, s) takes the block's 64-token tiles s, s + S,
+// s + 2 S, ...  A persistent grid takes items blockIdx.x, + gridDim.x, ...
+// (items are numbered ((b H + h) C + c) S + s): at any moment the running
+// items cover whole groups of S items of a few heads, so the workgroups of a
+// head sweep adjacent tiles together, and the host picks S so that the item
+// count is a multiple of the grid where it can.
+struct BwdItem {
+  size_t pair;  // (b H + h) C + c
+  int split;
+  int c0, c1;   // the block's token range
+  int mine;     // tiles of this item
+};
+
+__device__ __forceinline__ BwdItem bwd_item(int item, int S, int nblk, int N, int TB, int TT) {
+  BwdItem w;
+  w.pair = static_cast<size_t>(item / S);
+  w.split = item - static_cast<int>(w.pair) * S;
+  const int blk = static_cast<int>(w.pair % nblk);
+  w.c0 = blk * TB;
+  w.c1 = min(N, w.c0 + TB);
+  const int ntb = w.c1 > w.c0 ? (w.c1 - w.c0 + TT - 1) / TT : 0;
+  w.mine = w.split < ntb ? (ntb - w.split + S - 1) / S : 0;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_query_bf16: dQ and the partials of (G_n, g_n), bfloat16 queries.  Item
+// (b, h, c, s) writes its partial to dst[item] (d*d floats of G, then d of g).
 //
 // Per 64-token tile, four waves:
 //  1. wave w takes tokens 16 w .. 16 w + 15 as MFMA rows (A row m holds token
 //     4 (m % 4) + m / 4, so each store instruction writes 4 consecutive
 //     token rows): den from phi(Q) against z, w_i from dO (bf16 hi/lo) against
-//     S (hi/lo, "rows of S"); in the epilogue t_i is a 16-lane sum, dq is
-//     formed and stored, and 1/den, dden go to LDS; phi(Q) rows go to an LDS
-//     tile (token-major, swizzled as in the KV reduction);
+//     S (hi/lo, "rows of S"); phi(Q) is moved to the accumulator layout with
+//     one-hot MFMAs; in the epilogue t_i is a 16-lane sum, dq is formed and
+//     stored, and 1/den, dden go to LDS; phi(Q) rows go to an LDS tile
+//     (token-major, swizzled as in the KV reduction);
 //  2. after a barrier each lane scales its dO by 1/den and writes dnum as a
 //     bf16 hi/lo pair into two more LDS tiles;
 //  3. after a barrier the waves accumulate G (2 x 2 blocks of d/2 x d/2) over
@@ -182,14 +225,22 @@ struct DoRow<true> {
 //     does; waves in block column 0 also accumulate g against dden.
 // The phi(Q) tile and the per-token scalars are double-buffered: a wave
 // writes tile i + 1's only after the barrier of step 1 of tile i, which every
-// wave reaches after its step 3 of tile i - 1.
+// wave reaches after its step 3 of tile i - 1.  A barrier at the start of
+// every item separates it from the previous item's LDS use.
+// Waves per SIMD each kernel is compiled for (its launch bound); with four
+// waves per workgroup this is also the number of resident workgroups per CU
+// (LDS permitting: 23 / 53 / 137 KB per workgroup at d = 32 / 64 / 128),
+// which sizes the persistent grid.
+template <int D>
+constexpr int bwd_query_min_waves() {
+  return D == 128 ? 1 : D == 64 ? 2 : 4;
+}
+
 template <int D, bool GO_BF16>
-__global__ __launch_bounds__(256) void bwd_query_bf16(const uint16_t* __restrict__ q,
-                                                      const void* __restrict__ dout,
-                                                      const float* __restrict__ states,
-                                                      void* __restrict__ dq, int N, int TB,
-                                                      int splits, int tps, float eps,
-                                                      float* __restrict__ dst) {
+__global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
+    const uint16_t* __restrict__ q, const void* __restrict__ dout,
+    const float* __restrict__ states, void* __restrict__ dq, int N, int TB, int nblk, int S,
+    int items, float eps, float* __restrict__ dst) {
   using Sh = BwdShape<D>;
   constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, GRP = Sh::GRP, UPR = Sh::UPR;
   constexpr int TT = Sh::TT, BR = Sh::BR, NR = Sh::NR;
@@ -201,248 +252,242 @@ __global__ __launch_bounds__(256) void bwd_query_bf16(const uint16_t* __restrict
   __shared__ uint4 dnh[UNITS], dnl[UNITS];
   __shared__ float srd[2][TT], sdd[2][TT];
 
-  const int nblk = gridDim.x / splits;
-  const int blk = blockIdx.x / splits;
-  const int split = blockIdx.x - blk * splits;
-  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
-  const int c0 = blk * TB;
-  const int c1 = min(N, c0 + TB);
-  const int t0 = c0 + split * tps;
-  const int t1 = min(c1, t0 + tps);
-  const float* st = states + (bh * nblk + blk) * E;
-
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int n = lane & 15, g = lane >> 4;
   const int sig = 4 * (n & 3) + (n >> 2);
   const int wi = wave >> 1, wj = wave & 1;
+  const int ta = 16 * wave + sig;  // this lane's A row within a tile
 
-  build_row_frags<D>(st, sfrag, wave, lane);
-  if (wave < KS) {
-    const float* zp = st + D * D + 32 * wave + 8 * g;
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) split_bf16x2(zp[j], zp[j + 1], &h[j / 2], &l[j / 2]);
-    zfrag[2 * wave][lane] = make_uint4(h[0], h[1], h[2], h[3]);
-    zfrag[2 * wave + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
-  }
-  float zc[NBK];
-#pragma unroll
-  for (int nb = 0; nb < NBK; ++nb) zc[nb] = st[D * D + bwd_col<D>(nb, n)];
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const BwdItem w = bwd_item(item, S, nblk, N, TB, TT);
+    const size_t bh = w.pair / nblk;
+    const float* st = states + w.pair * E;
+    const uint4* qb = reinterpret_cast<const uint4*>(q + bh * static_cast<size_t>(N) * D);
+    const size_t row0 = bh * static_cast<size_t>(N);
+    auto tile_base = [&](int k) { return w.c0 + (w.split + k * S) * TT; };
 
-  f32x4 accG[NR][NR], accg[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    accg[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NR; ++c) accG[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();
-
-  const uint4* qb = reinterpret_cast<const uint4*>(q + bh * static_cast<size_t>(N) * D);
-  const uint16_t* qrow = q + bh * static_cast<size_t>(N) * D;
-  const size_t row0 = bh * static_cast<size_t>(N);
-  uint4 qa[KS];
-  DoRow<GO_BF16> da[KS];
-  // Rows past the range load its last row; they are zeroed where used.
-  auto gload = [&](int it) {
-    const int tc = min(t0 + it * TT + 16 * wave + sig, t1 - 1);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qa[s] = qb[static_cast<size_t>(tc) * UPR + 4 * s + g];
-      da[s].load(dout, (row0 + tc) * D + 32 * s + 8 * g);
-    }
-  };
-
-  const int ntiles = t1 > t0 ? (t1 - t0 + TT - 1) / TT : 0;
-  if (ntiles > 0) gload(0);
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int ta = 16 * wave + sig;  // this lane's A row within the tile
-    const bool va = t0 + it * TT + ta < t1;
-    uint4 qp[KS];
-    float dv[KS][8];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      qp[s] = va ? relu_bf16x8(qa[s]) : make_uint4(0, 0, 0, 0);
-      da[s].get(dv[s]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dv[s][j] = va ? dv[s][j] : 0.f;
-    }
-    if (it + 1 < ntiles) gload(it + 1);
-
-    // 1. phi(Q) rows to the tile; den and w on MFMA
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qt[buf][ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta))] = qp[s];
-    f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 accw[NBK];
-#pragma unroll
-    for (int nb = 0; nb < NBK; ++nb) accw[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      accz = mfma_16x16x32(qp[s], zfrag[2 * s][lane], accz);
-      accz = mfma_16x16x32(qp[s], zfrag[2 * s + 1][lane], accz);
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) split_bf16x2(dv[s][j], dv[s][j + 1], &h[j / 2], &l[j / 2]);
-      const uint4 ah = make_uint4(h[0], h[1], h[2], h[3]);
-      const uint4 al = make_uint4(l[0], l[1], l[2], l[3]);
-#pragma unroll
-      for (int nb = 0; nb < NBK; ++nb) {
-        const uint4 bh16 = sfrag[2 * (s * NBK + nb)][lane];
-        const uint4 bl16 = sfrag[2 * (s * NBK + nb) + 1][lane];
-        accw[nb] = mfma_16x16x32(ah, bh16, accw[nb]);
-        accw[nb] = mfma_16x16x32(ah, bl16, accw[nb]);
-        if constexpr (!GO_BF16) accw[nb] = mfma_16x16x32(al, bh16, accw[nb]);
-      }
-    }
-    // epilogue: rows 4 g + i hold tokens 4 i + g of the wave's sixteen
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = 16 * wave + 4 * i + g;
-      const int tok = t0 + it * TT + tt;
-      const int tc = min(tok, t1 - 1);
-      float qf[NBK];
-#pragma unroll
-      for (int gr = 0; gr < GRP; ++gr) {
-        float x[W];
-        load_row_w<W>(qrow + static_cast<size_t>(tc) * D + 16 * W * gr + W * n, x);
-#pragma unroll
-        for (int e = 0; e < W; ++e) qf[gr * W + e] = x[e];
-      }
-      float t = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NBK; ++nb) t = fmaf(fmaxf(qf[nb], 0.f), accw[nb][i], t);
-      t += __shfl_xor(t, 1, 16);
-      t += __shfl_xor(t, 2, 16);
-      t += __shfl_xor(t, 4, 16);
-      t += __shfl_xor(t, 8, 16);
-      // rows past the range have phi(q) = 0 and dO = 0; rd = 0 keeps them
-      // exactly zero even when eps = 0
-      const float rd = tok < t1 ? fast_rcp(accz[i] + eps) : 0.f;
-      const float c = t * rd;
-      if (tok < t1) {
-#pragma unroll
-        for (int gr = 0; gr < GRP; ++gr) {
-          float x[W];
-#pragma unroll
-          for (int e = 0; e < W; ++e) {
-            const int nb = gr * W + e;
-            const float gq = (accw[nb][i] - c * zc[nb]) * rd;
-            x[e] = qf[nb] > 0.f ? gq : 0.f;
-          }
-          store_row_w<W, GO_BF16>(dq, (row0 + tok) * D + 16 * W * gr + W * n, x);
-        }
-      }
-      if (n == 0) {
-        srd[buf][tt] = rd;
-        sdd[buf][tt] = -c * rd;
-      }
-    }
-    __syncthreads();
-
-    // 2. dnum = dO / den as a bf16 hi/lo pair, token-major
-    {
-      const float rd = srd[buf][ta];
+    // PF register stages: while tile k is processed, the loads of tiles
+    // k + 1 .. k + PF are in flight (one stage at d = 128, where registers
+    // are short).  Rows past the block load its last row; they are zeroed
+    // where used.
+    constexpr int PF = D == 128 ? 1 : 2;
+    uint4 qa0[KS], qa1[KS];
+    DoRow<GO_BF16> da0[KS], da1[KS];
+    auto gload = [&](int k, uint4 (&qa)[KS], DoRow<GO_BF16> (&da)[KS]) {
+      const int tc = min(tile_base(k) + ta, w.c1 - 1);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int j = 0; j < 8; j += 2)
-          split_bf16x2(dv[s][j] * rd, dv[s][j + 1] * rd, &h[j / 2], &l[j / 2]);
-        const int u = ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta));
-        dnh[u] = make_uint4(h[0], h[1], h[2], h[3]);
-        dnl[u] = make_uint4(l[0], l[1], l[2], l[3]);
+        qa[s] = qb[static_cast<size_t>(tc) * UPR + 4 * s + g];
+        da[s].load(dout, (row0 + tc) * D + 32 * s + 8 * g);
       }
+    };
+    if (w.mine > 0) gload(0, qa0, da0);
+    if (PF == 2 && w.mine > 1) gload(1, qa1, da1);
+
+    __syncthreads();  // the previous item's LDS readers are done
+    build_row_frags<D>(st, sfrag, wave, lane);
+    if (wave < KS) {
+      const float* zp = st + D * D + 32 * wave + 8 * g;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) split_bf16x2(zp[j], zp[j + 1], &h[j / 2], &l[j / 2]);
+      zfrag[2 * wave][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+      zfrag[2 * wave + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+    float zc[NBK];
+#pragma unroll
+    for (int nb = 0; nb < NBK; ++nb) zc[nb] = st[D * D + bwd_col<D>(nb, n)];
+
+    f32x4 accG[NR][NR], accg[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      accg[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NR; ++c) accG[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
 
-    // 3. G += phi(Q)^T dnum, g += phi(Q)^T dden over the tile's tokens
-    const uint16_t* lq = reinterpret_cast<const uint16_t*>(qt[buf]);
-    const uint16_t* lh = reinterpret_cast<const uint16_t*>(dnh);
-    const uint16_t* ll = reinterpret_cast<const uint16_t*>(dnl);
+    auto tile = [&](int k, uint4 (&qa)[KS], DoRow<GO_BF16> (&da)[KS]) {
+      const int buf = k & 1;
+      const int base = tile_base(k);
+      const bool va = base + ta < w.c1;
+      uint4 qp[KS];
+      float dv[KS][8];
 #pragma unroll
-    for (int ks = 0; ks < TT; ks += 32) {
-      uint4 a[NR];
+      for (int s = 0; s < KS; ++s) {
+        qp[s] = va ? relu_bf16x8(qa[s]) : make_uint4(0, 0, 0, 0);
+        da[s].get(dv[s]);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) a[r] = tile_column8<UPR>(lq, ks, wi * BR + 16 * r, lane);
+        for (int j = 0; j < 8; ++j) dv[s][j] = va ? dv[s][j] : 0.f;
+      }
+      if (k + PF < w.mine) gload(k + PF, qa, da);
+
+      // 1. phi(Q) rows to the tile; den and w on MFMA
 #pragma unroll
-      for (int c = 0; c < NR; ++c) {
-        const uint4 bh16 = tile_column8<UPR>(lh, ks, wj * BR + 16 * c, lane);
-        const uint4 bl16 = tile_column8<UPR>(ll, ks, wj * BR + 16 * c, lane);
+      for (int s = 0; s < KS; ++s) qt[buf][ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta))] = qp[s];
+      f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 accw[NBK];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          accG[r][c] = mfma_16x16x32(a[r], bh16, accG[r][c]);
-          accG[r][c] = mfma_16x16x32(a[r], bl16, accG[r][c]);
+      for (int nb = 0; nb < NBK; ++nb) accw[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        accz = mfma_16x16x32(qp[s], zfrag[2 * s][lane], accz);
+        accz = mfma_16x16x32(qp[s], zfrag[2 * s + 1][lane], accz);
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) split_bf16x2(dv[s][j], dv[s][j + 1], &h[j / 2], &l[j / 2]);
+        const uint4 ah = make_uint4(h[0], h[1], h[2], h[3]);
+        const uint4 al = make_uint4(l[0], l[1], l[2], l[3]);
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb) {
+          const uint4 bh16 = sfrag[2 * (s * NBK + nb)][lane];
+          const uint4 bl16 = sfrag[2 * (s * NBK + nb) + 1][lane];
+          accw[nb] = mfma_16x16x32(ah, bh16, accw[nb]);
+          accw[nb] = mfma_16x16x32(ah, bl16, accw[nb]);
+          if constexpr (!GO_BF16) accw[nb] = mfma_16x16x32(al, bh16, accw[nb]);
         }
       }
-      if (wj == 0) {
-        uint4 ddh = make_uint4(0, 0, 0, 0), ddl = make_uint4(0, 0, 0, 0);
+      // phi(Q) in the accumulator layout (exact), for t_i and the mask
+      f32x4 qacc[NBK];
+      rows_to_acc<D>(qp, qacc, lane);
+      // epilogue: rows 4 g + i hold tokens 4 i + g of the wave's sixteen
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = 16 * wave + 4 * i + g;
+        const int tok = base + tt;
+        float t = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb) t = fmaf(qacc[nb][i], accw[nb][i], t);
+        t += __shfl_xor(t, 1, 16);
+        t += __shfl_xor(t, 2, 16);
+        t += __shfl_xor(t, 4, 16);
+        t += __shfl_xor(t, 8, 16);
+        // rows past the block have phi(q) = 0 and dO = 0; rd = 0 keeps them
+        // exactly zero even when eps = 0
+        const float rd = tok < w.c1 ? fast_rcp(accz[i] + eps) : 0.f;
+        const float c = t * rd;
+        if (tok < w.c1) {
+#pragma unroll
+          for (int gr = 0; gr < GRP; ++gr) {
+            float x[W];
+#pragma unroll
+            for (int e = 0; e < W; ++e) {
+              const int nb = gr * W + e;
+              const float gq = (accw[nb][i] - c * zc[nb]) * rd;
+              x[e] = qacc[nb][i] > 0.f ? gq : 0.f;
+            }
+            store_row_w<W, GO_BF16>(dq, (row0 + tok) * D + 16 * W * gr + W * n, x);
+          }
+        }
         if (n == 0) {
-          const float* p = &sdd[buf][ks + 8 * g];
+          srd[buf][tt] = rd;
+          sdd[buf][tt] = -c * rd;
+        }
+      }
+      __syncthreads();
+
+      // 2. dnum = dO / den as a bf16 hi/lo pair, token-major
+      {
+        const float rd = srd[buf][ta];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
           uint32_t h[4], l[4];
 #pragma unroll
-          for (int j = 0; j < 8; j += 2) split_bf16x2(p[j], p[j + 1], &h[j / 2], &l[j / 2]);
-          ddh = make_uint4(h[0], h[1], h[2], h[3]);
-          ddl = make_uint4(l[0], l[1], l[2], l[3]);
-        }
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          accg[r] = mfma_16x16x32(a[r], ddh, accg[r]);
-          accg[r] = mfma_16x16x32(a[r], ddl, accg[r]);
+          for (int j = 0; j < 8; j += 2)
+            split_bf16x2(dv[s][j] * rd, dv[s][j + 1] * rd, &h[j / 2], &l[j / 2]);
+          const int u = ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta));
+          dnh[u] = make_uint4(h[0], h[1], h[2], h[3]);
+          dnl[u] = make_uint4(l[0], l[1], l[2], l[3]);
         }
       }
-    }
-  }
+      __syncthreads();
 
-  float* o = dst + ((bh * nblk + blk) * splits + split) * static_cast<size_t>(E);
+      // 3. G += phi(Q)^T dnum, g += phi(Q)^T dden over the tile's tokens
+      const uint16_t* lq = reinterpret_cast<const uint16_t*>(qt[buf]);
+      const uint16_t* lh = reinterpret_cast<const uint16_t*>(dnh);
+      const uint16_t* ll = reinterpret_cast<const uint16_t*>(dnl);
 #pragma unroll
-  for (int r = 0; r < NR; ++r)
+      for (int ks = 0; ks < TT; ks += 32) {
+        uint4 a[NR];
 #pragma unroll
-    for (int c = 0; c < NR; ++c)
+        for (int r = 0; r < NR; ++r) a[r] = tile_column8<UPR>(lq, ks, wi * BR + 16 * r, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        o[(wi * BR + 16 * r + 4 * g + i) * D + wj * BR + 16 * c + n] = accG[r][c][i];
-  if (wj == 0 && n == 0) {
+        for (int c = 0; c < NR; ++c) {
+          const uint4 bh16 = tile_column8<UPR>(lh, ks, wj * BR + 16 * c, lane);
+          const uint4 bl16 = tile_column8<UPR>(ll, ks, wj * BR + 16 * c, lane);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            accG[r][c] = mfma_16x16x32(a[r], bh16, accG[r][c]);
+            accG[r][c] = mfma_16x16x32(a[r], bl16, accG[r][c]);
+          }
+        }
+        if (wj == 0) {
+          uint4 ddh = make_uint4(0, 0, 0, 0), ddl = make_uint4(0, 0, 0, 0);
+          if (n == 0) {
+            const float* pp = &sdd[buf][ks + 8 * g];
+            uint32_t h[4], l[4];
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) split_bf16x2(pp[j], pp[j + 1], &h[j / 2], &l[j / 2]);
+            ddh = make_uint4(h[0], h[1], h[2], h[3]);
+            ddl = make_uint4(l[0], l[1], l[2], l[3]);
+          }
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            accg[r] = mfma_16x16x32(a[r], ddh, accg[r]);
+            accg[r] = mfma_16x16x32(a[r], ddl, accg[r]);
+          }
+        }
+      }
+    };
+    for (int k = 0; k < w.mine; k += PF) {
+      tile(k, qa0, da0);
+      if (PF == 2 && k + 1 < w.mine) tile(k + 1, qa1, da1);
+    }
+
+    float* o = dst + static_cast<size_t>(item) * E;
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[D * D + wi * BR + 16 * r + 4 * g + i] = accg[r][i];
+      for (int c = 0; c < NR; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          o[(wi * BR + 16 * r + 4 * g + i) * D + wj * BR + 16 * c + n] = accG[r][c][i];
+    if (wj == 0 && n == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[D * D + wi * BR + 16 * r + 4 * g + i] = accg[r][i];
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_key_bf16: dK and dV, bfloat16 keys and values.  Grid (blocks x splits,
-// H, B); workgroup (c, s) reads R_c ("rows of R" and "columns of R" operand
-// sets, built once into LDS) and covers a contiguous token range of block c.
-// Each wave takes 16 tokens per step as MFMA rows:
+// bwd_key_bf16: dK and dV, bfloat16 keys and values.  For each item the
+// workgroup builds two operand sets of R_c in LDS ("rows of R" and "columns
+// of R"); each wave takes 16 tokens of every tile as MFMA rows:
 //   dphi(k) = v R^T + r  (A = v, B = rows of R),
 //   dv      = phi(k) R   (A = phi(k), B = columns of R),
-// and stores both with the readout's 4-token-row store pattern.  No barrier
-// inside the loop.
+// masks dphi(k) with phi(k) moved to the accumulator layout by one-hot
+// MFMAs, and stores both with the readout's 4-token-row store pattern.  No
+// barrier inside an item.
+// (LDS: 8 / 32 / 128 KB per workgroup at d = 32 / 64 / 128)
+template <int D>
+constexpr int bwd_key_min_waves() {
+  return D == 128 ? 1 : D == 64 ? 4 : 6;
+}
+
 template <int D, bool GO_BF16>
-__global__ __launch_bounds__(256) void bwd_key_bf16(const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v,
-                                                    const float* __restrict__ R,
-                                                    void* __restrict__ dk, void* __restrict__ dv,
-                                                    int N, int TB, int splits, int tps) {
+__global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ R,
+    void* __restrict__ dk, void* __restrict__ dv, int N, int TB, int nblk, int S, int items) {
   using Sh = BwdShape<D>;
   constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, GRP = Sh::GRP, UPR = Sh::UPR;
+  constexpr int TT = Sh::TT;
   constexpr int E = D * D + D;
   __shared__ uint4 rrow[Sh::NF][kWave];
   __shared__ uint4 rcol[Sh::NF][kWave];
-
-  const int nblk = gridDim.x / splits;
-  const int blk = blockIdx.x / splits;
-  const int split = blockIdx.x - blk * splits;
-  const size_t bh = static_cast<size_t>(blockIdx.z) * gridDim.y + blockIdx.y;
-  const int c0 = blk * TB;
-  const int c1 = min(N, c0 + TB);
-  const int t0 = c0 + split * tps;
-  const int t1 = min(c1, t0 + tps);
-  if (t1 <= t0) return;
-  const float* rs = R + (bh * nblk + blk) * E;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -450,71 +495,83 @@ __global__ __launch_bounds__(256) void bwd_key_bf16(const uint16_t* __restrict__
   const int n = lane & 15, g = lane >> 4;
   const int sig = 4 * (n & 3) + (n >> 2);
 
-  build_row_frags<D>(rs, rrow, wave, lane);
-  build_col_frags<D>(rs, rcol, wave, lane);
-  float rc[NBK];
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const BwdItem w = bwd_item(item, S, nblk, N, TB, TT);
+    const size_t bh = w.pair / nblk;
+    const float* rs = R + w.pair * E;
+    const size_t row0 = bh * static_cast<size_t>(N);
+    const uint4* kb = reinterpret_cast<const uint4*>(k + row0 * D);
+    const uint4* vb = reinterpret_cast<const uint4*>(v + row0 * D);
+    // this wave's 16 tokens of tile j of the item
+    auto wave_base = [&](int j) { return w.c0 + (w.split + j * S) * TT + 16 * wave; };
+    uint4 ka[KS], va[KS];
+    auto gload = [&](int j) {
+      const int tc = min(wave_base(j) + sig, w.c1 - 1);
 #pragma unroll
-  for (int nb = 0; nb < NBK; ++nb) rc[nb] = rs[D * D + bwd_col<D>(nb, n)];
-  __syncthreads();
+      for (int s = 0; s < KS; ++s) {
+        ka[s] = kb[static_cast<size_t>(tc) * UPR + 4 * s + g];
+        va[s] = vb[static_cast<size_t>(tc) * UPR + 4 * s + g];
+      }
+    };
+    if (w.mine > 0) gload(0);
 
-  const size_t row0 = bh * static_cast<size_t>(N);
-  const uint4* kb = reinterpret_cast<const uint4*>(k + row0 * D);
-  const uint4* vb = reinterpret_cast<const uint4*>(v + row0 * D);
-  const uint16_t* krow = k + row0 * D;
-  uint4 ka[KS], va[KS];
-  // this wave's 16-token steps: t0 + 16 (4 i + wave), i = 0, 1, ...
-  const int nsteps = (t1 - t0 + 15) / 16;
-  auto gload = [&](int step) {
-    const int tc = min(t0 + 16 * step + sig, t1 - 1);
+    __syncthreads();  // the previous item's LDS readers are done
+    build_row_frags<D>(rs, rrow, wave, lane);
+    build_col_frags<D>(rs, rcol, wave, lane);
+    float rc[NBK];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      ka[s] = kb[static_cast<size_t>(tc) * UPR + 4 * s + g];
-      va[s] = vb[static_cast<size_t>(tc) * UPR + 4 * s + g];
-    }
-  };
-  if (wave < nsteps) gload(wave);
-  for (int step = wave; step < nsteps; step += 4) {
-    const bool valid = t0 + 16 * step + sig < t1;
-    uint4 kp[KS], vv[KS];
+    for (int nb = 0; nb < NBK; ++nb) rc[nb] = rs[D * D + bwd_col<D>(nb, n)];
+    __syncthreads();
+
+    for (int j = 0; j < w.mine; ++j) {
+      // read the operand fragments from LDS where they are used instead of
+      // holding all of them in registers across the loop
+      asm volatile("" ::: "memory");
+      const int base = wave_base(j);
+      const bool valid = base + sig < w.c1;
+      uint4 kp[KS], vv[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kp[s] = valid ? relu_bf16x8(ka[s]) : make_uint4(0, 0, 0, 0);
-      vv[s] = valid ? va[s] : make_uint4(0, 0, 0, 0);
-    }
-    if (step + 4 < nsteps) gload(step + 4);
-    f32x4 acck[NBK], accv[NBK];
-#pragma unroll
-    for (int nb = 0; nb < NBK; ++nb) {
-      acck[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accv[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS; ++s) {
+        kp[s] = valid ? relu_bf16x8(ka[s]) : make_uint4(0, 0, 0, 0);
+        vv[s] = valid ? va[s] : make_uint4(0, 0, 0, 0);
+      }
+      if (j + 1 < w.mine) gload(j + 1);
+      f32x4 acck[NBK], accv[NBK];
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) {
-        const int f = 2 * (s * NBK + nb);
-        acck[nb] = mfma_16x16x32(vv[s], rrow[f][lane], acck[nb]);
-        acck[nb] = mfma_16x16x32(vv[s], rrow[f + 1][lane], acck[nb]);
-        accv[nb] = mfma_16x16x32(kp[s], rcol[f][lane], accv[nb]);
-        accv[nb] = mfma_16x16x32(kp[s], rcol[f + 1][lane], accv[nb]);
+        acck[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accv[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = t0 + 16 * step + 4 * i + g;
-      if (tok >= t1) continue;
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int gr = 0; gr < GRP; ++gr) {
-        float kf[W], xk[W], xv[W];
-        const int col = 16 * W * gr + W * n;
-        load_row_w<W>(krow + static_cast<size_t>(tok) * D + col, kf);
-#pragma unroll
-        for (int e = 0; e < W; ++e) {
-          const int nb = gr * W + e;
-          xk[e] = kf[e] > 0.f ? acck[nb][i] + rc[nb] : 0.f;
-          xv[e] = accv[nb][i];
+        for (int nb = 0; nb < NBK; ++nb) {
+          const int f = 2 * (s * NBK + nb);
+          acck[nb] = mfma_16x16x32(vv[s], rrow[f][lane], acck[nb]);
+          acck[nb] = mfma_16x16x32(vv[s], rrow[f + 1][lane], acck[nb]);
+          accv[nb] = mfma_16x16x32(kp[s], rcol[f][lane], accv[nb]);
+          accv[nb] = mfma_16x16x32(kp[s], rcol[f + 1][lane], accv[nb]);
         }
-        store_row_w<W, GO_BF16>(dk, (row0 + tok) * D + col, xk);
-        store_row_w<W, GO_BF16>(dv, (row0 + tok) * D + col, xv);
+      // phi(K) in the accumulator layout (exact): its sign is the mask
+      f32x4 kacc[NBK];
+      rows_to_acc<D>(kp, kacc, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = base + 4 * i + g;
+        if (tok >= w.c1) continue;
+#pragma unroll
+        for (int gr = 0; gr < GRP; ++gr) {
+          float xk[W], xv[W];
+          const int col = 16 * W * gr + W * n;
+#pragma unroll
+          for (int e = 0; e < W; ++e) {
+            const int nb = gr * W + e;
+            xk[e] = kacc[nb][i] > 0.f ? acck[nb][i] + rc[nb] : 0.f;
+            xv[e] = accv[nb][i];
+          }
+          store_row_w<W, GO_BF16>(dk, (row0 + tok) * D + col, xk);
+          store_row_w<W, GO_BF16>(dv, (row0 + tok) * D + col, xv);
+        }
       }
     }
   }

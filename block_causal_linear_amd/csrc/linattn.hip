@@ -36,12 +36,23 @@ constexpr int kSweepWorkgroups = 768;
 // (256 measured best at the long-horizon shape among 128..1024).
 constexpr int kSweepWorkgroups128 = 256;
 constexpr int kReadoutTargetWorkgroups = 1024;
-// Backward workgroups the planner aims for: the query-gradient kernel (four
-// waves, 53 KB of LDS at d = 64: three per CU) and the key-gradient kernel
-// (four waves, 32 KB).  At d = 128 both hold 128-137 KB of LDS: one per CU.
-constexpr int kBwdQueryTargetWorkgroups = 768;
-constexpr int kBwdKeyTargetWorkgroups = 1024;
-constexpr int kBwdTargetWorkgroups128 = 256;
+// Resident workgroups of the two bf16 backward kernels on a 256-CU MI355X:
+// their persistent grids.  Each kernel is compiled for a number of waves
+// per SIMD (its launch bound), which with four-wave workgroups is the
+// number of workgroups per CU.
+constexpr int kCUs = 256;
+int bwd_query_capacity(int d) {
+  return kCUs * (d == 128 ? la::bwd_query_min_waves<128>()
+                 : d == 64 ? la::bwd_query_min_waves<64>()
+                           : la::bwd_query_min_waves<32>());
+}
+int bwd_key_capacity(int d) {
+  return kCUs * (d == 128 ? la::bwd_key_min_waves<128>()
+                 : d == 64 ? la::bwd_key_min_waves<64>()
+                           : la::bwd_key_min_waves<32>());
+}
+// float32 backward kernels: workgroups over contiguous token ranges.
+constexpr int kBwdF32TargetWorkgroups = 512;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -245,12 +256,32 @@ int run(const Plan& p, const void* q, const void* k, const void* v, const float*
 struct BwdPlan {
   int nblk;        // blocks (0 when N == 0)
   int T;           // tokens per block
-  int qsplits;     // query-gradient workgroups per block
-  int qtps;        // tokens per query-gradient workgroup
-  int ksplits;     // key-gradient workgroups per block
-  int ktps;        // tokens per key-gradient workgroup
+  int qs;          // query-gradient items (splits) per block
+  int qgrid;       // its grid (bf16: persistent, <= items)
+  int qtps;        // float32: tokens per split
+  int ks;          // key-gradient items per block
+  int kgrid;
+  int ktps;
   size_t ws_bytes; // workspace the plan needs
 };
+
+long long gcd_ll(long long a, long long b) {
+  while (b != 0) {
+    const long long t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Items per block for a persistent grid of `cap` workgroups over `pairs`
+// (b, h, block) pairs: pairs * S = lcm(pairs, cap), a whole number of
+// rounds of the grid, unless that needs more than about four rounds.
+long long items_per_block(long long pairs, long long cap) {
+  long long s = cap / gcd_ll(pairs, cap);
+  const long long most = (4 * cap + pairs - 1) / pairs;
+  return s < most ? s : most;
+}
 
 // ws_avail: the caller's workspace size (SIZE_MAX when planning the size).
 BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest, int krequest,
@@ -259,22 +290,25 @@ BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest
   p.T = T < N ? T : N;
   p.nblk = N == 0 ? 0 : (N + p.T - 1) / p.T;
   if (N == 0) return p;
-  const int tile = in_dt == LA_BF16 ? 64 : 16;
+  const bool bf = in_dt == LA_BF16;
+  const int tile = bf ? 64 : 16;
   const long long pairs = static_cast<long long>(B) * H * p.nblk;
   const size_t st = static_cast<size_t>(d) * d + d;
   const size_t r_bytes = static_cast<size_t>(pairs) * st * sizeof(float);
   const int Tb = p.T;
   const int ntiles = (Tb + tile - 1) / tile;
 
+  // query-gradient splits (each writes one partial state gradient)
   long long s;
   if (qrequest > 0) {
     s = qrequest;
+  } else if (bf) {
+    s = items_per_block(pairs, bwd_query_capacity(d));
   } else {
-    const long long target = d == 128 ? kBwdTargetWorkgroups128 : kBwdQueryTargetWorkgroups;
-    s = (target + pairs - 1) / pairs;
-    const long long by_size = Tb / (kKvMinTokensPerFeature * (d + 1));
-    s = s < by_size ? s : by_size;
+    s = (kBwdF32TargetWorkgroups + pairs - 1) / pairs;
   }
+  const long long by_size = Tb / (kKvMinTokensPerFeature * (d + 1));
+  if (qrequest <= 0 && s > by_size) s = by_size;
   if (s > ntiles) s = ntiles;
   if (s > 1 && ws_avail != SIZE_MAX) {
     // splits + 1 state-sized slots per (b, h, block)
@@ -283,23 +317,37 @@ BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest
     if (s > most) s = most;
   }
   if (s < 1) s = 1;
-  int per = static_cast<int>((Tb + s - 1) / s);
-  p.qtps = (per + tile - 1) / tile * tile;
-  p.qsplits = (Tb + p.qtps - 1) / p.qtps;
-  p.ws_bytes = p.qsplits > 1 ? r_bytes * (p.qsplits + 1) : r_bytes;
+  if (bf) {
+    p.qs = static_cast<int>(s);
+    const long long items = pairs * s;
+    p.qgrid = static_cast<int>(items < bwd_query_capacity(d) ? items : bwd_query_capacity(d));
+  } else {
+    const int per = static_cast<int>((Tb + s - 1) / s);
+    p.qtps = (per + tile - 1) / tile * tile;
+    p.qs = (Tb + p.qtps - 1) / p.qtps;
+  }
+  p.ws_bytes = p.qs > 1 ? r_bytes * (p.qs + 1) : r_bytes;
 
+  // key-gradient items
   long long kw;
   if (krequest > 0) {
     kw = (krequest + pairs - 1) / pairs;
+  } else if (bf) {
+    kw = items_per_block(pairs, bwd_key_capacity(d));
   } else {
-    const long long target = d == 128 ? kBwdTargetWorkgroups128 : kBwdKeyTargetWorkgroups;
-    kw = (target + pairs - 1) / pairs;
+    kw = (kBwdF32TargetWorkgroups + pairs - 1) / pairs;
   }
   if (kw > ntiles) kw = ntiles;
   if (kw < 1) kw = 1;
-  per = static_cast<int>((Tb + kw - 1) / kw);
-  p.ktps = (per + tile - 1) / tile * tile;
-  p.ksplits = (Tb + p.ktps - 1) / p.ktps;
+  if (bf) {
+    p.ks = static_cast<int>(kw);
+    const long long items = pairs * kw;
+    p.kgrid = static_cast<int>(items < bwd_key_capacity(d) ? items : bwd_key_capacity(d));
+  } else {
+    const int per = static_cast<int>((Tb + kw - 1) / kw);
+    p.ktps = (per + tile - 1) / tile * tile;
+    p.ks = (Tb + p.ktps - 1) / p.ktps;
+  }
   return p;
 }
 
@@ -317,16 +365,17 @@ template <int D, bool GO_BF16>
 int launch_bwd_query(const BwdPlan& p, const void* q, const void* dout, const float* states,
                      void* dq, int in_dt, int B, int H, int N, float eps, float* dst,
                      hipStream_t stream) {
-  const dim3 grid(p.nblk * p.qsplits, H, B);
   if (in_dt == LA_BF16) {
-    la::bwd_query_bf16<D, GO_BF16><<<grid, la::BwdShape<D>::NT, 0, stream>>>(
-        static_cast<const uint16_t*>(q), dout, states, dq, N, p.T, p.qsplits, p.qtps, eps, dst);
+    const int items = B * H * p.nblk * p.qs;
+    la::bwd_query_bf16<D, GO_BF16><<<p.qgrid, la::BwdShape<D>::NT, 0, stream>>>(
+        static_cast<const uint16_t*>(q), dout, states, dq, N, p.T, p.nblk, p.qs, items, eps, dst);
   } else {
+    const dim3 grid(p.nblk * p.qs, H, B);
     constexpr size_t smem = la::bwd_query_f32_smem<D>();
     const int rc = allow_smem(&la::bwd_query_f32<D, GO_BF16>, smem);
     if (rc != LA_OK) return rc;
     la::bwd_query_f32<D, GO_BF16><<<grid, la::kBlock, smem, stream>>>(
-        static_cast<const float*>(q), dout, states, dq, N, p.T, p.qsplits, p.qtps, eps, dst);
+        static_cast<const float*>(q), dout, states, dq, N, p.T, p.qs, p.qtps, eps, dst);
   }
   return launched();
 }
@@ -334,17 +383,18 @@ int launch_bwd_query(const BwdPlan& p, const void* q, const void* dout, const fl
 template <int D, bool GO_BF16>
 int launch_bwd_key(const BwdPlan& p, const void* k, const void* v, const float* R, void* dk,
                    void* dv, int in_dt, int B, int H, int N, hipStream_t stream) {
-  const dim3 grid(p.nblk * p.ksplits, H, B);
   if (in_dt == LA_BF16) {
-    la::bwd_key_bf16<D, GO_BF16><<<grid, la::BwdShape<D>::NT, 0, stream>>>(
+    const int items = B * H * p.nblk * p.ks;
+    la::bwd_key_bf16<D, GO_BF16><<<p.kgrid, la::BwdShape<D>::NT, 0, stream>>>(
         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), R, dk, dv, N, p.T,
-        p.ksplits, p.ktps);
+        p.nblk, p.ks, items);
   } else {
+    const dim3 grid(p.nblk * p.ks, H, B);
     constexpr size_t smem = la::bwd_key_f32_smem<D>();
     const int rc = allow_smem(&la::bwd_key_f32<D, GO_BF16>, smem);
     if (rc != LA_OK) return rc;
     la::bwd_key_f32<D, GO_BF16><<<grid, la::kBlock, smem, stream>>>(
-        static_cast<const float*>(k), static_cast<const float*>(v), R, dk, dv, N, p.T, p.ksplits,
+        static_cast<const float*>(k), static_cast<const float*>(v), R, dk, dv, N, p.T, p.ks,
         p.ktps);
   }
   return launched();
@@ -358,7 +408,7 @@ int run_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const
   constexpr int E = D * D + D;
   const int n4 = E / 4;
   float* R = static_cast<float*>(workspace);
-  float* partials = p.qsplits > 1 ? R + static_cast<size_t>(B) * H * p.nblk * E : R;
+  float* partials = p.qs > 1 ? R + static_cast<size_t>(B) * H * p.nblk * E : R;
   int rc;
   if ((rc = record(opts, 0, stream)) != LA_OK) return rc;
   if ((rc = launch_bwd_query<D, GO_BF16>(p, q, dout, states, dq, in_dt, B, H, N, eps, partials,
@@ -367,7 +417,7 @@ int run_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const
   if ((rc = record(opts, 1, stream)) != LA_OK) return rc;
   const dim3 grid((n4 + la::kBlock - 1) / la::kBlock, H, B);
   la::state_suffix_scan<<<grid, la::kBlock, 0, stream>>>(
-      reinterpret_cast<const float4*>(partials), p.nblk, p.qsplits, n4,
+      reinterpret_cast<const float4*>(partials), p.nblk, p.qs, n4,
       reinterpret_cast<const float4*>(dstates), reinterpret_cast<float4*>(R),
       reinterpret_cast<float4*>(dstate_in));
   if ((rc = launched()) != LA_OK) return rc;

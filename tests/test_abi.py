@@ -205,8 +205,9 @@ def test_backward_workspace_size():
     E = 64 * 64 + 64
     # one short block: one query split, the workspace holds R only
     assert la.backward_workspace_size(1, 1, 100, 100, 64) == E * 4
-    # the 720p chunk: 24 query splits per head -> R plus 24 partials per head
-    assert la.backward_workspace_size(1, 32, 75600, 75600, 64) == 32 * E * 4 * 25
+    # the 720p chunk: 16 query items per head (512 = one round of the
+    # persistent grid) -> R plus 16 partials per head
+    assert la.backward_workspace_size(1, 32, 75600, 75600, 64) == 32 * E * 4 * 17
     # config-5 shape in one call: 40 blocks x 64 heads, one split each
     E2 = 128 * 128 + 128
     assert la.backward_workspace_size(4, 16, 40 * 4096, 4096, 128) == 4 * 16 * 40 * E2 * 4
