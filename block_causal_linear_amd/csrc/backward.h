@@ -40,6 +40,20 @@ struct BwdShape {
   static constexpr int NF = KS * NBK * 2;      // operand fragments of one d x d matrix
 };
 
+// Unit swizzle of the query kernel's token-major LDS tiles.  Its writes come
+// from the MFMA A layout: the eight lanes of a 16-byte store instruction
+// hold tokens 4 r + m' of the wave's sixteen (r = lane / 4 in {0, 1},
+// m' = lane % 4), i.e. rows t = 4 m + r with four values of m and two of r.
+// XORing the unit of row t = 4 m + r with 2 (r ^ 2 ((m >> 1) & 1)) + (m & 1)
+// sends those eight rows to eight different 16-byte columns, and keeps the
+// four consecutive rows of a transposing read (one m, r = 0..3) on four
+// different 32-byte column pairs.
+template <int UPR>
+__device__ __forceinline__ int bwd_swizzle(int t) {
+  const int r = t & 3, m = t >> 2;
+  return (2 * (r ^ (2 * ((m >> 1) & 1))) + (m & 1)) & (UPR - 1);
+}
+
 // Accumulator column n of block nb holds feature 16 W (nb / W) + W n + nb % W
 // (the readout's placement): each lane owns W consecutive features per
 // group, so one vector store per (token, group) writes them, and the 16
@@ -126,23 +140,57 @@ __device__ __forceinline__ void rows_to_acc(const uint4 (&a)[BwdShape<D>::KS],
   }
 }
 
-// W values to one token row of a gradient (float32 or bfloat16).
+// Sum over the 16 lanes of each row of a wavefront (lanes 16 g .. 16 g + 15),
+// every lane receiving its row's sum: DPP quad permutations (xor 1, xor 2),
+// then the half-row mirror (lane i <- 7 - i) and the row mirror
+// (i <- 15 - i), each adding the other half of what is summed so far.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float t) {
+  t += dpp_f32<0xB1>(t);   // quad_perm [1, 0, 3, 2]
+  t += dpp_f32<0x4E>(t);   // quad_perm [2, 3, 0, 1]
+  t += dpp_f32<0x141>(t);  // row_half_mirror
+  t += dpp_f32<0x140>(t);  // row_mirror
+  return t;
+}
+
+// Stores of gradient rows go through a raw buffer descriptor that covers the
+// valid rows of one tile only: the hardware drops stores past num_records, so
+// the rows past the end of a block need no branch (a branch around stores
+// makes the compiler wait for every outstanding load, prefetches included).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t tile_rsrc(void* base, size_t elem_off, int elem_size,
+                                            int bytes) {
+  // word 3: 32-bit data format, as raw (untyped) buffer accesses expect
+  return __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(base) + elem_off * elem_size, 0,
+                                           bytes, 0x00020000);
+}
+
+// W values at byte offset `off` of a tile descriptor (float32 or bfloat16).
 template <int W, bool BF16>
-__device__ __forceinline__ void store_row_w(void* base, size_t idx, const float (&x)[W]) {
+__device__ __forceinline__ void store_row_buf(rsrc_t r, int off, const float (&x)[W]) {
   if constexpr (BF16) {
-    uint16_t* p = static_cast<uint16_t*>(base) + idx;
     if constexpr (W == 4) {
-      *reinterpret_cast<u32x2*>(p) = u32x2{pack2(to_bf16(x[0]), to_bf16(x[1])),
-                                           pack2(to_bf16(x[2]), to_bf16(x[3]))};
+      __builtin_amdgcn_raw_buffer_store_b64(
+          u32x2{pack2(to_bf16(x[0]), to_bf16(x[1])), pack2(to_bf16(x[2]), to_bf16(x[3]))}, r,
+          off, 0, 0);
     } else {
-      *reinterpret_cast<uint32_t*>(p) = pack2(to_bf16(x[0]), to_bf16(x[1]));
+      __builtin_amdgcn_raw_buffer_store_b32(pack2(to_bf16(x[0]), to_bf16(x[1])), r, off, 0, 0);
     }
   } else {
-    float* p = static_cast<float*>(base) + idx;
     if constexpr (W == 4) {
-      *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                __float_as_uint(x[3])},
+          r, off, 0, 0);
     } else {
-      *reinterpret_cast<f32x2*>(p) = f32x2{x[0], x[1]};
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x[0]), __float_as_uint(x[1])},
+                                            r, off, 0, 0);
     }
   }
 }
@@ -214,19 +262,23 @@ __device__ __forceinline__ BwdItem bwd_item(int item, int S, int nblk, int N, in
 //  1. wave w takes tokens 16 w .. 16 w + 15 as MFMA rows (A row m holds token
 //     4 (m % 4) + m / 4, so each store instruction writes 4 consecutive
 //     token rows): den from phi(Q) against z, w_i from dO (bf16 hi/lo) against
-//     S (hi/lo, "rows of S"); phi(Q) is moved to the accumulator layout with
-//     one-hot MFMAs; in the epilogue t_i is a 16-lane sum, dq is formed and
-//     stored, and 1/den, dden go to LDS; phi(Q) rows go to an LDS tile
-//     (token-major, swizzled as in the KV reduction);
-//  2. after a barrier each lane scales its dO by 1/den and writes dnum as a
-//     bf16 hi/lo pair into two more LDS tiles;
+//     S (hi/lo, "rows of S"); phi(Q) rows go to an LDS tile (token-major,
+//     swizzled) and come back in the accumulator layout; in the epilogue
+//     t_i is a 16-lane DPP sum, dq is formed and stored, and dden goes to
+//     LDS;
+//  2. each lane fetches 1/den of its own A row from the lanes that formed
+//     it (wave shuffles), scales its dO and writes dnum as a bf16 hi/lo
+//     pair into two more LDS tiles;
 //  3. after a barrier the waves accumulate G (2 x 2 blocks of d/2 x d/2) over
 //     the tile's tokens with transposing LDS reads, as the KV reduction
 //     does; waves in block column 0 also accumulate g against dden.
-// The phi(Q) tile and the per-token scalars are double-buffered: a wave
-// writes tile i + 1's only after the barrier of step 1 of tile i, which every
-// wave reaches after its step 3 of tile i - 1.  A barrier at the start of
-// every item separates it from the previous item's LDS use.
+// The LDS tiles and dden are double-buffered, so one barrier per tile
+// suffices: a wave writes tile i + 1's buffers only after the barrier of
+// tile i, which every wave reaches after its step 3 of tile i - 1, the last
+// reader of those buffers.  At d = 128 (LDS too small for two dnum tiles)
+// the dnum tiles are single and a second barrier before step 2 keeps tile
+// i + 1's writes behind every wave's step 3 of tile i.  A barrier at the
+// start of every item separates it from the previous item's LDS use.
 // Waves per SIMD each kernel is compiled for (its launch bound); with four
 // waves per workgroup this is also the number of resident workgroups per CU
 // (LDS permitting: 23 / 53 / 137 KB per workgroup at d = 32 / 64 / 128),
@@ -248,9 +300,11 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
   constexpr int UNITS = TT * UPR;
   __shared__ uint4 sfrag[Sh::NF][kWave];  // rows of S, hi/lo
   __shared__ uint4 zfrag[KS * 2][kWave];  // z in every column, hi/lo
+  constexpr int DNB = D == 128 ? 1 : 2;   // dnum tile buffers
   __shared__ uint4 qt[2][UNITS];          // phi(Q) tile, two buffers
-  __shared__ uint4 dnh[UNITS], dnl[UNITS];
-  __shared__ float srd[2][TT], sdd[2][TT];
+  __shared__ uint4 dnh[DNB][UNITS], dnl[DNB][UNITS];
+  __shared__ float sdd[2][TT];
+  __shared__ float zsh[D];                // z, for the epilogue
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -270,8 +324,11 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
 
     // PF register stages: while tile k is processed, the loads of tiles
     // k + 1 .. k + PF are in flight (one stage at d = 128, where registers
-    // are short).  Rows past the block load its last row; they are zeroed
-    // where used.
+    // are short).  Rows past the block load its last row again; their
+    // 1/den is set to 0 in the epilogue, which makes their dnum and dden
+    // exactly 0 (no contribution to G or g), and their dq stores fall
+    // outside the tile's descriptor.  (Zeroing them in registers instead
+    // would put a divergent branch, and the waits it brings, in the loop.)
     constexpr int PF = D == 128 ? 1 : 2;
     uint4 qa0[KS], qa1[KS];
     DoRow<GO_BF16> da0[KS], da1[KS];
@@ -283,8 +340,10 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
         da[s].load(dout, (row0 + tc) * D + 32 * s + 8 * g);
       }
     };
-    if (w.mine > 0) gload(0, qa0, da0);
-    if (PF == 2 && w.mine > 1) gload(1, qa1, da1);
+    if (w.mine > 0) {
+      gload(0, qa0, da0);
+      if (PF == 2) gload(1, qa1, da1);
+    }
 
     __syncthreads();  // the previous item's LDS readers are done
     build_row_frags<D>(st, sfrag, wave, lane);
@@ -296,9 +355,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
       zfrag[2 * wave][lane] = make_uint4(h[0], h[1], h[2], h[3]);
       zfrag[2 * wave + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
     }
-    float zc[NBK];
-#pragma unroll
-    for (int nb = 0; nb < NBK; ++nb) zc[nb] = st[D * D + bwd_col<D>(nb, n)];
+    if (tid < D) zsh[tid] = st[D * D + tid];
 
     f32x4 accG[NR][NR], accg[NR];
 #pragma unroll
@@ -312,21 +369,21 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
     auto tile = [&](int k, uint4 (&qa)[KS], DoRow<GO_BF16> (&da)[KS]) {
       const int buf = k & 1;
       const int base = tile_base(k);
-      const bool va = base + ta < w.c1;
+      constexpr int GE = GO_BF16 ? 2 : 4;  // gradient element bytes
+      const rsrc_t rdq =
+          tile_rsrc(dq, (row0 + base) * D, GE, max(0, min(TT, w.c1 - base)) * D * GE);
       uint4 qp[KS];
       float dv[KS][8];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        qp[s] = va ? relu_bf16x8(qa[s]) : make_uint4(0, 0, 0, 0);
+        qp[s] = relu_bf16x8(qa[s]);
         da[s].get(dv[s]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) dv[s][j] = va ? dv[s][j] : 0.f;
       }
-      if (k + PF < w.mine) gload(k + PF, qa, da);
+      gload(k + PF, qa, da);
 
       // 1. phi(Q) rows to the tile; den and w on MFMA
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qt[buf][ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta))] = qp[s];
+      for (int s = 0; s < KS; ++s) qt[buf][ta * UPR + ((4 * s + g) ^ bwd_swizzle<UPR>(ta))] = qp[s];
       f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
       f32x4 accw[NBK];
 #pragma unroll
@@ -349,74 +406,105 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
           if constexpr (!GO_BF16) accw[nb] = mfma_16x16x32(al, bh16, accw[nb]);
         }
       }
-      // phi(Q) in the accumulator layout (exact), for t_i and the mask
+      // phi(Q) in the accumulator layout, for t_i and the mask: read back
+      // from the tile rows this wave has just written (its own rows only;
+      // a wavefront's LDS operations complete in order, the fences keep the
+      // compiler from moving the reads above the writes)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       f32x4 qacc[NBK];
-      rows_to_acc<D>(qp, qacc, lane);
+      {
+        const uint16_t* lq = reinterpret_cast<const uint16_t*>(qt[buf]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = 16 * wave + 4 * i + g;
+#pragma unroll
+          for (int gr = 0; gr < GRP; ++gr) {
+            const int f = 16 * W * gr + W * n;
+            const uint16_t* pq =
+                lq + (tt * UPR + ((f >> 3) ^ bwd_swizzle<UPR>(tt))) * 8 + (f & 7);
+            float x[W];
+            if constexpr (W == 4) {
+              const uint2 u = *reinterpret_cast<const uint2*>(pq);
+              x[0] = __uint_as_float(u.x << 16);
+              x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+              x[2] = __uint_as_float(u.y << 16);
+              x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+            } else {
+              const uint32_t u = *reinterpret_cast<const uint32_t*>(pq);
+              x[0] = __uint_as_float(u << 16);
+              x[1] = __uint_as_float(u & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int e = 0; e < W; ++e) qacc[gr * W + e][i] = x[e];
+          }
+        }
+      }
       // epilogue: rows 4 g + i hold tokens 4 i + g of the wave's sixteen
+      float rdv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tt = 16 * wave + 4 * i + g;
-        const int tok = base + tt;
+        const int tok = base + tt;  // rows past the block are dropped by rdq
         float t = 0.f;
 #pragma unroll
         for (int nb = 0; nb < NBK; ++nb) t = fmaf(qacc[nb][i], accw[nb][i], t);
-        t += __shfl_xor(t, 1, 16);
-        t += __shfl_xor(t, 2, 16);
-        t += __shfl_xor(t, 4, 16);
-        t += __shfl_xor(t, 8, 16);
-        // rows past the block have phi(q) = 0 and dO = 0; rd = 0 keeps them
-        // exactly zero even when eps = 0
+        t = row16_sum(t);
+        // rows past the block: rd = 0 (see the loads above)
         const float rd = tok < w.c1 ? fast_rcp(accz[i] + eps) : 0.f;
+        rdv[i] = rd;
         const float c = t * rd;
-        if (tok < w.c1) {
 #pragma unroll
-          for (int gr = 0; gr < GRP; ++gr) {
-            float x[W];
+        for (int gr = 0; gr < GRP; ++gr) {
+          float x[W];
 #pragma unroll
-            for (int e = 0; e < W; ++e) {
-              const int nb = gr * W + e;
-              const float gq = (accw[nb][i] - c * zc[nb]) * rd;
-              x[e] = qacc[nb][i] > 0.f ? gq : 0.f;
-            }
-            store_row_w<W, GO_BF16>(dq, (row0 + tok) * D + 16 * W * gr + W * n, x);
+          for (int e = 0; e < W; ++e) {
+            const int nb = gr * W + e;
+            const float gq = (accw[nb][i] - c * zsh[bwd_col<D>(nb, n)]) * rd;
+            x[e] = qacc[nb][i] > 0.f ? gq : 0.f;
           }
+          store_row_buf<W, GO_BF16>(rdq, (tt * D + 16 * W * gr + W * n) * GE, x);
         }
-        if (n == 0) {
-          srd[buf][tt] = rd;
-          sdd[buf][tt] = -c * rd;
-        }
+        if (n == 0) sdd[buf][tt] = -c * rd;
       }
-      __syncthreads();
+      if constexpr (DNB == 1) __syncthreads();
 
-      // 2. dnum = dO / den as a bf16 hi/lo pair, token-major
+      // 2. dnum = dO / den as a bf16 hi/lo pair, token-major.  This lane's
+      // A row, token 4 (n % 4) + n / 4, is row n % 4 of lane group n / 4.
       {
-        const float rd = srd[buf][ta];
+        const int src = 16 * (n >> 2) + n;
+        const float r0 = __shfl(rdv[0], src), r1 = __shfl(rdv[1], src);
+        const float r2 = __shfl(rdv[2], src), r3 = __shfl(rdv[3], src);
+        const int ri = n & 3;
+        const float rd = ri == 0 ? r0 : ri == 1 ? r1 : ri == 2 ? r2 : r3;
+        const int db = DNB == 2 ? buf : 0;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
           uint32_t h[4], l[4];
 #pragma unroll
           for (int j = 0; j < 8; j += 2)
             split_bf16x2(dv[s][j] * rd, dv[s][j + 1] * rd, &h[j / 2], &l[j / 2]);
-          const int u = ta * UPR + ((4 * s + g) ^ unit_swizzle<UPR>(ta));
-          dnh[u] = make_uint4(h[0], h[1], h[2], h[3]);
-          dnl[u] = make_uint4(l[0], l[1], l[2], l[3]);
+          const int u = ta * UPR + ((4 * s + g) ^ bwd_swizzle<UPR>(ta));
+          dnh[db][u] = make_uint4(h[0], h[1], h[2], h[3]);
+          dnl[db][u] = make_uint4(l[0], l[1], l[2], l[3]);
         }
       }
       __syncthreads();
 
       // 3. G += phi(Q)^T dnum, g += phi(Q)^T dden over the tile's tokens
       const uint16_t* lq = reinterpret_cast<const uint16_t*>(qt[buf]);
-      const uint16_t* lh = reinterpret_cast<const uint16_t*>(dnh);
-      const uint16_t* ll = reinterpret_cast<const uint16_t*>(dnl);
+      const uint16_t* lh = reinterpret_cast<const uint16_t*>(dnh[DNB == 2 ? buf : 0]);
+      const uint16_t* ll = reinterpret_cast<const uint16_t*>(dnl[DNB == 2 ? buf : 0]);
 #pragma unroll
       for (int ks = 0; ks < TT; ks += 32) {
         uint4 a[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) a[r] = tile_column8<UPR>(lq, ks, wi * BR + 16 * r, lane);
+        for (int r = 0; r < NR; ++r) a[r] = tile_column8<UPR, bwd_swizzle<UPR>>(lq, ks, wi * BR + 16 * r, lane);
 #pragma unroll
         for (int c = 0; c < NR; ++c) {
-          const uint4 bh16 = tile_column8<UPR>(lh, ks, wj * BR + 16 * c, lane);
-          const uint4 bl16 = tile_column8<UPR>(ll, ks, wj * BR + 16 * c, lane);
+          const uint4 bh16 = tile_column8<UPR, bwd_swizzle<UPR>>(lh, ks, wj * BR + 16 * c, lane);
+          const uint4 bl16 = tile_column8<UPR, bwd_swizzle<UPR>>(ll, ks, wj * BR + 16 * c, lane);
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             accG[r][c] = mfma_16x16x32(a[r], bh16, accG[r][c]);
@@ -441,9 +529,16 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
         }
       }
     };
+    // Every call and every prefetch is unconditional, so the two register
+    // stages stay in fixed registers (conditional ones make the compiler
+    // shuffle registers that are still being loaded, and wait for them).
+    // With an odd tile count the last call is a tile past the block: all
+    // its rows have rd = 0, so it adds exactly zero to G and g, and its
+    // descriptor covers no bytes.  Its loads (and the prefetches past the
+    // end) read the block's last row.
     for (int k = 0; k < w.mine; k += PF) {
       tile(k, qa0, da0);
-      if (PF == 2 && k + 1 < w.mine) tile(k + 1, qa1, da1);
+      if constexpr (PF == 2) tile(k + 1, qa1, da1);
     }
 
     float* o = dst + static_cast<size_t>(item) * E;
@@ -488,6 +583,7 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
   constexpr int E = D * D + D;
   __shared__ uint4 rrow[Sh::NF][kWave];
   __shared__ uint4 rcol[Sh::NF][kWave];
+  __shared__ float rsh[D];  // r, for the epilogue
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -518,9 +614,7 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
     __syncthreads();  // the previous item's LDS readers are done
     build_row_frags<D>(rs, rrow, wave, lane);
     build_col_frags<D>(rs, rcol, wave, lane);
-    float rc[NBK];
-#pragma unroll
-    for (int nb = 0; nb < NBK; ++nb) rc[nb] = rs[D * D + bwd_col<D>(nb, n)];
+    if (tid < D) rsh[tid] = rs[D * D + tid];
     __syncthreads();
 
     for (int j = 0; j < w.mine; ++j) {
@@ -528,14 +622,20 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
       // holding all of them in registers across the loop
       asm volatile("" ::: "memory");
       const int base = wave_base(j);
-      const bool valid = base + sig < w.c1;
+      // the tile's valid rows; stores past them are dropped (rows past the
+      // block hold copies of its last row: every row is independent here)
+      constexpr int GE = GO_BF16 ? 2 : 4;
+      const int tb = w.c0 + (w.split + j * S) * TT;
+      const int bytes = max(0, min(TT, w.c1 - tb)) * D * GE;
+      const rsrc_t rdk = tile_rsrc(dk, (row0 + tb) * D, GE, bytes);
+      const rsrc_t rdv = tile_rsrc(dv, (row0 + tb) * D, GE, bytes);
       uint4 kp[KS], vv[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        kp[s] = valid ? relu_bf16x8(ka[s]) : make_uint4(0, 0, 0, 0);
-        vv[s] = valid ? va[s] : make_uint4(0, 0, 0, 0);
+        kp[s] = relu_bf16x8(ka[s]);
+        vv[s] = va[s];
       }
-      if (j + 1 < w.mine) gload(j + 1);
+      gload(j + 1);  // past the end: the block's last row again, unused
       f32x4 acck[NBK], accv[NBK];
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) {
@@ -557,8 +657,7 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
       rows_to_acc<D>(kp, kacc, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = base + 4 * i + g;
-        if (tok >= w.c1) continue;
+        const int tt = 16 * wave + 4 * i + g;  // row within the tile
 #pragma unroll
         for (int gr = 0; gr < GRP; ++gr) {
           float xk[W], xv[W];
@@ -566,11 +665,11 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
 #pragma unroll
           for (int e = 0; e < W; ++e) {
             const int nb = gr * W + e;
-            xk[e] = kacc[nb][i] > 0.f ? acck[nb][i] + rc[nb] : 0.f;
+            xk[e] = kacc[nb][i] > 0.f ? acck[nb][i] + rsh[col + e] : 0.f;
             xv[e] = accv[nb][i];
           }
-          store_row_w<W, GO_BF16>(dk, (row0 + tok) * D + col, xk);
-          store_row_w<W, GO_BF16>(dv, (row0 + tok) * D + col, xv);
+          store_row_buf<W, GO_BF16>(rdk, (tt * D + col) * GE, xk);
+          store_row_buf<W, GO_BF16>(rdv, (tt * D + col) * GE, xv);
         }
       }
     }

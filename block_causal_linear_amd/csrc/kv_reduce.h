@@ -67,8 +67,10 @@ __device__ __forceinline__ int unit_swizzle(int t) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Lane's MFMA operand: feature f0 + (lane % 16) of tokens ks + 8g .. +7,
-// g = lane / 16, from a token-major swizzled tile.
-template <int UPR>
+// g = lane / 16, from a token-major tile whose 16-byte unit index is XORed
+// with SWZ(t) in token row t (SWZ keeps the 4 rows one read touches on
+// distinct 32-byte bank groups).
+template <int UPR, int (*SWZ)(int) = unit_swizzle<UPR>>
 __device__ __forceinline__ uint4 tile_column8(const uint16_t* tile, int ks, int f0, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int f = f0 + 4 * (j & 3);  // this lane's 4-feature chunk
@@ -76,7 +78,7 @@ __device__ __forceinline__ uint4 tile_column8(const uint16_t* tile, int ks, int 
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = ks + 8 * g + 4 * h + (j >> 2);
-    const int unit = (f >> 3) ^ unit_swizzle<UPR>(t);
+    const int unit = (f >> 3) ^ SWZ(t);
     const uint16_t* p = tile + (t * UPR + unit) * 8 + (f & 7);
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(p));
