@@ -435,3 +435,54 @@ def test_blockcausal_long_horizon_d128_one_call():
             report(f"long-horizon one-call block {n}", state=es)
         worst = max(worst, eo, es)
     assert worst <= TOL["bf16"], worst
+
+
+# ---------------------------------------------------------------------------
+# the largest sequence the ABI accepts: N * d < 2^31 elements per head
+
+
+def test_max_size_sequence():
+    """One head of 2^25 - 1 tokens at d = 64 (N * d = 2^31 - 64), drawn on
+    the GPU from a seeded generator: la_global_forward and
+    la_blockcausal_forward with two blocks of 2^24 tokens.  The states are
+    compared whole against the oracle's fp64 sums (accumulated over host
+    chunks), the outputs on sampled rows that include the first and last
+    token of each block."""
+    N, d, T = (1 << 25) - 1, 64, 1 << 24
+    gen = torch.Generator(device="cuda").manual_seed(20251203)
+    q, k, v = (torch.randn((1, 1, N, d), generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    out = torch.empty((1, 1, N, d), dtype=torch.float32, device="cuda")
+    _, st = la.global_forward(q, k, v, out=out, eps=EPS)
+    torch.cuda.synchronize()
+
+    S = np.zeros((1, 1, d, d))
+    z = np.zeros((1, 1, d))
+    S_half = z_half = None
+    step = 1 << 21
+    for c0 in range(0, N, step):
+        Kc = host(k[:, :, c0:c0 + step])
+        Vc = host(v[:, :, c0:c0 + step])
+        KV, kk = oracle.kv_of_block(Kc, Vc)
+        S, z = S + KV, z + kk
+        if c0 + step == T:
+            S_half, z_half = S.copy(), z.copy()
+    es, ez = state_err(host(st), S, z)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, T - 1, T, N - 2, N - 1],
+                                     rng.integers(0, N, 4000)]))
+    Qs = host(q[:, :, torch.from_numpy(rows).cuda()])
+    eo = out_err(host(out[:, :, torch.from_numpy(rows).cuda()]), oracle.readout(Qs, S, z, EPS))
+    report("max-size global", out=eo, S=es, z=ez)
+    assert max(eo, es, ez) <= TOL["bf16"], (eo, es, ez)
+
+    _, states = la.blockcausal_forward(q, k, v, T, out=out, eps=EPS)
+    torch.cuda.synchronize()
+    e0 = max(state_err(host(states[:, :, 0]), S_half, z_half))
+    e1 = max(state_err(host(states[:, :, 1]), S, z))
+    o = host(out[:, :, torch.from_numpy(rows).cuda()])
+    first = rows < T
+    eo0 = out_err(o[:, :, first], oracle.readout(Qs[:, :, first], S_half, z_half, EPS))
+    eo1 = out_err(o[:, :, ~first], oracle.readout(Qs[:, :, ~first], S, z, EPS))
+    report("max-size block-causal", out0=eo0, out1=eo1, state0=e0, state1=e1)
+    assert max(e0, e1, eo0, eo1) <= TOL["bf16"], (e0, e1, eo0, eo1)
