@@ -68,6 +68,9 @@ __all__ = [
     "readout_backward",
     "kv_backward",
     "blockcausal_backward",
+    "temporal_conv_chunk",
+    "temporal_conv_stream",
+    "temporal_conv_blockcausal",
 ]
 
 
@@ -319,3 +322,78 @@ def blockcausal_backward(Q, K, V, bounds, dO, eps, S0=None, z0=None, dS=None, dz
     if C == 0:
         return dQ, dK, dV, np.zeros((B, H, d, d)), np.zeros((B, H, d))
     return dQ, dK, dV, RS[0], Rz[0]
+
+
+# --------------------------------------------------------------------------
+# Temporal convolution of the Spatial-Temporal Mix-FFN and its chunk-boundary
+# cache.  [TR] section "Verimli doğrusal DiT": the MLP alternates a 1x3x3
+# spatial and a 3x1x1 temporal convolution; [ZH] section 1: a temporal
+# convolution module models motion between frames.  What the pages leave
+# open, and the reading taken here:
+# * the 3x1x1 convolution is depthwise (one 3-tap filter per channel along
+#   latent frames, as the Mix-FFN's convolutions are per channel), with an
+#   optional per-channel bias;
+# * in block-causal streaming it follows the attention's visibility rule
+#   ([TR]: later blocks read earlier ones, never the reverse; bidirectional
+#   inside a block): frame f of a chunk reads frames f - 1, f, f + 1 of the
+#   sequence, except that a frame of a later chunk is never visible (zero),
+#   and before the first frame of the video there is nothing (zero).  So a
+#   stream needs only the previous chunk's last frame: a one-frame cache,
+#   constant in memory like the attention state.
+# Layout: x [B, F, P, C] (frames, positions per frame, channels), w [C, 3]
+# (taps for f - 1, f, f + 1), b [C], a cache [B, P, C].
+
+
+def temporal_conv_chunk(x, w, b=None, cache=None):
+    """One chunk of F frames: y[f] = w0 x[f-1] + w1 x[f] + w2 x[f+1] + b per
+    channel, with x[-1] = cache (zeros if None: the start of a video) and
+    x[F] = 0 (the next chunk is not visible).  Returns (y, cache_out) with
+    cache_out = x[F-1] (the cache is unchanged when F = 0)."""
+    x = _f64(x)
+    w = _f64(w)
+    B, F, P, C = x.shape
+    prev = np.zeros((B, P, C)) if cache is None else _f64(cache)
+    if F == 0:
+        return np.zeros_like(x), prev
+    xp = np.concatenate([prev[:, None], x, np.zeros((B, 1, P, C))], axis=1)  # [B, F+2, P, C]
+    y = w[:, 0] * xp[:, 0:F] + w[:, 1] * xp[:, 1:F + 1] + w[:, 2] * xp[:, 2:F + 2]
+    if b is not None:
+        y = y + _f64(b)
+    return y, x[:, F - 1]
+
+
+def temporal_conv_stream(chunks, w, b=None, cache=None):
+    """Chunks in order with the one-frame cache carried between them.
+    Returns (outputs, caches)."""
+    outs, caches = [], []
+    for xc in chunks:
+        y, cache = temporal_conv_chunk(xc, w, b, cache)
+        outs.append(y)
+        caches.append(cache)
+    return outs, caches
+
+
+def temporal_conv_blockcausal(x, w, b, Tf, cache=None):
+    """The whole sequence of F frames in chunks of Tf frames, written as an
+    explicit visibility-masked sum (a separate route from the carried
+    cache): y[f] = sum over taps t in {-1, 0, 1} of w[t + 1] x[f + t] where
+    frame g = f + t is used iff 0 <= g < F and chunk(g) <= chunk(f), and
+    x[-1] = cache (zeros if None)."""
+    x = _f64(x)
+    w = _f64(w)
+    B, F, P, C = x.shape
+    y = np.zeros_like(x)
+    for f in range(F):
+        acc = np.zeros((B, P, C))
+        for t in (-1, 0, 1):
+            g = f + t
+            if g < 0:
+                src = None if cache is None else _f64(cache)
+            elif g < F and g // Tf <= f // Tf:
+                src = x[:, g]
+            else:
+                src = None
+            if src is not None:
+                acc = acc + w[:, t + 1] * src
+        y[:, f] = acc if b is None else acc + _f64(b)
+    return y
