@@ -341,6 +341,67 @@ def bench_backward(args):
     print(json.dumps(result), flush=True)
 
 
+TCONV = {
+    # name: (B, frames per chunk, chunks, positions per frame, channels)
+    "tconv720p": (1, 21, 1, 3600, 2048),
+    "tconv480p_onecall": (1, 21, 12, 1560, 1024),
+}
+
+
+def bench_tconv(args):
+    """One step = one temporal-convolution call (bf16 activations in and
+    out, float32 taps and bias, the one-frame cache read and written) over
+    resident inputs: the 720p chunk, or the 1-minute 480p stream in one
+    block-causal call."""
+    import torch
+
+    import block_causal_linear_amd as la
+
+    B, T, n, P, C = TCONV[args.workload]
+    F = T * n
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(3000)
+    log(f"drawing inputs on the GPU for {args.workload} (B={B} F={F} T={T} P={P} C={C})")
+    x = torch.randn((B, F, P, C), generator=gen, device=dev).to(torch.bfloat16)
+    w = torch.randn((C, 3), generator=gen, device=dev).div_(3 ** 0.5)
+    b = torch.randn((C,), generator=gen, device=dev).mul_(0.1)
+    cache = torch.randn((B, P, C), generator=gen, device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    cache_out = torch.empty_like(cache)
+
+    def step():
+        la.temporal_conv_blockcausal(x, w, T, b, cache_in=cache, y=y, cache_out=cache_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # x read once, y written once, the cache read and written (taps and bias
+    # are a few KB)
+    nbytes = 2 * B * F * P * C * 2 + 2 * B * P * C * 2
+    result = {
+        "metric": "latent tokens/sec + % peak HBM BW, Mix-FFN temporal conv with chunk cache",
+        "value": B * F * P / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "frames": F, "frames_per_chunk": T,
+                   "positions_per_frame": P, "channels": C, "x_y": "bf16"},
+        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "kernel": "temporal_conv<true, true>",
+                     "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_alg_per_launch": nbytes, "launch_us": ms * 1e3},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,7 +412,8 @@ def main():
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--workload", default="chunk720p",
                     choices=["chunk720p", "global480p", "global720p", "stream480p", "longhorizon",
-                             "stream480p_onecall", "longhorizon_onecall"] + list(BACKWARD))
+                             "stream480p_onecall", "longhorizon_onecall"] + list(BACKWARD)
+                    + list(TCONV))
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-stage HIP events on every N-th timed step")
     ap.add_argument("--plain-steps", type=int, default=0,
@@ -374,6 +436,9 @@ def main():
         return
     if args.workload in BACKWARD:
         bench_backward(args)
+        return
+    if args.workload in TCONV:
+        bench_tconv(args)
         return
     if args.workload != "chunk720p":
         bench_other(args)

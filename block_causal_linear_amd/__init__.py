@@ -66,6 +66,8 @@ _SIGNATURES = {
                           _P, _Z, _P],
     "la_global_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
                            _P],
+    "la_temporal_conv_chunk": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
+    "la_temporal_conv_blockcausal": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P],
     "la_plan": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
     "la_status_string": [_I],
     "la_abi_version": [],
@@ -394,6 +396,62 @@ def global_backward(q, k, v, state, dout, eps=DEFAULT_EPS, dq=None, dk=None, dv=
         B, H, N, d, _DTYPE[q.dtype], _DTYPE[dout.dtype], float(eps), _ptr(workspace), ws_bytes,
         _stream(q.device)), "la_global_backward")
     return dq, dk, dv
+
+
+def _prepare_tconv(x, weight, bias, cache_in, y, cache_out, out_dtype, want_cache):
+    _need(x, "x")
+    if x.dim() != 4 or x.dtype not in _DTYPE:
+        raise ValueError("x must be [B, F, P, C], float32 or bfloat16")
+    B, F, P, C = x.shape
+    _need(weight, "weight", torch.float32)
+    if tuple(weight.shape) != (C, 3) or weight.device != x.device:
+        raise ValueError(f"weight must be [{C}, 3] float32 on x's device")
+    if bias is not None:
+        _need(bias, "bias", torch.float32)
+        if tuple(bias.shape) != (C,) or bias.device != x.device:
+            raise ValueError(f"bias must be [{C}] float32 on x's device")
+    for name, t in (("cache_in", cache_in), ("cache_out", cache_out)):
+        if t is not None:
+            _need(t, name, x.dtype)
+            if tuple(t.shape) != (B, P, C) or t.device != x.device:
+                raise ValueError(f"{name} must be [{B}, {P}, {C}] {x.dtype} on x's device")
+    if y is None:
+        y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _need(y, "y")
+    if y.shape != x.shape or y.dtype not in _DTYPE or y.device != x.device:
+        raise ValueError("y must be [B, F, P, C], float32 or bfloat16, on x's device")
+    if cache_out is None and want_cache:
+        cache_out = torch.empty((B, P, C), dtype=x.dtype, device=x.device)
+    return y, cache_out
+
+
+def temporal_conv_chunk(x, weight, bias=None, cache_in=None, y=None, cache_out=None,
+                        out_dtype=None, want_cache=True):
+    """One chunk of the Mix-FFN's depthwise 3x1x1 temporal convolution with
+    its one-frame cache: x [B, F, P, C], weight [C, 3] (taps f-1, f, f+1),
+    bias [C] or None, cache_in [B, P, C] (None: zeros).  Returns
+    (y, cache_out) with cache_out the chunk's last frame; cache_out may be
+    cache_in."""
+    y, cache_out = _prepare_tconv(x, weight, bias, cache_in, y, cache_out, out_dtype, want_cache)
+    B, F, P, C = x.shape
+    _check(lib().la_temporal_conv_chunk(
+        _ptr(x), _ptr(cache_in), _ptr(weight), _ptr(bias), _ptr(y), _ptr(cache_out), B, F, P, C,
+        _DTYPE[x.dtype], _DTYPE[y.dtype], _stream(x.device)), "la_temporal_conv_chunk")
+    return y, cache_out
+
+
+def temporal_conv_blockcausal(x, weight, Tf, bias=None, cache_in=None, y=None, cache_out=None,
+                              out_dtype=None, want_cache=True):
+    """A whole sequence of F frames in chunks of Tf frames: the chunk call
+    over the chunks in order with the cache carried.  Returns
+    (y, cache_out)."""
+    y, cache_out = _prepare_tconv(x, weight, bias, cache_in, y, cache_out, out_dtype, want_cache)
+    B, F, P, C = x.shape
+    _check(lib().la_temporal_conv_blockcausal(
+        _ptr(x), _ptr(cache_in), _ptr(weight), _ptr(bias), _ptr(y), _ptr(cache_out), B, F,
+        int(Tf), P, C, _DTYPE[x.dtype], _DTYPE[y.dtype], _stream(x.device)),
+        "la_temporal_conv_blockcausal")
+    return y, cache_out
 
 
 def plan(B, H, L, d, in_dtype=torch.bfloat16, out_dtype=torch.float32, kv_splits=0,

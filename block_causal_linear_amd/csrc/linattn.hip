@@ -14,10 +14,11 @@
 #include "readout.h"
 #include "state_update.h"
 #include "backward.h"
+#include "temporal_conv.h"
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -507,6 +508,56 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
 #undef LA_RUN_BWD
 }
 
+// ---------------------------------------------------------------------------
+// Temporal convolution: checks, then one launch.  one_chunk: the chunk call
+// (cache_out may be cache_in).
+int temporal_conv(const void* x, const void* cache_in, const float* w, const float* bias, void* y,
+                  void* cache_out, int B, int F, int Tf, int P, int C, int x_dt, int y_dt,
+                  hipStream_t stream) {
+  if (B <= 0 || F < 0 || P <= 0 || C <= 0 || Tf <= 0) return LA_E_INVAL;
+  if (C % 8 != 0) return LA_E_UNSUPPORTED;
+  if ((x_dt != LA_F32 && x_dt != LA_BF16) || (y_dt != LA_F32 && y_dt != LA_BF16))
+    return LA_E_UNSUPPORTED;
+  if (w == nullptr || (F > 0 && (x == nullptr || y == nullptr))) return LA_E_INVAL;
+  const long long nchunks = F == 0 ? 1 : (static_cast<long long>(F) + Tf - 1) / Tf;
+  const long long cols = static_cast<long long>(B) * P * (C / 8);
+  if (nchunks > 65535 || (cols + la::kBlock - 1) / la::kBlock > 0x7FFFFFFFLL) return LA_E_INVAL;
+  const void* ptrs[] = {x, cache_in, w, bias, y, cache_out};
+  for (const void* ptr : ptrs)
+    if (ptr != nullptr && !aligned16(ptr)) return LA_E_ALIGN;
+  const size_t xb = static_cast<size_t>(B) * F * P * C * elem_size(x_dt);
+  const size_t yb = static_cast<size_t>(B) * F * P * C * elem_size(y_dt);
+  const size_t cb = static_cast<size_t>(B) * P * C * elem_size(x_dt);
+  const size_t wb = static_cast<size_t>(C) * 3 * sizeof(float);
+  const size_t bb = static_cast<size_t>(C) * sizeof(float);
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, cache_in, cb) || overlaps(y, yb, cache_out, cb) ||
+      overlaps(y, yb, w, wb) || overlaps(y, yb, bias, bb) || overlaps(cache_out, cb, x, xb) ||
+      overlaps(cache_out, cb, w, wb) || overlaps(cache_out, cb, bias, bb))
+    return LA_E_ALIAS;
+  // the cache may be updated in place only when one thread reads and writes
+  // each element (a single chunk)
+  if (overlaps(cache_out, cb, cache_in, cb) && !(cache_out == cache_in && nchunks == 1))
+    return LA_E_ALIAS;
+
+  const dim3 grid(static_cast<unsigned>((cols + la::kBlock - 1) / la::kBlock),
+                  static_cast<unsigned>(nchunks));
+  const int C8 = C / 8;
+  const bool xb16 = x_dt == LA_BF16, yb16 = y_dt == LA_BF16;
+  if (xb16 && yb16)
+    la::temporal_conv<true, true><<<grid, la::kBlock, 0, stream>>>(x, cache_in, w, bias, y, cache_out,
+                                                                  F, Tf, P, C8, cols);
+  else if (xb16)
+    la::temporal_conv<true, false><<<grid, la::kBlock, 0, stream>>>(x, cache_in, w, bias, y,
+                                                                   cache_out, F, Tf, P, C8, cols);
+  else if (yb16)
+    la::temporal_conv<false, true><<<grid, la::kBlock, 0, stream>>>(x, cache_in, w, bias, y,
+                                                                   cache_out, F, Tf, P, C8, cols);
+  else
+    la::temporal_conv<false, false><<<grid, la::kBlock, 0, stream>>>(x, cache_in, w, bias, y,
+                                                                    cache_out, F, Tf, P, C8, cols);
+  return launched();
+}
+
 // Checks shared by every forward call, then the launches.  `need_state_in`:
 // the chunk call requires it; the global and block-causal calls take NULL as
 // zero.  `states_blocks`: number of states `states` holds per (b, h).
@@ -675,6 +726,19 @@ int la_global_backward(const void* q, const void* k, const void* v, const float*
                        size_t workspace_bytes, hipStream_t stream) {
   return backward(q, k, v, state, dout, nullptr, dq, dk, dv, nullptr, B, H, N, N > 0 ? N : 1, d,
                   in_dt, grad_dt, eps, workspace, workspace_bytes, false, nullptr, stream);
+}
+
+int la_temporal_conv_chunk(const void* x, const void* cache_in, const float* weight,
+                           const float* bias, void* y, void* cache_out, int B, int F, int P, int C,
+                           int x_dt, int y_dt, hipStream_t stream) {
+  return temporal_conv(x, cache_in, weight, bias, y, cache_out, B, F, F > 0 ? F : 1, P, C, x_dt,
+                       y_dt, stream);
+}
+
+int la_temporal_conv_blockcausal(const void* x, const void* cache_in, const float* weight,
+                                 const float* bias, void* y, void* cache_out, int B, int F, int Tf,
+                                 int P, int C, int x_dt, int y_dt, hipStream_t stream) {
+  return temporal_conv(x, cache_in, weight, bias, y, cache_out, B, F, Tf, P, C, x_dt, y_dt, stream);
 }
 
 const char* la_status_string(int status) {

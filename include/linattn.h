@@ -257,6 +257,44 @@ int la_global_backward(const void* q, const void* k, const void* v, const float*
                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Temporal convolution of the Spatial-Temporal Mix-FFN with its
+ * chunk-boundary cache ([TR] section "Verimli doğrusal DiT": the MLP
+ * alternates 1x3x3 spatial and 3x1x1 temporal convolutions; [ZH] section 1:
+ * a temporal convolution module).  The pages do not give its streaming
+ * treatment; this library's reading: the 3x1x1 convolution is depthwise
+ * (one 3-tap filter per channel along latent frames), and it follows the
+ * block-causal attention's visibility rule ([TR]: a block reads earlier
+ * blocks, never later ones), so per batch b, frame f, position p, channel c:
+ *   y[f] = w[c][0] x[f-1] + w[c][1] x[f] + w[c][2] x[f+1] + bias[c]
+ * with x[f+1] = 0 when frame f+1 is in a later chunk or past the end, and
+ * x[-1] = the cache (the previous chunk's last frame; NULL = zeros, the start
+ * of a video).  A stream therefore carries one frame, constant in memory.
+ *   x, y      : [B][F][P][C] (frames, positions per frame, channels),
+ *               x_dt / y_dt each LA_F32 or LA_BF16; C a multiple of 8.
+ *   cache_in  : [B][P][C] x_dt, read; NULL = zeros.
+ *   weight    : [C][3] float32 (taps for f-1, f, f+1); bias: [C] float32 or NULL.
+ *   cache_out : [B][P][C] x_dt, written with the last frame (NULL: not
+ *               wanted); F = 0 copies cache_in (or zeros) into it.
+ * Errors: LA_E_INVAL (B, P, C <= 0, F < 0, Tf <= 0, a needed pointer NULL,
+ * more than 65535 chunks), LA_E_UNSUPPORTED (C not a multiple of 8, dtype),
+ * LA_E_ALIGN, LA_E_ALIAS (y overlapping anything else; cache_out overlapping
+ * x, weight, bias, or cache_in unless it is cache_in itself and the call has
+ * one chunk).
+ */
+
+/* One chunk of F frames.  cache_out may be cache_in (in-place update). */
+int la_temporal_conv_chunk(const void* x, const void* cache_in, const float* weight,
+                           const float* bias, void* y, void* cache_out, int B, int F, int P, int C,
+                           int x_dt, int y_dt, hipStream_t stream);
+
+/* A whole sequence of F frames in chunks of Tf frames (the training form):
+ * equals la_temporal_conv_chunk over the chunks in order with the cache
+ * carried.  With more than one chunk, cache_out must not overlap cache_in. */
+int la_temporal_conv_blockcausal(const void* x, const void* cache_in, const float* weight,
+                                 const float* bias, void* y, void* cache_out, int B, int F, int Tf,
+                                 int P, int C, int x_dt, int y_dt, hipStream_t stream);
+
+/*
  * la_plan - the launch shape a forward call with these arguments (and the
  * given kv_splits / readout_workgroups requests, 0 = library's choice) would
  * use, with no device work: *kv_splits receives the split count (1 = the KV

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 3
+    assert la.abi_version() == 4
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -211,3 +211,32 @@ def test_backward_workspace_size():
     # config-5 shape in one call: 40 blocks x 64 heads, one split each
     E2 = 128 * 128 + 128
     assert la.backward_workspace_size(4, 16, 40 * 4096, 4096, 128) == 4 * 16 * 40 * E2 * 4
+
+
+def tconv(x=A, ci=2 * A, w=3 * A, b=4 * A, y=5 * A, co=6 * A, B=1, F=21, P=36, C=64,
+          xdt=BF16, ydt=BF16, Tf=None):
+    if Tf is None:
+        return la.lib().la_temporal_conv_chunk(x, ci, w, b, y, co, B, F, P, C, xdt, ydt, None)
+    return la.lib().la_temporal_conv_blockcausal(x, ci, w, b, y, co, B, F, Tf, P, C, xdt, ydt,
+                                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), la.LA_E_INVAL),
+    (dict(F=-1), la.LA_E_INVAL),
+    (dict(P=0), la.LA_E_INVAL),
+    (dict(C=12), la.LA_E_UNSUPPORTED),
+    (dict(xdt=4), la.LA_E_UNSUPPORTED),
+    (dict(w=None), la.LA_E_INVAL),
+    (dict(x=None), la.LA_E_INVAL),
+    (dict(Tf=0), la.LA_E_INVAL),
+    (dict(F=70000, Tf=1), la.LA_E_INVAL),          # more chunks than the grid allows
+    (dict(x=A + 2), la.LA_E_ALIGN),
+    (dict(co=6 * A + 8), la.LA_E_ALIGN),
+    (dict(y=A + 1024), la.LA_E_ALIAS),             # y overlaps x
+    (dict(co=A), la.LA_E_ALIAS),                   # cache_out inside x
+    (dict(co=2 * A + 64), la.LA_E_ALIAS),          # partial overlap with cache_in
+    (dict(co=2 * A, Tf=7), la.LA_E_ALIAS),         # in place with three chunks
+])
+def test_temporal_conv_rejects(kw, code):
+    assert tconv(**kw) == code

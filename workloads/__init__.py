@@ -29,6 +29,8 @@ EPS = float(np.float32(1e-6))
 Q_ID, K_ID, V_ID, MASK_ID = 0, 1, 2, 3
 # upstream gradients for the backward tests: dL/dO, dL/d(block states)
 DO_ID, DSTATE_ID = 4, 5
+# temporal-convolution inputs: activations, taps and bias, cache
+TC_X_ID, TC_W_ID, TC_C_ID = 6, 7, 8
 
 
 @dataclass(frozen=True)
@@ -140,3 +142,17 @@ def random_state_grads(seed, B, H, C, d, scale=1e-4):
     dS = (g.standard_normal((C, B, H, d, d)) * scale).astype(np.float32)
     dz = (g.standard_normal((C, B, H, d)) * scale).astype(np.float32)
     return dS, dz
+
+
+def random_tconv(seed, B, F, P, C, dtype="bf16", chunk=0):
+    """Inputs of the Mix-FFN temporal convolution: activations x [B, F, P, C]
+    ~ N(0, 1) rounded to the storage precision (chunk-addressable: chunk n
+    of a stream is its own draw), taps w [C, 3] ~ N(0, 1/3) and bias [C] ~
+    N(0, 0.1^2) in float32, and a cache [B, P, C] ~ N(0, 1) at the storage
+    precision (the last frame of a preceding chunk)."""
+    x = draw(seed, TC_X_ID, chunk, (B, F, P, C), dtype=dtype)
+    g = _rng(seed, TC_W_ID, 0)
+    w = (g.standard_normal((C, 3)) / np.sqrt(3.0)).astype(np.float32)
+    b = (g.standard_normal(C) * 0.1).astype(np.float32)
+    cache = draw(seed, TC_C_ID, 0, (B, 1, P, C), dtype=dtype)[:, 0]
+    return x, w, b, cache
