@@ -34,14 +34,23 @@ constexpr int kKvMinTokensPerFeature = 4;
 // d = 128 where each stages a 64 KB state).
 constexpr int kSweepWorkgroups = 768;
 // At d = 128 a sweep workgroup has eight waves and 144 KB of LDS: one per CU
-// (256 measured best at the long-horizon shape among 128..1024).
+// (256 measured best at the long-horizon shape among 128..1024).  The
+// default build reads out d = 128 with readout_items_bf16 instead (faster at
+// every long-horizon shape measured); building with LA_READOUT_ITEMS_MIN_D
+// above 128 restores the sweep there.
 constexpr int kSweepWorkgroups128 = 256;
 constexpr int kReadoutTargetWorkgroups = 1024;
+// Shortest item of the item readout (d = 128): at the long-horizon chunk
+// (64 heads x 4,096 tokens) items of 1,024 tokens on 256 workgroups measured
+// 49.7 us against 54.1 us for 512-token items on 512 workgroups.
+constexpr int kReadoutItemMinTokens = 1024;
+// Compute units of an MI355X: the persistent grids below are sized to the
+// resident workgroups of one round.
+constexpr int kCUs = 256;
 // Resident workgroups of the two bf16 backward kernels on a 256-CU MI355X:
 // their persistent grids.  Each kernel is compiled for a number of waves
 // per SIMD (its launch bound), which with four-wave workgroups is the
 // number of workgroups per CU.
-constexpr int kCUs = 256;
 int bwd_query_capacity(int d) {
   return kCUs * (d == 128 ? la::bwd_query_min_waves<128>()
                  : d == 64 ? la::bwd_query_min_waves<64>()
@@ -54,6 +63,24 @@ int bwd_key_capacity(int d) {
 }
 // float32 backward kernels: workgroups over contiguous token ranges.
 constexpr int kBwdF32TargetWorkgroups = 512;
+
+long long gcd_ll(long long a, long long b) {
+  while (b != 0) {
+    const long long t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Items per block for a persistent grid of `cap` workgroups over `pairs`
+// (b, h, block) pairs: pairs * S = lcm(pairs, cap), a whole number of
+// rounds of the grid, unless that needs more than about four rounds.
+long long items_per_block(long long pairs, long long cap) {
+  long long s = cap / gcd_ll(pairs, cap);
+  const long long most = (4 * cap + pairs - 1) / pairs;
+  return s < most ? s : most;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -73,7 +100,9 @@ struct Plan {
   int kv_tile;         // tokens per KV tile
   bool direct;         // one block, one split: the KV kernel writes the state
   bool in_place;       // several blocks, one split: partials live in `states`
-  bool sweep;          // readout_sweep_bf16 (bf16 inputs; else readout_f32)
+  bool sweep;          // readout_sweep_bf16 (bf16 inputs, d < LA_READOUT_ITEMS_MIN_D)
+  bool items;          // readout_items_bf16 (bf16 inputs, larger d); else readout_f32
+  int ro_splits;       // readout_items_bf16: items per block
   int readout_tpw;     // readout_f32: tokens per workgroup
   int readout_wgs;     // readout workgroups in the grid
   int units_per_block; // sweep readout: four-tile units per block
@@ -97,7 +126,8 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
   p.kv_tile = in_dt == LA_BF16 ? 64 : 16;
   p.T = T < N ? T : N;
   p.nblk = N == 0 ? 0 : (N + p.T - 1) / p.T;
-  p.sweep = in_dt == LA_BF16;
+  p.sweep = in_dt == LA_BF16 && d < LA_READOUT_ITEMS_MIN_D;
+  p.items = in_dt == LA_BF16 && d >= LA_READOUT_ITEMS_MIN_D;
   if (N == 0) return p;
   const long long bhc = static_cast<long long>(B) * H;
   const long long pairs = bhc * p.nblk;  // (b, h, block) pairs
@@ -128,7 +158,23 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
   p.in_place = p.nblk > 1 && p.splits == 1;
 
   // readout
-  if (p.sweep) {
+  if (p.items) {
+    const long long cap = static_cast<long long>(kCUs) *
+                          (d == 128 ? la::readout_items_min_waves<128>()
+                           : d == 64 ? la::readout_items_min_waves<64>()
+                                     : la::readout_items_min_waves<32>());
+    long long s2 = readout_request > 0 ? (readout_request + pairs - 1) / pairs
+                                       : items_per_block(pairs, cap);
+    // an item builds the state's operands (64 KB at d = 128) before it
+    // streams: keep items at least kReadoutItemMinTokens long
+    const long long by_len = Tb / kReadoutItemMinTokens;
+    if (readout_request <= 0 && s2 > by_len) s2 = by_len;
+    const long long tiles = (Tb + 63) / 64;
+    if (s2 > tiles) s2 = tiles;
+    if (s2 < 1) s2 = 1;
+    p.ro_splits = static_cast<int>(s2);
+    p.readout_wgs = static_cast<int>(pairs * s2 < cap ? pairs * s2 : cap);
+  } else if (p.sweep) {
     const int unit = 4 * 16 * (d == 128 ? 2 : LA_READOUT_ROWS);
     p.units_per_block = (Tb + unit - 1) / unit;
     long long wgs = readout_request > 0 ? readout_request
@@ -178,6 +224,17 @@ int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int
 template <int D>
 int launch_readout(const Plan& p, const void* q, int out_dt, int B, int H, int N,
                    const float* states, void* out, float eps, hipStream_t stream) {
+  if (p.items) {
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const int items = B * H * p.nblk * p.ro_splits;
+    if (out_dt == LA_BF16)
+      la::readout_items_bf16<D, true><<<p.readout_wgs, la::RowTile<D>::NT, 0, stream>>>(
+          qq, states, out, N, p.T, p.nblk, p.ro_splits, items, eps);
+    else
+      la::readout_items_bf16<D, false><<<p.readout_wgs, la::RowTile<D>::NT, 0, stream>>>(
+          qq, states, out, N, p.T, p.nblk, p.ro_splits, items, eps);
+    return launched();
+  }
   if (p.sweep) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const int total = B * H * p.nblk * p.units_per_block;
@@ -266,24 +323,6 @@ struct BwdPlan {
   size_t ws_bytes; // workspace the plan needs
 };
 
-long long gcd_ll(long long a, long long b) {
-  while (b != 0) {
-    const long long t = a % b;
-    a = b;
-    b = t;
-  }
-  return a;
-}
-
-// Items per block for a persistent grid of `cap` workgroups over `pairs`
-// (b, h, block) pairs: pairs * S = lcm(pairs, cap), a whole number of
-// rounds of the grid, unless that needs more than about four rounds.
-long long items_per_block(long long pairs, long long cap) {
-  long long s = cap / gcd_ll(pairs, cap);
-  const long long most = (4 * cap + pairs - 1) / pairs;
-  return s < most ? s : most;
-}
-
 // ws_avail: the caller's workspace size (SIZE_MAX when planning the size).
 BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest, int krequest,
                       size_t ws_avail) {
@@ -368,7 +407,7 @@ int launch_bwd_query(const BwdPlan& p, const void* q, const void* dout, const fl
                      hipStream_t stream) {
   if (in_dt == LA_BF16) {
     const int items = B * H * p.nblk * p.qs;
-    la::bwd_query_bf16<D, GO_BF16><<<p.qgrid, la::BwdShape<D>::NT, 0, stream>>>(
+    la::bwd_query_bf16<D, GO_BF16><<<p.qgrid, la::RowTile<D>::NT, 0, stream>>>(
         static_cast<const uint16_t*>(q), dout, states, dq, N, p.T, p.nblk, p.qs, items, eps, dst);
   } else {
     const dim3 grid(p.nblk * p.qs, H, B);
@@ -386,7 +425,7 @@ int launch_bwd_key(const BwdPlan& p, const void* k, const void* v, const float* 
                    void* dv, int in_dt, int B, int H, int N, hipStream_t stream) {
   if (in_dt == LA_BF16) {
     const int items = B * H * p.nblk * p.ks;
-    la::bwd_key_bf16<D, GO_BF16><<<p.kgrid, la::BwdShape<D>::NT, 0, stream>>>(
+    la::bwd_key_bf16<D, GO_BF16><<<p.kgrid, la::RowTile<D>::NT, 0, stream>>>(
         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), R, dk, dv, N, p.T,
         p.nblk, p.ks, items);
   } else {

@@ -7,6 +7,7 @@
 #pragma once
 
 #include "la_common.h"
+#include "row_tiles.h"
 
 // (Measured at the 720p chunk: plain loads and stores beat the
 // non-temporal forms, and two 16-token row blocks per wave tile beat four.)
@@ -283,6 +284,125 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int s = 0; s < KS; ++s) a[r][s] = an[r][s];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Readout over persistent work items (bf16 queries; used at d = 128, where
+// the sweep's per-unit rebuild of a 66 KB state's operands costs more than
+// it saves).  Block c of (b, h) is cut into S items; a persistent grid
+// takes items blockIdx.x, + gridDim.x, ... (row_item).  Per item the
+// workgroup builds the state's operands once in LDS, "columns of S" as bf16
+// hi/lo pairs and z in every column; each wave then takes 16 tokens of each
+// of the item's tiles as MFMA rows (A = phi(Q), loaded two tiles ahead),
+// and stores o = num / (den + eps) with the row-bounded buffer stores of the
+// backward kernels (rows past the block hold copies of its last row and are
+// dropped by the descriptor), so the loop has no branch.
+#ifndef LA_READOUT_ITEMS_MIN_D
+#define LA_READOUT_ITEMS_MIN_D 128  // smallest d that uses readout_items_bf16
+#endif
+
+// Waves per SIMD the kernel is compiled for; with four waves per workgroup
+// also its resident workgroups per CU (LDS: 72 KB at d = 128, 20 KB at 64).
+template <int D>
+constexpr int readout_items_min_waves() {
+  return D == 128 ? 2 : 4;
+}
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_items_bf16(
+    const uint16_t* __restrict__ q, const float* __restrict__ states, void* __restrict__ out,
+    int N, int TB, int nblk, int S, int items, float eps) {
+  using Sh = RowTile<D>;
+  constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, GRP = Sh::GRP, UPR = Sh::UPR;
+  constexpr int TT = Sh::TT;
+  constexpr int E = D * D + D;
+  constexpr int OE = OUT_BF16 ? 2 : 4;
+  __shared__ uint4 scol[Sh::NF][kWave];   // columns of S, hi/lo
+  __shared__ uint4 zfrag[KS * 2][kWave];  // z in every column, hi/lo
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  const int sig = 4 * (n & 3) + (n >> 2);
+
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const RowItem w = row_item(item, S, nblk, N, TB, TT);
+    const size_t bh = w.pair / nblk;
+    const float* st = states + w.pair * E;
+    const size_t row0 = bh * static_cast<size_t>(N);
+    const uint4* qb = reinterpret_cast<const uint4*>(q + row0 * D);
+    auto tile_base = [&](int j) { return w.c0 + (w.split + j * S) * TT; };
+
+    uint4 qa0[KS], qa1[KS];
+    // rows past the block (and prefetches past the item) load its last row
+    auto gload = [&](int j, uint4 (&qa)[KS]) {
+      const int tc = min(tile_base(j) + 16 * wave + sig, w.c1 - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qa[s] = qb[static_cast<size_t>(tc) * UPR + 4 * s + g];
+    };
+    if (w.mine > 0) {
+      gload(0, qa0);
+      gload(1, qa1);
+    }
+
+    __syncthreads();  // the previous item's LDS readers are done
+    build_col_frags<D>(st, scol, wave, lane);
+    if (wave < KS) {
+      const float* zp = st + D * D + 32 * wave + 8 * g;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) split_bf16x2(zp[j], zp[j + 1], &h[j / 2], &l[j / 2]);
+      zfrag[2 * wave][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+      zfrag[2 * wave + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+    __syncthreads();
+
+    auto tile = [&](int j, uint4 (&qa)[KS]) {
+      // read the operands from LDS where they are used instead of holding
+      // them in registers across the loop
+      asm volatile("" ::: "memory");
+      const int tb = tile_base(j);
+      const rsrc_t ro = tile_rsrc(out, (row0 + tb) * D, OE, max(0, min(TT, w.c1 - tb)) * D * OE);
+      uint4 qp[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qp[s] = relu_bf16x8(qa[s]);
+      gload(j + 2, qa);
+      f32x4 accz = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[NBK];
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        accz = mfma_16x16x32(qp[s], zfrag[2 * s][lane], accz);
+        accz = mfma_16x16x32(qp[s], zfrag[2 * s + 1][lane], accz);
+#pragma unroll
+        for (int nb = 0; nb < NBK; ++nb) {
+          const int f = 2 * (s * NBK + nb);
+          acc[nb] = mfma_16x16x32(qp[s], scol[f][lane], acc[nb]);
+          acc[nb] = mfma_16x16x32(qp[s], scol[f + 1][lane], acc[nb]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float inv = fast_rcp(accz[i] + eps);
+        const int tt = 16 * wave + 4 * i + g;  // row within the tile
+#pragma unroll
+        for (int gr = 0; gr < GRP; ++gr) {
+          float x[W];
+#pragma unroll
+          for (int e = 0; e < W; ++e) x[e] = acc[gr * W + e][i] * inv;
+          store_row_buf<W, OUT_BF16>(ro, (tt * D + 16 * W * gr + W * n) * OE, x);
+        }
+      }
+    };
+    // unconditional pairs: with an odd tile count the last call is a tile
+    // past the block, whose stores all fall outside its descriptor
+    for (int j = 0; j < w.mine; j += 2) {
+      tile(j, qa0);
+      tile(j + 1, qa1);
+    }
   }
 }
 

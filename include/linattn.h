@@ -149,8 +149,11 @@ int la_blockcausal_forward(const void* q, const void* k, const void* v,
  *   readout_workgroups: workgroups of the readout grid; 0 lets the library
  *                   choose.  At d <= 64 with bfloat16 inputs every wave
  *                   sweeps 32-token tiles of all heads, and the request is
- *                   clamped to one wave per tile; otherwise it is rounded to
- *                   whole workgroups per (b, h).  Results do not depend on it.
+ *                   clamped to one wave per tile; at d = 128 with bfloat16
+ *                   inputs the request sets the number of work items (whole
+ *                   items per (b, h, block)) of a persistent grid; with
+ *                   float32 inputs it is rounded to whole workgroups per
+ *                   (b, h).  Results do not depend on it.
  *   stage_events  : NULL, or 4 caller-created events recorded on `stream`
  *                   before the KV reduction, before the split reduce (or the
  *                   prefix over blocks), before the readout, and after the

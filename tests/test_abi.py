@@ -148,9 +148,13 @@ def test_plan_shapes():
     assert la.plan(1, 32, 75600, 64)[1] == 768
     assert la.plan(1, 32, 75600, 64, readout_workgroups=300)[1] == 300
     assert la.plan(1, 1, 100, 64, readout_workgroups=300)[1] == 1
-    # d = 128 sweeps too: 256 eight-wave workgroups; float32 inputs keep
-    # per-head workgroups (512 at d = 128: 8 per head here)
+    # d = 128 reads out over persistent work items of at least 1,024 tokens:
+    # 64 heads x 4 items = 256 workgroups; a request sets the item count (up
+    # to the resident grid of 512); float32 inputs keep per-head workgroups
+    # (512 at d = 128: 8 per head here)
     assert la.plan(4, 16, 4096, 128)[1] == 256
+    assert la.plan(4, 16, 4096, 128, readout_workgroups=2048)[1] == 512
+    assert la.plan(4, 16, 40 * 4096, 128)[1] == 512
     assert la.plan(4, 16, 4096, 128, in_dtype=la.torch.float32)[1] == 4 * 16 * 8
     with pytest.raises(la.LinAttnError):
         la.plan(1, 1, 10, 48)
