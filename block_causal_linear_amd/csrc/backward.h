@@ -70,9 +70,18 @@ __device__ __forceinline__ int bwd_swizzle(int t) {
 // waves per workgroup this is also the number of resident workgroups per CU
 // (LDS permitting: 23 / 53 / 137 KB per workgroup at d = 32 / 64 / 128),
 // which sizes the persistent grid.
+#ifndef LA_BWDQ_WAVES64
+#define LA_BWDQ_WAVES64 2  // query kernel waves per SIMD at d = 64
+#endif
+#ifndef LA_BWDQ_PF64
+#define LA_BWDQ_PF64 2     // query kernel prefetch stages at d = 64
+#endif
+#ifndef LA_BWDQ_DNB64
+#define LA_BWDQ_DNB64 2    // query kernel dnum tile buffers at d = 64
+#endif
 template <int D>
 constexpr int bwd_query_min_waves() {
-  return D == 128 ? 1 : D == 64 ? 2 : 4;
+  return D == 128 ? 1 : D == 64 ? LA_BWDQ_WAVES64 : 4;
 }
 
 template <int D, bool GO_BF16>
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
   constexpr int UNITS = TT * UPR;
   __shared__ uint4 sfrag[Sh::NF][kWave];  // rows of S, hi/lo
   __shared__ uint4 zfrag[KS * 2][kWave];  // z in every column, hi/lo
-  constexpr int DNB = D == 128 ? 1 : 2;   // dnum tile buffers
+  constexpr int DNB = D == 128 ? 1 : D == 64 ? LA_BWDQ_DNB64 : 2;  // dnum tile buffers
   __shared__ uint4 qt[2][UNITS];          // phi(Q) tile, two buffers
   __shared__ uint4 dnh[DNB][UNITS], dnl[DNB][UNITS];
   __shared__ float sdd[2][TT];
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
     // exactly 0 (no contribution to G or g), and their dq stores fall
     // outside the tile's descriptor.  (Zeroing them in registers instead
     // would put a divergent branch, and the waits it brings, in the loop.)
-    constexpr int PF = D == 128 ? 1 : 2;
+    constexpr int PF = D == 128 ? 1 : D == 64 ? LA_BWDQ_PF64 : 2;
     uint4 qa0[KS], qa1[KS];
     DoRow<GO_BF16> da0[KS], da1[KS];
     auto gload = [&](int k, uint4 (&qa)[KS], DoRow<GO_BF16> (&da)[KS]) {
@@ -251,7 +260,8 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
             const float gq = (accw[nb][i] - c * zsh[acc_col<D>(nb, n)]) * rd;
             x[e] = qacc[nb][i] > 0.f ? gq : 0.f;
           }
-          store_row_buf<W, GO_BF16>(rdq, (tt * D + 16 * W * gr + W * n) * GE, x);
+          // non-temporal (see the key kernel's stores)
+          store_row_buf<W, GO_BF16, true>(rdq, (tt * D + 16 * W * gr + W * n) * GE, x);
         }
         if (n == 0) sdd[buf][tt] = -c * rd;
       }
@@ -355,9 +365,15 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
 // MFMAs, and stores both with the readout's 4-token-row store pattern.  No
 // barrier inside an item.
 // (LDS: 8 / 32 / 128 KB per workgroup at d = 32 / 64 / 128)
+#ifndef LA_BWDK_WAVES64
+#define LA_BWDK_WAVES64 4  // key kernel waves per SIMD at d = 64
+#endif
+#ifndef LA_BWDK_PF
+#define LA_BWDK_PF 1       // key kernel prefetch stages
+#endif
 template <int D>
 constexpr int bwd_key_min_waves() {
-  return D == 128 ? 1 : D == 64 ? 4 : 6;
+  return D == 128 ? 1 : D == 64 ? LA_BWDK_WAVES64 : 6;
 }
 
 template <int D, bool GO_BF16>
@@ -387,8 +403,11 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
     const uint4* vb = reinterpret_cast<const uint4*>(v + row0 * D);
     // this wave's 16 tokens of tile j of the item
     auto wave_base = [&](int j) { return w.c0 + (w.split + j * S) * TT + 16 * wave; };
-    uint4 ka[KS], va[KS];
-    auto gload = [&](int j) {
+    // PF register stages of the wave's next tiles; loads past the item read
+    // the block's last row (unused)
+    constexpr int PF = LA_BWDK_PF;
+    uint4 ka0[KS], va0[KS], ka1[KS], va1[KS];
+    auto gload = [&](int j, uint4 (&ka)[KS], uint4 (&va)[KS]) {
       const int tc = min(wave_base(j) + sig, w.c1 - 1);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -396,7 +415,10 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
         va[s] = vb[static_cast<size_t>(tc) * UPR + 4 * s + g];
       }
     };
-    if (w.mine > 0) gload(0);
+    if (w.mine > 0) {
+      gload(0, ka0, va0);
+      if (PF == 2) gload(1, ka1, va1);
+    }
 
     __syncthreads();  // the previous item's LDS readers are done
     build_row_frags<D>(rs, rrow, wave, lane);
@@ -404,7 +426,7 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
     if (tid < D) rsh[tid] = rs[D * D + tid];
     __syncthreads();
 
-    for (int j = 0; j < w.mine; ++j) {
+    auto step = [&](int j, uint4 (&ka)[KS], uint4 (&va)[KS]) {
       // read the operand fragments from LDS where they are used instead of
       // holding all of them in registers across the loop
       asm volatile("" ::: "memory");
@@ -421,7 +443,7 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
         kp[s] = relu_bf16x8(ka[s]);
         vv[s] = va[s];
       }
-      gload(j + 1);  // past the end: the block's last row again, unused
+      gload(j + PF, ka, va);
       f32x4 acck[NBK], accv[NBK];
 #pragma unroll
       for (int nb = 0; nb < NBK; ++nb) {
@@ -454,10 +476,20 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
             xk[e] = kacc[nb][i] > 0.f ? acck[nb][i] + rsh[col + e] : 0.f;
             xv[e] = accv[nb][i];
           }
-          store_row_buf<W, GO_BF16>(rdk, (tt * D + col) * GE, xk);
-          store_row_buf<W, GO_BF16>(rdv, (tt * D + col) * GE, xv);
+          // non-temporal: by itself this kernel measures slower with it at
+          // d = 64 (378 -> 390 us), but its write-back lines otherwise drain
+          // during the next kernel on the stream; per backward call at the
+          // 720p chunk: 726 us with non-temporal stores in both kernels,
+          // 733 us with plain stores here
+          store_row_buf<W, GO_BF16, true>(rdk, (tt * D + col) * GE, xk);
+          store_row_buf<W, GO_BF16, true>(rdv, (tt * D + col) * GE, xv);
         }
       }
+    };
+    // unconditional pairs when PF = 2 (a step past the item stores nothing)
+    for (int j = 0; j < w.mine; j += PF) {
+      step(j, ka0, va0);
+      if constexpr (PF == 2) step(j + 1, ka1, va1);
     }
   }
 }

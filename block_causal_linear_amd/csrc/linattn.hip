@@ -28,11 +28,12 @@ constexpr int kKvTargetWorkgroups = 512;
 // partial (d*d + d floats) stays small next to the K/V bytes it reads.
 constexpr int kKvMinTokensPerFeature = 4;
 // Readout workgroups the planner aims for.  The sweep readout (bf16 inputs)
-// runs three or four waves per SIMD at d <= 64: 768 workgroups of four waves
-// were measured best at the 720p shape.  The float32 readout gives each
+// runs three or four waves per SIMD at d <= 64: with its non-temporal stores
+// 512 workgroups of four waves measured best at the 720p shape (171 us
+// against 172-176 us for 768; 384 and 640 were slower).  The float32 readout gives each
 // workgroup a contiguous token range of one head (1024 workgroups, 512 at
 // d = 128 where each stages a 64 KB state).
-constexpr int kSweepWorkgroups = 768;
+constexpr int kSweepWorkgroups = 512;
 // At d = 128 a sweep workgroup has eight waves and 144 KB of LDS: one per CU
 // (256 measured best at the long-horizon shape among 128..1024).  The
 // default build reads out d = 128 with readout_items_bf16 instead (faster at

@@ -9,10 +9,11 @@
 #include "la_common.h"
 #include "row_tiles.h"
 
-// (Measured at the 720p chunk: plain loads and stores beat the
-// non-temporal forms, and two 16-token row blocks per wave tile beat four.)
+// (Measured at the 720p chunk: non-temporal stores of the output beat plain
+// ones, 171-172 us against 174-176 us per readout; plain loads beat
+// non-temporal ones; two 16-token row blocks per wave tile beat one or four.)
 #ifndef LA_READOUT_STREAM_STORES
-#define LA_READOUT_STREAM_STORES 0
+#define LA_READOUT_STREAM_STORES 1
 #endif
 #ifndef LA_READOUT_STREAM_LOADS
 #define LA_READOUT_STREAM_LOADS 0
@@ -393,7 +394,8 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_ite
           float x[W];
 #pragma unroll
           for (int e = 0; e < W; ++e) x[e] = acc[gr * W + e][i] * inv;
-          store_row_buf<W, OUT_BF16>(ro, (tt * D + 16 * W * gr + W * n) * OE, x);
+          // non-temporal: 52.5 -> 46.4 us per long-horizon chunk readout
+          store_row_buf<W, OUT_BF16, true>(ro, (tt * D + 16 * W * gr + W * n) * OE, x);
         }
       }
     };

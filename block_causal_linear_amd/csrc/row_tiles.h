@@ -141,25 +141,29 @@ __device__ __forceinline__ rsrc_t tile_rsrc(void* base, size_t elem_off, int ele
 }
 
 // W values at byte offset `off` of a tile descriptor (float32 or bfloat16).
-template <int W, bool BF16>
+// NT: the non-temporal cache policy (the kernel never reads the rows back).
+// Judge it by whole calls, not one kernel's time: plain stores leave dirty
+// lines that drain during whatever kernel runs next.
+template <int W, bool BF16, bool NT>
 __device__ __forceinline__ void store_row_buf(rsrc_t r, int off, const float (&x)[W]) {
+  constexpr int AUX = NT ? 2 : 0;  // cache-policy bit 1: nt
   if constexpr (BF16) {
     if constexpr (W == 4) {
       __builtin_amdgcn_raw_buffer_store_b64(
           u32x2{pack2(to_bf16(x[0]), to_bf16(x[1])), pack2(to_bf16(x[2]), to_bf16(x[3]))}, r,
-          off, 0, 0);
+          off, 0, AUX);
     } else {
-      __builtin_amdgcn_raw_buffer_store_b32(pack2(to_bf16(x[0]), to_bf16(x[1])), r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(pack2(to_bf16(x[0]), to_bf16(x[1])), r, off, 0, AUX);
     }
   } else {
     if constexpr (W == 4) {
       __builtin_amdgcn_raw_buffer_store_b128(
           u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
                 __float_as_uint(x[3])},
-          r, off, 0, 0);
+          r, off, 0, AUX);
     } else {
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x[0]), __float_as_uint(x[1])},
-                                            r, off, 0, 0);
+                                            r, off, 0, AUX);
     }
   }
 }

@@ -143,9 +143,9 @@ def test_plan_shapes():
     assert la.plan(1, 1, 100, 64, kv_splits=50)[0] == 1
     assert la.plan(1, 1, 6400, 64, kv_splits=7)[0] == 7
     assert la.plan(1, 1, 0, 64)[0] == 0
-    # readout: the sweep grid (768 workgroups) at 720p; a request is honoured
+    # readout: the sweep grid (512 workgroups) at 720p; a request is honoured
     # up to one workgroup per 128-token unit
-    assert la.plan(1, 32, 75600, 64)[1] == 768
+    assert la.plan(1, 32, 75600, 64)[1] == 512
     assert la.plan(1, 32, 75600, 64, readout_workgroups=300)[1] == 300
     assert la.plan(1, 1, 100, 64, readout_workgroups=300)[1] == 1
     # d = 128 reads out over persistent work items of at least 1,024 tokens:
