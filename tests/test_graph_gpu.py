@@ -1,0 +1,79 @@
+"""HIP graph capture of the library's calls (they launch kernels and nothing
+else: no allocation, no memset, no synchronisation), replayed several
+times with eager work and synchronisations in between; every replay must
+match the eager results bit for bit.  The expected values are the eager
+calls' own results: this checks capture and replay, not numerics (the
+parity tests do that against the oracle)."""
+
+import pytest
+import torch
+
+import workloads
+from helpers import dev
+
+import block_causal_linear_amd as la
+
+pytestmark = pytest.mark.gpu
+EPS = workloads.EPS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_graph_replays_match_eager():
+    B, H, L, d = 1, 4, 3000, 64
+    Q, K, V = workloads.random_qkv(301, B, H, L, d)
+    q, k, v = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    do = dev(workloads.random_grads(302, B, H, L, d), "f32")
+    x, w, b, cache = workloads.random_tconv(303, 1, 5, 40, 64)
+    xt, wt, bt, ct = dev(x, "bf16"), dev(w, "f32"), dev(b, "f32"), dev(cache, "bf16")
+
+    state_in = la.new_state(B, H, d)
+    la.global_forward(q, k, v, state_out=state_in, eps=EPS)
+    out = torch.empty((B, H, L, d), device="cuda")
+    st = torch.empty((B, H, d * d + d), device="cuda")
+    dq, dk, dv = (torch.empty((B, H, L, d), device="cuda") for _ in range(3))
+    dsi = torch.empty_like(st)
+    ws = torch.empty(la.backward_workspace_size(B, H, L, L, d), dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(xt)
+    co = torch.empty_like(ct)
+    fresh = torch.empty_like(st)
+
+    def calls():
+        la.state_reset(fresh)
+        la.chunk_forward(q, k, v, state_in, out=out, state_out=st, eps=EPS)
+        la.chunk_backward(q, k, v, st, do, eps=EPS, dq=dq, dk=dk, dv=dv, dstate_in=dsi,
+                          workspace=ws)
+        la.temporal_conv_chunk(xt, wt, bt, cache_in=ct, y=y, cache_out=co)
+
+    results = [out, st, dq, dk, dv, dsi, y, co, fresh]
+    calls()
+    torch.cuda.synchronize()
+    eager = [r.clone() for r in results]
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for rep in range(4):
+        for r in results:
+            r.fill_(float("nan")) if r.dtype.is_floating_point else r.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, r, e in zip("out st dq dk dv dsi y co fresh".split(), results, eager):
+            assert torch.equal(r, e), (rep, name)
+        # eager work between replays
+        la.chunk_forward(q, k, v, state_in, eps=EPS)
+        torch.cuda.synchronize()
