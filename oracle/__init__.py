@@ -71,6 +71,12 @@ __all__ = [
     "temporal_conv_chunk",
     "temporal_conv_stream",
     "temporal_conv_blockcausal",
+    "rope_axes",
+    "rope_angles",
+    "rope_rotate",
+    "rope_chunk_forward",
+    "rope_prefix_forward",
+    "rope_quadratic_forward",
 ]
 
 
@@ -397,3 +403,120 @@ def temporal_conv_blockcausal(x, w, b, Tf, cache=None):
                 acc = acc + w[:, t + 1] * src
         y[:, f] = acc if b is None else acc + _f64(b)
     return y
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding over the latent token grid.  [ZH] section 1: the
+# Linear DiT adds rotary position encoding (RoPE) for awareness of relative
+# positions in space and time.  The pages say no more, so every step below
+# is a reading:
+# * 3-D RoPE: token i of a sequence whose frames hold grid_h x grid_w tokens
+#   (row-major) sits at frame frame0 + i // (grid_h grid_w), row
+#   (i // grid_w) % grid_h, column i % grid_w.  The head dimension is split
+#   into a temporal, a row and a column group of d_t, d_h, d_w features,
+#   d_h = d_w = 2 floor(d / 6) and d_t = d - d_h - d_w (three even parts as
+#   equal as they can be, the remainder to time).
+# * Features (2m, 2m + 1) form pair m; pairs [0, d_t/2) rotate with the
+#   frame, the next d_h/2 with the row, the last d_w/2 with the column.  Pair
+#   j of a group of size d_a turns by the angle p * theta^(-2 j / d_a) for
+#   the token's position p on that axis; (x, y) -> (x cos - y sin,
+#   x sin + y cos).
+# * Placement: the linear-attention form of RoPE of Su et al., "RoFormer:
+#   Enhanced Transformer with Rotary Position Embedding" (2021, section
+#   3.4.3): the rotation acts on the feature-mapped queries and keys in the
+#   numerator only; the denominator keeps the unrotated phi(q) . phi(k), which
+#   stays positive.  So the state becomes S = sum_j R_j phi(k_j) v_j^T (keys
+#   rotated by their absolute positions) while z = sum_j phi(k_j) is as before,
+#   and o_i = (R_i phi(q_i))^T S / (phi(q_i) . z + eps).  Since R_i^T R_j
+#   depends only on the position difference, the state carries across blocks
+#   as long as every call passes the absolute frame0 of its first token.
+
+
+def rope_axes(d):
+    """(d_t, d_h, d_w): the features given to frame, row and column."""
+    dh = 2 * (d // 6)
+    return d - 2 * dh, dh, dh
+
+
+def rope_angles(n, d, frame0, grid_h, grid_w, theta):
+    """Rotation angles [n, d/2] of the first n tokens of a sequence whose
+    token 0 is at frame frame0 (row 0, column 0)."""
+    i = np.arange(n)
+    hw = grid_h * grid_w
+    pos = (frame0 + i // hw, (i // grid_w) % grid_h, i % grid_w)
+    parts = []
+    for p, da in zip(pos, rope_axes(d)):
+        if da == 0:
+            continue
+        j = np.arange(da // 2, dtype=np.float64)
+        freq = float(theta) ** (-2.0 * j / da)
+        parts.append(np.asarray(p, dtype=np.float64)[:, None] * freq[None, :])
+    return np.concatenate(parts, axis=1)
+
+
+def rope_rotate(X, ang):
+    """Turn feature pair m of token t of X [..., n, d] by ang[t, m]."""
+    X = _f64(X)
+    x, y = X[..., 0::2], X[..., 1::2]
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(X)
+    out[..., 0::2] = x * c - y * s
+    out[..., 1::2] = x * s + y * c
+    return out
+
+
+def rope_chunk_forward(Q, K, V, S_in, z_in, eps, frame0, grid_h, grid_w, theta):
+    """One block with RoPE: S_out = S_in + (R phi(K))^T V, z_out = z_in +
+    phi(K)^T 1, o_i = (R_i phi(q_i))^T S_out / (phi(q_i) . z_out + eps), the
+    block's token 0 at frame frame0.  Returns (O, S_out, z_out)."""
+    fQ, fK, V = phi(Q), phi(K), _f64(V)
+    n, d = fQ.shape[-2], fQ.shape[-1]
+    ang = rope_angles(n, d, frame0, grid_h, grid_w, theta)
+    rK = rope_rotate(fK, ang)
+    S_out = _f64(S_in) + np.matmul(np.swapaxes(rK, -1, -2), V)
+    z_out = _f64(z_in) + fK.sum(axis=-2)
+    num = np.matmul(rope_rotate(fQ, ang), S_out)
+    den = np.matmul(fQ, z_out[..., :, None]) + float(eps)
+    return num / den, S_out, z_out
+
+
+def rope_prefix_forward(Q, K, V, bounds, eps, frame0, grid_h, grid_w, theta, S0=None, z0=None):
+    """The block-causal sequence with RoPE by the prefix route: angles of the
+    whole sequence, every block's rotated KV, an inclusive prefix sum over
+    blocks (plus S0, z0), then every block's queries.  Returns (O, S_prefix,
+    z_prefix) as ``prefix_forward``."""
+    fQ, fK, V = phi(Q), phi(K), _f64(V)
+    B, H, n, d = fQ.shape
+    ang = rope_angles(n, d, frame0, grid_h, grid_w, theta)
+    rQ, rK = rope_rotate(fQ, ang), rope_rotate(fK, ang)
+    C = len(bounds) - 1
+    KVs = [np.matmul(np.swapaxes(rK[:, :, a:b], -1, -2), V[:, :, a:b])
+           for a, b in zip(bounds[:-1], bounds[1:])]
+    ks = [fK[:, :, a:b].sum(axis=-2) for a, b in zip(bounds[:-1], bounds[1:])]
+    S_pre = np.cumsum(np.stack(KVs), axis=0)
+    z_pre = np.cumsum(np.stack(ks), axis=0)
+    if S0 is not None:
+        S_pre = S_pre + _f64(S0)
+        z_pre = z_pre + _f64(z0)
+    O = np.empty((B, H, n, d))
+    for c in range(C):
+        a, b = bounds[c], bounds[c + 1]
+        num = np.matmul(rQ[:, :, a:b], S_pre[c])
+        den = np.matmul(fQ[:, :, a:b], z_pre[c][..., :, None]) + float(eps)
+        O[:, :, a:b] = num / den
+    return O, S_pre, z_pre
+
+
+def rope_quadratic_forward(Q, K, V, block_id, eps, frame0, grid_h, grid_w, theta):
+    """Explicit quadratic form with RoPE (tiny inputs): W_ij = (R_i phi(q_i))
+    . (R_j phi(k_j)) and D_ij = phi(q_i) . phi(k_j), both masked by
+    [block(j) <= block(i)]; o_i = sum_j W_ij v_j / (sum_j D_ij + eps)."""
+    fQ, fK, V = phi(Q), phi(K), _f64(V)
+    n, d = fQ.shape[-2], fQ.shape[-1]
+    ang = rope_angles(n, d, frame0, grid_h, grid_w, theta)
+    rQ, rK = rope_rotate(fQ, ang), rope_rotate(fK, ang)
+    bid = np.asarray(block_id)
+    mask = (bid[None, :] <= bid[:, None]).astype(np.float64)
+    W = np.matmul(rQ, np.swapaxes(rK, -1, -2)) * mask
+    D = np.matmul(fQ, np.swapaxes(fK, -1, -2)) * mask
+    return np.matmul(W, V) / (D.sum(axis=-1, keepdims=True) + float(eps))
