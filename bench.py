@@ -213,7 +213,7 @@ def bench_other(args):
     if onecall:  # stage times cover all C blocks
         kv_b, ro_b = kv_b * C, ro_b * C
     tokens = B * L * C
-    ro_kernel = f"readout_sweep_bf16<{d}>"
+    ro_kernel = f"readout_items_bf16<{d}>" if d == 128 else f"readout_sweep_bf16<{d}>"
     result = {
         "metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -230,6 +230,100 @@ def bench_other(args):
                      "unit": "GB/s", "frac": ro_b / (ro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": None, "bytes_alg_per_launch": ro_b, "launch_us": ro_ms * 1e3},
         "stages_us": {"kv_partial": kv_ms * 1e3, "state_reduce": red_ms * 1e3,
+                      "readout": ro_ms * 1e3, "event_samples": int(stages.shape[0])},
+        "kv_partial_GBs": kv_b / (kv_ms * 1e-3) / 1e9,
+    }
+    print(json.dumps(result), flush=True)
+
+
+ROPE = {
+    "rope_chunk720p": 3,
+    "rope_stream480p_onecall": 4,
+    "rope_longhorizon_onecall": 5,
+}
+
+
+def bench_rope(args):
+    """The rotary-position forward (la_blockcausal_forward_rope).  One step:
+    the 720p chunk read against the state of the chunk before it (one block,
+    frame0 = 21), or a whole stream of blocks in one call."""
+    import torch
+
+    import block_causal_linear_amd as la
+    import workloads
+
+    chunk = args.workload == "rope_chunk720p"
+    w = workloads.CHUNK_720P if chunk else workloads.WORKLOADS[ROPE[args.workload]]
+    gh, gw = workloads.GRIDS[w.cid]
+    B, H, L, d = w.B, w.H, w.L, w.d
+    C = 1 if chunk else w.chunks
+    N = L * C
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev).manual_seed(2000 + w.cid)
+    log(f"drawing inputs on the GPU for rotary {w.name} (B={B} H={H} N={N} d={d} blocks={C}, "
+        f"frames of {gh} x {gw})")
+
+    def draw(n):
+        x = torch.randn((B, H, n, d), generator=gen, device=dev)
+        if w.scale != 1.0:
+            x.mul_(w.scale)
+        if w.outlier_frac > 0:
+            rows = torch.rand((B, H, n, 1), generator=gen, device=dev) < w.outlier_frac
+            x = torch.where(rows, x * w.outlier_scale, x)
+        return x.to(torch.bfloat16)
+
+    sets = [tuple(draw(N) for _ in range(3)) for _ in range(2 if chunk else 1)]
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+    states = torch.empty((B, H, C, d * d + d), dtype=torch.float32, device=dev)
+    state0, f0 = None, 0
+    if chunk:
+        q0, k0, v0 = (draw(N) for _ in range(3))
+        _, st = la.blockcausal_forward_rope(q0, k0, v0, N, 0, gh, gw, workloads.ROPE_THETA,
+                                            eps=workloads.EPS)
+        state0, f0 = st[:, :, 0].contiguous(), workloads.chunk_frame0(w, 1)
+        del q0, k0, v0
+    torch.cuda.synchronize()
+
+    every = max(1, args.event_every)
+    evs = {i: la.StageEvents() for i in range(0, args.steps, every)}
+
+    def step(i, ev=None):
+        q, k, v = sets[i % len(sets)]
+        la.blockcausal_forward_rope(q, k, v, L, f0, gh, gw, workloads.ROPE_THETA,
+                                    state_in=state0, out=out, states=states, eps=workloads.EPS,
+                                    kv_splits=args.kv_splits, stage_events=ev)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i, evs.get(i))
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stages = np.array([e.elapsed_ms() for e in evs.values()])
+    for e in evs.values():
+        e.close()
+    kv_ms, red_ms, ro_ms = (float(x) for x in stages.mean(axis=0))
+    call_b, kv_b, ro_b = bytes_alg(B, H, L, d, with_state_in=chunk)
+    call_b, kv_b, ro_b = call_b * C, kv_b * C, ro_b * C
+    result = {
+        "metric": METRIC, "value": B * N / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rotary " + w.name + ("" if chunk else "-one-call"),
+                   "B": B, "H": H, "d": d, "L": L, "blocks_per_step": C, "grid": [gh, gw],
+                   "theta": workloads.ROPE_THETA, "q_k_v": "bf16", "out": "f32",
+                   "state": "f32"},
+        "hbm_frac": call_b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "us_per_block": ms * 1e3 / C,
+        "roofline": {"bound": "hbm", "kernel": f"readout_rope_bf16<{d}>",
+                     "achieved": ro_b / (ro_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": ro_b / (ro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": None, "bytes_alg_per_launch": ro_b, "launch_us": ro_ms * 1e3},
+        "stages_us": {"kv_partial_rope": kv_ms * 1e3, "state_reduce_or_scan": red_ms * 1e3,
                       "readout": ro_ms * 1e3, "event_samples": int(stages.shape[0])},
         "kv_partial_GBs": kv_b / (kv_ms * 1e-3) / 1e9,
     }
@@ -413,7 +507,7 @@ def main():
     ap.add_argument("--workload", default="chunk720p",
                     choices=["chunk720p", "global480p", "global720p", "stream480p", "longhorizon",
                              "stream480p_onecall", "longhorizon_onecall"] + list(BACKWARD)
-                    + list(TCONV))
+                    + list(TCONV) + list(ROPE))
     ap.add_argument("--event-every", type=int, default=10,
                     help="record per-stage HIP events on every N-th timed step")
     ap.add_argument("--plain-steps", type=int, default=0,
@@ -439,6 +533,9 @@ def main():
         return
     if args.workload in TCONV:
         bench_tconv(args)
+        return
+    if args.workload in ROPE:
+        bench_rope(args)
         return
     if args.workload != "chunk720p":
         bench_other(args)

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 LA_OK, LA_E_INVAL, LA_E_UNSUPPORTED, LA_E_ALIGN, LA_E_ALIAS, LA_E_HIP = range(6)
 LA_F32, LA_BF16 = 0, 1
 DEFAULT_EPS = 1e-6
+DEFAULT_THETA = 10000.0
 
 _DTYPE = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
 
@@ -57,6 +58,12 @@ _SIGNATURES = {
     "la_blockcausal_forward": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P],
     "la_blockcausal_forward_ex": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                   ctypes.POINTER(LaunchOpts), _P],
+    "la_chunk_forward_rope": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F,
+                              _P],
+    "la_blockcausal_forward_rope": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                                    _I, _I, _F, _P],
+    "la_blockcausal_forward_rope_ex": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                       _I, _I, _I, _F, ctypes.POINTER(LaunchOpts), _P],
     "la_backward_workspace_size": [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)],
     "la_blockcausal_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _I, _F, _P, _Z, _P],
@@ -234,14 +241,7 @@ def global_forward(q, k, v, out=None, state_out=None, eps=DEFAULT_EPS,
     return out, state_out
 
 
-def blockcausal_forward(q, k, v, T, state_in=None, out=None, states=None, eps=DEFAULT_EPS,
-                        out_dtype=torch.float32, kv_splits=0, readout_workgroups=0,
-                        stage_events=None):
-    """A whole sequence in the block-causal form: the N tokens of every (b, h)
-    cut into C = ceil(N / T) blocks of T tokens; block n's queries read
-    state_in + KV_1 + ... + KV_n.  Returns (out, states) with states
-    [B, H, C, d*d + d] the state after every block (states[:, :, -1] is the
-    state after the sequence).  state_in None means zeros."""
+def _prepare_blockcausal(q, k, v, T, state_in, out, states, out_dtype):
     _need(q, "q")
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -260,6 +260,19 @@ def blockcausal_forward(q, k, v, T, state_in=None, out=None, states=None, eps=DE
         _need(state_in, "state_in", torch.float32)
         if tuple(state_in.shape) != (B, H, d * d + d) or state_in.device != q.device:
             raise ValueError("state_in must be [B, H, d*d + d] on q's device")
+    return T, out, states
+
+
+def blockcausal_forward(q, k, v, T, state_in=None, out=None, states=None, eps=DEFAULT_EPS,
+                        out_dtype=torch.float32, kv_splits=0, readout_workgroups=0,
+                        stage_events=None):
+    """A whole sequence in the block-causal form: the N tokens of every (b, h)
+    cut into C = ceil(N / T) blocks of T tokens; block n's queries read
+    state_in + KV_1 + ... + KV_n.  Returns (out, states) with states
+    [B, H, C, d*d + d] the state after every block (states[:, :, -1] is the
+    state after the sequence).  state_in None means zeros."""
+    T, out, states = _prepare_blockcausal(q, k, v, T, state_in, out, states, out_dtype)
+    B, H, N, d = q.shape
     o = _opts(kv_splits, readout_workgroups, stage_events)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out), _ptr(states),
             B, H, N, T, d, _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps))
@@ -269,6 +282,47 @@ def blockcausal_forward(q, k, v, T, state_in=None, out=None, states=None, eps=DE
     else:
         rc = L_.la_blockcausal_forward_ex(*args, ctypes.byref(o), _stream(q.device))
     _check(rc, "la_blockcausal_forward")
+    return out, states
+
+
+def chunk_forward_rope(q, k, v, state_in, frame0, grid_h, grid_w, theta=DEFAULT_THETA, out=None,
+                       state_out=None, eps=DEFAULT_EPS, out_dtype=torch.float32):
+    """chunk_forward with rotary position embedding on the numerator: token i
+    of the block sits at frame frame0 + i // (grid_h grid_w), row
+    (i // grid_w) % grid_h, column i % grid_w; the state's S holds keys
+    turned by their absolute positions.  Returns (out, state_out)."""
+    out, state_out = _prepare(q, k, v, out, out_dtype, state_out)
+    _need(state_in, "state_in", torch.float32)
+    if state_in.shape != state_out.shape or state_in.device != q.device:
+        raise ValueError("state_in must match state_out's shape and device")
+    B, H, L, d = q.shape
+    rc = lib().la_chunk_forward_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out), _ptr(state_out), B, H, L, d,
+        _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps), int(frame0), int(grid_h), int(grid_w),
+        float(theta), _stream(q.device))
+    _check(rc, "la_chunk_forward_rope")
+    return out, state_out
+
+
+def blockcausal_forward_rope(q, k, v, T, frame0, grid_h, grid_w, theta=DEFAULT_THETA,
+                             state_in=None, out=None, states=None, eps=DEFAULT_EPS,
+                             out_dtype=torch.float32, kv_splits=0, readout_workgroups=0,
+                             stage_events=None):
+    """blockcausal_forward with rotary position embedding on the numerator
+    (positions as in chunk_forward_rope, counted over the whole sequence).
+    With T >= N it is the global form (state_in None) or one block."""
+    T, out, states = _prepare_blockcausal(q, k, v, T, state_in, out, states, out_dtype)
+    B, H, N, d = q.shape
+    o = _opts(kv_splits, readout_workgroups, stage_events)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(state_in), _ptr(out), _ptr(states),
+            B, H, N, T, d, _DTYPE[q.dtype], _DTYPE[out.dtype], float(eps), int(frame0),
+            int(grid_h), int(grid_w), float(theta))
+    L_ = lib()
+    if o is None:
+        rc = L_.la_blockcausal_forward_rope(*args, _stream(q.device))
+    else:
+        rc = L_.la_blockcausal_forward_rope_ex(*args, ctypes.byref(o), _stream(q.device))
+    _check(rc, "la_blockcausal_forward_rope")
     return out, states
 
 

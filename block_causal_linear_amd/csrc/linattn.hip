@@ -15,10 +15,11 @@
 #include "state_update.h"
 #include "backward.h"
 #include "temporal_conv.h"
+#include "rope.h"
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -62,6 +63,8 @@ int bwd_key_capacity(int d) {
                  : d == 64 ? la::bwd_key_min_waves<64>()
                            : la::bwd_key_min_waves<32>());
 }
+// Rotary calls: sequences (and frame offsets) below this many tokens.
+constexpr int kRopeMaxTokens = 1 << 22;
 // float32 backward kernels: workgroups over contiguous token ranges.
 constexpr int kBwdF32TargetWorkgroups = 512;
 
@@ -121,14 +124,15 @@ int check_shape(int B, int H, int N, int d, int in_dt, int out_dt) {
 }
 
 // N tokens per (b, h) in blocks of T (T >= N: one block).
+// rope: the rotary readout runs on work items at every d.
 Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int request,
-               int readout_request) {
+               int readout_request, bool rope = false) {
   Plan p{};
   p.kv_tile = in_dt == LA_BF16 ? 64 : 16;
   p.T = T < N ? T : N;
   p.nblk = N == 0 ? 0 : (N + p.T - 1) / p.T;
-  p.sweep = in_dt == LA_BF16 && d < LA_READOUT_ITEMS_MIN_D;
-  p.items = in_dt == LA_BF16 && d >= LA_READOUT_ITEMS_MIN_D;
+  p.sweep = in_dt == LA_BF16 && d < LA_READOUT_ITEMS_MIN_D && !rope;
+  p.items = in_dt == LA_BF16 && (d >= LA_READOUT_ITEMS_MIN_D || rope);
   if (N == 0) return p;
   const long long bhc = static_cast<long long>(B) * H;
   const long long pairs = bhc * p.nblk;  // (b, h, block) pairs
@@ -207,10 +211,31 @@ int record(const la_launch_opts* o, int i, hipStream_t stream) {
 
 int launched() { return hipGetLastError() == hipSuccess ? LA_OK : LA_E_HIP; }
 
+template <typename Kern>
+int allow_smem(Kern* kern, size_t smem) {
+  if (smem <= 65536) return LA_OK;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             static_cast<int>(smem)) == hipSuccess
+             ? LA_OK
+             : LA_E_HIP;
+}
+
 template <int D>
 int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int H, int N,
-              const float* state_in, float* dst, hipStream_t stream) {
+              const float* state_in, float* dst, const la::RopeGrid* rope, hipStream_t stream) {
   const dim3 grid(p.nblk * p.splits, H, B);
+  if (rope != nullptr) {
+    if (in_dt == LA_BF16)
+      la::kv_partial_rope_bf16<D><<<grid, la::kv_threads<D>(), 0, stream>>>(
+          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, p.T, p.splits,
+          p.tps, state_in, dst, *rope);
+    else
+      la::kv_partial_rope_f32<D><<<grid, la::kBlock, 0, stream>>>(
+          static_cast<const float*>(k), static_cast<const float*>(v), N, p.T, p.splits, p.tps,
+          state_in, dst, *rope);
+    return launched();
+  }
   if (in_dt == LA_BF16)
     la::kv_partial_bf16<D><<<grid, la::kv_threads<D>(), 0, stream>>>(
         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, p.T, p.splits, p.tps,
@@ -223,8 +248,42 @@ int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int
 }
 
 template <int D>
+int launch_readout_rope(const Plan& p, const void* q, int out_dt, int B, int H, int N,
+                        const float* states, void* out, float eps, const la::RopeGrid& rope,
+                        hipStream_t stream) {
+  if (p.items) {
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const int items = B * H * p.nblk * p.ro_splits;
+    if (out_dt == LA_BF16)
+      la::readout_rope_bf16<D, true><<<p.readout_wgs, la::RowTile<D>::NT, 0, stream>>>(
+          qq, states, out, N, p.T, p.nblk, p.ro_splits, items, eps, rope);
+    else
+      la::readout_rope_bf16<D, false><<<p.readout_wgs, la::RowTile<D>::NT, 0, stream>>>(
+          qq, states, out, N, p.T, p.nblk, p.ro_splits, items, eps, rope);
+    return launched();
+  }
+  const dim3 grid(p.nblk * ((p.T + p.readout_tpw - 1) / p.readout_tpw), H, B);
+  const float* qq = static_cast<const float*>(q);
+  constexpr size_t smem = la::readout_rope_f32_smem<D>();
+  int rc;
+  if (out_dt == LA_BF16) {
+    if ((rc = allow_smem(&la::readout_rope_f32<D, true>, smem)) != LA_OK) return rc;
+    la::readout_rope_f32<D, true><<<grid, la::kBlock, smem, stream>>>(
+        qq, states, out, N, p.T, p.nblk, p.readout_tpw, eps, rope);
+  } else {
+    if ((rc = allow_smem(&la::readout_rope_f32<D, false>, smem)) != LA_OK) return rc;
+    la::readout_rope_f32<D, false><<<grid, la::kBlock, smem, stream>>>(
+        qq, states, out, N, p.T, p.nblk, p.readout_tpw, eps, rope);
+  }
+  return launched();
+}
+
+template <int D>
 int launch_readout(const Plan& p, const void* q, int out_dt, int B, int H, int N,
-                   const float* states, void* out, float eps, hipStream_t stream) {
+                   const float* states, void* out, float eps, const la::RopeGrid* rope,
+                   hipStream_t stream) {
+  if (rope != nullptr)
+    return launch_readout_rope<D>(p, q, out_dt, B, H, N, states, out, eps, *rope, stream);
   if (p.items) {
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const int items = B * H * p.nblk * p.ro_splits;
@@ -275,14 +334,14 @@ int launch_readout(const Plan& p, const void* q, int out_dt, int B, int H, int N
 template <int D>
 int run(const Plan& p, const void* q, const void* k, const void* v, const float* state_in,
         void* out, float* states, int B, int H, int N, int in_dt, int out_dt, float eps,
-        const la_launch_opts* opts, hipStream_t stream) {
+        const la::RopeGrid* rope, const la_launch_opts* opts, hipStream_t stream) {
   constexpr int E = D * D + D;
   const int n4 = E / 4;
   int rc;
   if ((rc = record(opts, 0, stream)) != LA_OK) return rc;
   float* partials = p.direct || p.in_place ? states : static_cast<float*>(out);
   if (p.nblk >= 1) {
-    if ((rc = launch_kv<D>(p, k, v, in_dt, B, H, N, state_in, partials, stream)) != LA_OK)
+    if ((rc = launch_kv<D>(p, k, v, in_dt, B, H, N, state_in, partials, rope, stream)) != LA_OK)
       return rc;
   }
   if ((rc = record(opts, 1, stream)) != LA_OK) return rc;
@@ -302,7 +361,7 @@ int run(const Plan& p, const void* q, const void* k, const void* v, const float*
   }
   if ((rc = record(opts, 2, stream)) != LA_OK) return rc;
   if (N > 0) {
-    if ((rc = launch_readout<D>(p, q, out_dt, B, H, N, states, out, eps, stream)) != LA_OK)
+    if ((rc = launch_readout<D>(p, q, out_dt, B, H, N, states, out, eps, rope, stream)) != LA_OK)
       return rc;
   }
   return record(opts, 3, stream);
@@ -390,16 +449,6 @@ BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest
     p.ks = (Tb + p.ktps - 1) / p.ktps;
   }
   return p;
-}
-
-template <typename Kern>
-int allow_smem(Kern* kern, size_t smem) {
-  if (smem <= 65536) return LA_OK;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(smem)) == hipSuccess
-             ? LA_OK
-             : LA_E_HIP;
 }
 
 template <int D, bool GO_BF16>
@@ -604,10 +653,19 @@ int temporal_conv(const void* x, const void* cache_in, const float* w, const flo
 int forward(const void* q, const void* k, const void* v, const float* state_in,
             bool need_state_in, bool blockcausal, void* out, float* states, int B, int H, int N,
             int T, int d, int in_dt, int out_dt, float eps, const la_launch_opts* opts,
-            hipStream_t stream) {
+            hipStream_t stream, const la::RopeGrid* rope = nullptr) {
   int rc = check_shape(B, H, N, d, in_dt, out_dt);
   if (rc != LA_OK) return rc;
   if (T <= 0) return LA_E_INVAL;
+  if (rope != nullptr) {
+    // token indices (plus a tile of padding) below 2^22, where the kernels'
+    // float divisions are exact, and every frame index exact in float
+    if (rope->gh <= 0 || rope->gw <= 0 || static_cast<long long>(rope->gh) * rope->gw >= kRopeMaxTokens)
+      return LA_E_INVAL;
+    if (N >= kRopeMaxTokens - 64 || rope->frame0 <= -kRopeMaxTokens || rope->frame0 >= kRopeMaxTokens)
+      return LA_E_INVAL;
+    if (!(rope->theta > 0.0f) || !isfinite(rope->theta)) return LA_E_INVAL;
+  }
   if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
   if (states == nullptr || (need_state_in && state_in == nullptr)) return LA_E_INVAL;
   if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr)) return LA_E_INVAL;
@@ -638,15 +696,32 @@ int forward(const void* q, const void* k, const void* v, const float* state_in,
   // a block-causal sequence of no tokens has no blocks and no states
   if (blockcausal && N == 0) return LA_OK;
   const Plan p = make_plan(B, H, N, T, d, in_dt, out_dt, opts ? opts->kv_splits : 0,
-                           opts ? opts->readout_workgroups : 0);
+                           opts ? opts->readout_workgroups : 0, rope != nullptr);
   switch (d) {
     case 32:
-      return run<32>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, opts, stream);
+      return run<32>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, rope, opts,
+                     stream);
     case 64:
-      return run<64>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, opts, stream);
+      return run<64>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, rope, opts,
+                     stream);
     default:
-      return run<128>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, opts, stream);
+      return run<128>(p, q, k, v, state_in, out, states, B, H, N, in_dt, out_dt, eps, rope, opts,
+                      stream);
   }
+}
+
+la::RopeGrid rope_grid(int frame0, int grid_h, int grid_w, float theta) {
+  la::RopeGrid g{};
+  g.frame0 = frame0;
+  g.gh = grid_h;
+  g.gw = grid_w;
+  g.hw = grid_h > 0 && grid_w > 0 && static_cast<long long>(grid_h) * grid_w < kRopeMaxTokens
+             ? grid_h * grid_w
+             : 0;
+  g.rcp_hw = g.hw > 0 ? static_cast<float>(1.0 / g.hw) : 0.0f;
+  g.rcp_gw = grid_w > 0 ? static_cast<float>(1.0 / grid_w) : 0.0f;
+  g.theta = theta;
+  return g;
 }
 
 }  // namespace
@@ -707,6 +782,34 @@ int la_blockcausal_forward_ex(const void* q, const void* k, const void* v, const
                               hipStream_t stream) {
   return forward(q, k, v, state_in, false, true, out, states, B, H, N, T, d, in_dt, out_dt, eps, opts,
                  stream);
+}
+
+int la_chunk_forward_rope(const void* q, const void* k, const void* v, const float* state_in,
+                          void* out, float* state_out, int B, int H, int L, int d, int in_dt,
+                          int out_dt, float eps, int frame0, int grid_h, int grid_w, float theta,
+                          hipStream_t stream) {
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return forward(q, k, v, state_in, true, false, out, state_out, B, H, L, L > 0 ? L : 1, d,
+                 in_dt, out_dt, eps, nullptr, stream, &g);
+}
+
+int la_blockcausal_forward_rope(const void* q, const void* k, const void* v,
+                                const float* state_in, void* out, float* states, int B, int H,
+                                int N, int T, int d, int in_dt, int out_dt, float eps, int frame0,
+                                int grid_h, int grid_w, float theta, hipStream_t stream) {
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return forward(q, k, v, state_in, false, true, out, states, B, H, N, T, d, in_dt, out_dt, eps,
+                 nullptr, stream, &g);
+}
+
+int la_blockcausal_forward_rope_ex(const void* q, const void* k, const void* v,
+                                   const float* state_in, void* out, float* states, int B, int H,
+                                   int N, int T, int d, int in_dt, int out_dt, float eps,
+                                   int frame0, int grid_h, int grid_w, float theta,
+                                   const la_launch_opts* opts, hipStream_t stream) {
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return forward(q, k, v, state_in, false, true, out, states, B, H, N, T, d, in_dt, out_dt, eps,
+                 opts, stream, &g);
 }
 
 int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_request,

@@ -181,6 +181,56 @@ int la_blockcausal_forward_ex(const void* q, const void* k, const void* v,
                               float eps, const la_launch_opts* opts, hipStream_t stream);
 
 /*
+ * Rotary position embedding ([ZH] section 1: the Linear DiT adds rotary
+ * position encoding for relative positions in space and time; the pages say
+ * nothing of where it enters linear attention, so the following is this
+ * library's reading).
+ *   Positions: token i of a (b, h) sequence (for la_chunk_forward_rope, of
+ *   the block) sits at frame frame0 + i / (grid_h * grid_w), row
+ *   (i / grid_w) % grid_h and column i % grid_w: the latent frames of the
+ *   video, each grid_h x grid_w tokens in row-major order.
+ *   Rotation R_i: feature pair m = (2m, 2m + 1) turns by p * theta^(-2j/d_a)
+ *   radians, (x, y) -> (x cos - y sin, x sin + y cos), where the first d_t/2
+ *   pairs use the frame (p = frame, j = m, d_a = d_t), the next d_h/2 the row
+ *   and the last d_w/2 the column; d_h = d_w = 2 * (d / 6) and d_t = d - d_h
+ *   - d_w (d = 64: 24, 20, 20).
+ *   Placement: the linear-attention form of RoPE (Su et al., "RoFormer",
+ *   2021, section 3.4.3), on the numerator only:
+ *     S_out = S_in + sum_j R_j phi(k_j) v_j^T,   z_out = z_in + sum_j phi(k_j),
+ *     o_i = (R_i phi(q_i))^T S_out / (phi(q_i) . z_out + eps).
+ *   The state layout is unchanged; its S holds keys turned by their absolute
+ *   positions, so a stream carries it from block to block when every call
+ *   passes the absolute frame0 of its first token (whole frames per block).
+ *   A state from the plain calls and one from these calls are not
+ *   interchangeable.
+ * Arguments and rules are those of la_chunk_forward / la_blockcausal_forward
+ * plus frame0, grid_h, grid_w and theta (10000 in RoFormer); with T >= N and
+ * state_in NULL, la_blockcausal_forward_rope is the global form.  Extra
+ * errors (LA_E_INVAL): grid_h or grid_w <= 0, grid_h * grid_w >= 2^22,
+ * N >= 2^22 - 64, |frame0| >= 2^22, theta not positive and finite.
+ * bfloat16 inputs take sin and cos from the hardware's v_sin_f32 /
+ * v_cos_f32 (absolute error near 1e-6 at the angles used); float32 inputs
+ * from sincospif.
+ */
+int la_chunk_forward_rope(const void* q, const void* k, const void* v,
+                          const float* state_in, void* out, float* state_out,
+                          int B, int H, int L, int d, int in_dt, int out_dt, float eps,
+                          int frame0, int grid_h, int grid_w, float theta,
+                          hipStream_t stream);
+
+int la_blockcausal_forward_rope(const void* q, const void* k, const void* v,
+                                const float* state_in, void* out, float* states,
+                                int B, int H, int N, int T, int d, int in_dt, int out_dt,
+                                float eps, int frame0, int grid_h, int grid_w, float theta,
+                                hipStream_t stream);
+
+int la_blockcausal_forward_rope_ex(const void* q, const void* k, const void* v,
+                                   const float* state_in, void* out, float* states,
+                                   int B, int H, int N, int T, int d, int in_dt, int out_dt,
+                                   float eps, int frame0, int grid_h, int grid_w, float theta,
+                                   const la_launch_opts* opts, hipStream_t stream);
+
+/*
  * Gradients (training uses the same attention: [EN] abstract; [TR] trains
  * with block-causal attention over the blocks of a video).  For a loss L,
  * given dO = dL/dO and optionally dL/dS_n, dL/dz_n for the state after every

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 4
+    assert la.abi_version() == 5
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -96,6 +96,51 @@ def test_chunk_rejects(kw, code):
 ])
 def test_global_rejects(kw, code):
     assert glob(**kw) == code
+
+
+def rope_chunk(q=A, k=2 * A, v=3 * A, si=4 * A, out=5 * A, so=6 * A, B=1, H=2, L=64, d=64,
+               idt=BF16, odt=F32, eps=1e-6, f0=0, gh=4, gw=4, theta=10000.0):
+    return la.lib().la_chunk_forward_rope(q, k, v, si, out, so, B, H, L, d, idt, odt, eps, f0,
+                                          gh, gw, theta, None)
+
+
+def rope_bc(q=A, k=2 * A, v=3 * A, si=4 * A, out=5 * A, sts=6 * A, B=1, H=2, N=640, T=64, d=64,
+            idt=BF16, odt=F32, eps=1e-6, f0=0, gh=4, gw=4, theta=10000.0):
+    return la.lib().la_blockcausal_forward_rope(q, k, v, si, out, sts, B, H, N, T, d, idt, odt,
+                                                eps, f0, gh, gw, theta, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gh=0), la.LA_E_INVAL),
+    (dict(gw=-2), la.LA_E_INVAL),
+    (dict(gh=4096, gw=1024), la.LA_E_INVAL),        # 2^22 tokens per frame
+    (dict(theta=0.0), la.LA_E_INVAL),
+    (dict(theta=-1.0), la.LA_E_INVAL),
+    (dict(theta=float("nan")), la.LA_E_INVAL),
+    (dict(theta=float("inf")), la.LA_E_INVAL),
+    (dict(f0=1 << 22), la.LA_E_INVAL),
+    (dict(f0=-(1 << 22)), la.LA_E_INVAL),
+    (dict(L=(1 << 22) - 64), la.LA_E_INVAL),
+    (dict(d=48), la.LA_E_UNSUPPORTED),
+    (dict(si=None), la.LA_E_INVAL),
+    (dict(q=A + 8), la.LA_E_ALIGN),
+    (dict(out=A), la.LA_E_ALIAS),
+    (dict(eps=-1.0), la.LA_E_INVAL),
+])
+def test_rope_chunk_rejects(kw, code):
+    assert rope_chunk(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), la.LA_E_INVAL),
+    (dict(gw=0), la.LA_E_INVAL),
+    (dict(theta=float("nan")), la.LA_E_INVAL),
+    (dict(N=1 << 22), la.LA_E_INVAL),
+    (dict(si=6 * A), la.LA_E_ALIAS),
+    (dict(idt=5), la.LA_E_UNSUPPORTED),
+])
+def test_rope_blockcausal_rejects(kw, code):
+    assert rope_bc(**kw) == code
 
 
 def bc(q=A, k=2 * A, v=3 * A, si=4 * A, out=5 * A, sts=6 * A, B=1, H=2, N=640, T=64, d=64,

@@ -65,6 +65,21 @@ WORKLOADS = {
                 outlier_frac=0.01, outlier_scale=8.0),
 }
 
+# Latent token grid (rows, columns) of one frame per workload, for the
+# rotary-position calls: chunk n of a workload starts at frame
+# n * L / (rows * columns).  Config 1 (64 tokens per chunk) is taken as four
+# 4 x 4 frames and config 5 (4,096 tokens) as four 32 x 32 frames; the
+# video workloads use the grids above.
+GRIDS = {1: (4, 4), 2: (30, 52), 3: (45, 80), 4: (30, 52), 5: (32, 32)}
+ROPE_THETA = 10000.0
+
+
+def chunk_frame0(w, chunk):
+    """Frame index of the first token of chunk ``chunk`` of workload ``w``."""
+    gh, gw = GRIDS[w.cid]
+    return chunk * w.L // (gh * gw)
+
+
 # The timed workload: one block-causal chunk at the 720p latent shape, the
 # config-3 distribution, chunk 1 read against the state left by chunk 0.
 CHUNK_720P = Workload(3, "720p-chunk", "chunk", 1, 32, 64, LAT_720, 2, "bf16", scale=0.5)
