@@ -219,11 +219,13 @@ def test_rope_480p_1min_one_call():
         O_ref, S, z = oracle.rope_chunk_forward(Qn, Kn, Vn, S, z, EPS, workloads.chunk_frame0(w, n),
                                                 gh, gw, THETA)
         es = max(state_err(host(states[:, :, n]), S, z))
-        eo = 0.0
         if n in (0, 5, w.chunks - 1):
             eo = out_err(host(out[:, :, n * T:(n + 1) * T]), O_ref)
-        report(f"rope 480p one-call block {n}", out=eo, state=es)
-        worst = max(worst, eo, es)
+            report(f"rope 480p one-call block {n}", out=eo, state=es)
+            worst = max(worst, eo)
+        else:
+            report(f"rope 480p one-call block {n}", state=es)
+        worst = max(worst, es)
     assert worst <= TOL["bf16"], worst
 
 
