@@ -25,6 +25,10 @@ constexpr int kAbiVersion = 5;
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
 // splits x 32 heads), one per compute unit at d = 128 (sixteen waves each).
 constexpr int kKvTargetWorkgroups = 512;
+// The rotary KV kernel (bound by instruction issue, not bandwidth) gains from
+// a third workgroup per CU at d <= 64: 145 us against 155 us at the 720p
+// chunk (24 splits against 16).
+constexpr int kKvRopeTargetWorkgroups = 768;
 // A split should carry at least this many tokens per (d + 1) so that its
 // partial (d*d + d floats) stays small next to the K/V bytes it reads.
 constexpr int kKvMinTokensPerFeature = 4;
@@ -144,7 +148,9 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
   if (request > 0) {
     s = request;
   } else {
-    const long long target = d == 128 ? kKvTargetWorkgroups / 2 : kKvTargetWorkgroups;
+    const long long target = d == 128 ? kKvTargetWorkgroups / 2
+                             : rope    ? kKvRopeTargetWorkgroups
+                                       : kKvTargetWorkgroups;
     s = (target + pairs - 1) / pairs;
     const long long by_size = Tb / (kKvMinTokensPerFeature * (d + 1));
     s = s < by_size ? s : by_size;

@@ -45,14 +45,18 @@ def test_graph_replays_match_eager():
     co = torch.empty_like(ct)
     fresh = torch.empty_like(st)
 
+    out_r = torch.empty_like(out)
+    st_r = torch.empty_like(st)
+
     def calls():
         la.state_reset(fresh)
         la.chunk_forward(q, k, v, state_in, out=out, state_out=st, eps=EPS)
+        la.chunk_forward_rope(q, k, v, state_in, 3, 20, 25, out=out_r, state_out=st_r, eps=EPS)
         la.chunk_backward(q, k, v, st, do, eps=EPS, dq=dq, dk=dk, dv=dv, dstate_in=dsi,
                           workspace=ws)
         la.temporal_conv_chunk(xt, wt, bt, cache_in=ct, y=y, cache_out=co)
 
-    results = [out, st, dq, dk, dv, dsi, y, co, fresh]
+    results = [out, st, dq, dk, dv, dsi, y, co, fresh, out_r, st_r]
     calls()
     torch.cuda.synchronize()
     eager = [r.clone() for r in results]
@@ -72,8 +76,47 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, r, e in zip("out st dq dk dv dsi y co fresh".split(), results, eager):
+        for name, r, e in zip("out st dq dk dv dsi y co fresh out_r st_r".split(), results,
+                              eager):
             assert torch.equal(r, e), (rep, name)
         # eager work between replays
         la.chunk_forward(q, k, v, state_in, eps=EPS)
         torch.cuda.synchronize()
+
+
+def test_concurrent_streams_match_sequential():
+    """Calls on two streams with disjoint buffers may overlap on the GPU; each
+    result equals the same call run alone (bit for bit)."""
+    B, H, L, d = 1, 8, 20000, 64
+    sets = []
+    for seed in (311, 312):
+        Q, K, V = workloads.random_qkv(seed, B, H, L, d)
+        q, k, v = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+        st_in = la.new_state(B, H, d)
+        la.global_forward(q, k, v, state_out=st_in, eps=EPS)
+        sets.append((q, k, v, st_in))
+    torch.cuda.synchronize()
+
+    def run(i, rope):
+        q, k, v, st_in = sets[i]
+        if rope:
+            return la.chunk_forward_rope(q, k, v, st_in, 0, 50, 40, eps=EPS)
+        return la.chunk_forward(q, k, v, st_in, eps=EPS)
+
+    alone = []
+    for i, rope in ((0, False), (1, True)):
+        o, st = run(i, rope)
+        torch.cuda.synchronize()
+        alone.append((o.clone(), st.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        res = [None, None]
+        for i, rope in ((0, False), (1, True)):
+            with torch.cuda.stream(streams[i]):
+                res[i] = run(i, rope)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(res[i][0], alone[i][0]) and torch.equal(res[i][1], alone[i][1]), \
+                (rep, i)
