@@ -39,7 +39,10 @@ METRIC = "latent tokens/sec + % peak HBM BW, block-causal linear attn, 720p chun
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "readout_720p_chunk_traffic.json")
-KERNEL_SOURCES = ["la_common.h", "kv_reduce.h", "state_update.h", "readout.h", "linattn.hip"]
+# What defines the readout kernel's HBM traffic at the 720p chunk: its
+# sources, and the planner constants that set its grid.
+KERNEL_SOURCES = ["la_common.h", "row_tiles.h", "readout.h"]
+PLAN_CONSTANTS = ("kSweepWorkgroups", "LA_READOUT_ROWS", "LA_READOUT_STREAM")
 
 
 def log(msg):
@@ -48,9 +51,14 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_causal_linear_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "block_causal_linear_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    with open(os.path.join(csrc, "linattn.hip"), "rb") as f:
+        for line in f:
+            if any(c.encode() in line for c in PLAN_CONSTANTS):
+                h.update(line)
     return h.hexdigest()[:16]
 
 
