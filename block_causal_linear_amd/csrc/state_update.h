@@ -15,7 +15,8 @@ namespace la {
 // order and adds the result to S_in.  The order is fixed, so repeated runs
 // are bitwise identical.  splits == 0 copies state_in (or writes zeros when
 // state_in is null).  state_in may equal state_out: each element is read
-// before it is written, by the same thread.
+// before it is written, by the same thread.  Wave 0 issues its S_in load
+// with the partial loads, so the kernel waits on memory once, not twice.
 __global__ __launch_bounds__(kBlock) void state_reduce(const float4* __restrict__ partials,
                                                        int splits, int n4,
                                                        const float4* state_in,
@@ -35,6 +36,9 @@ __global__ __launch_bounds__(kBlock) void state_reduce(const float4* __restrict_
     a.z += x.z;
     a.w += x.w;
   };
+  const size_t idx = bh * n4 + e;
+  float4 si = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (j == 0 && e < n4 && state_in != nullptr) si = state_in[idx];
   if (e < n4) {
     const float4* p = partials + bh * static_cast<size_t>(splits) * n4 + e;
     int s = s0;
@@ -57,9 +61,7 @@ __global__ __launch_bounds__(kBlock) void state_reduce(const float4* __restrict_
   add(t, part[1][el]);
   add(t, part[2][el]);
   add(t, part[3][el]);
-  const size_t idx = bh * n4 + e;
   if (state_in != nullptr) {
-    const float4 si = state_in[idx];
     t.x = si.x + t.x;
     t.y = si.y + t.y;
     t.z = si.z + t.z;
