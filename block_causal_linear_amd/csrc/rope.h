@@ -74,6 +74,47 @@ __device__ __forceinline__ RopePos rope_pos(const RopeGrid& g, int tok) {
           static_cast<float>(rem - row * g.gw)};
 }
 
+// A token's grid position carried along a sequence in fixed steps of `step`
+// tokens: the step splits once into whole frames, rows and columns, and each
+// advance adds them with at most one carry per axis (no division).
+struct RopeStep {
+  int f, r, c;
+};
+
+__device__ __forceinline__ RopeStep rope_step(const RopeGrid& g, int step) {
+  const int f = step / g.hw;
+  const int rem = step - f * g.hw;
+  const int r = rem / g.gw;
+  return {f, r, rem - r * g.gw};
+}
+
+struct RopeTrack {
+  int f, r, c;  // frame (frame0 included), row, column
+  __device__ __forceinline__ void init(const RopeGrid& g, int tok) {
+    const int fr = rope_div(tok, g.hw, g.rcp_hw);
+    const int rem = tok - fr * g.hw;
+    r = rope_div(rem, g.gw, g.rcp_gw);
+    c = rem - r * g.gw;
+    f = g.frame0 + fr;
+  }
+  __device__ __forceinline__ void advance(const RopeGrid& g, const RopeStep& s) {
+    c += s.c;
+    r += s.r;
+    f += s.f;
+    if (c >= g.gw) {
+      c -= g.gw;
+      ++r;
+    }
+    if (r >= g.gh) {
+      r -= g.gh;
+      ++f;
+    }
+  }
+  __device__ __forceinline__ RopePos pos() const {
+    return {static_cast<float>(f), static_cast<float>(r), static_cast<float>(c)};
+  }
+};
+
 // The position pair m turns with.
 template <int D>
 __device__ __forceinline__ float rope_axis_pos(const RopePos& p, int m) {
@@ -176,6 +217,11 @@ __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_rope_bf16(
   float2 fq[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) fq[e] = rope_freq<D>(4 * cu + e, rg.theta);
+  // positions of this thread's token rows, tile after tile
+  const RopeStep tstep = rope_step(rg, T::TT);
+  RopeTrack trk[T::CPT];
+#pragma unroll
+  for (int i = 0; i < T::CPT; ++i) trk[i].init(rg, t0 + (tid + T::NT * i) / T::UPR);
   float zacc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) zacc[j] = 0.f;
@@ -203,8 +249,8 @@ __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_rope_bf16(
       }
     }
   };
-  auto lstore = [&](const uint4 (&rk)[T::CPT], const uint4 (&rv)[T::CPT], int buf, int tile) {
-    const int base = t0 + tile * T::TT;
+  // called for tiles 0, 1, 2, ... in order: the trackers advance one tile per call
+  auto lstore = [&](const uint4 (&rk)[T::CPT], const uint4 (&rv)[T::CPT], int buf) {
 #pragma unroll
     for (int i = 0; i < T::CPT; ++i) {
       const int u = tid + T::NT * i;
@@ -215,7 +261,8 @@ __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_rope_bf16(
 #pragma unroll
       for (int j = 0; j < 8; ++j) zacc[j] += f[j];
       // rows past the split are zero and stay zero
-      const RopePos p = rope_pos(rg, base + t);
+      const RopePos p = trk[i].pos();
+      trk[i].advance(rg, tstep);
       uint32_t h[4], l[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -257,12 +304,12 @@ __global__ __launch_bounds__(kv_threads<D>()) void kv_partial_rope_bf16(
   if (ntiles > 0) gload(rk0, rv0, 0);
   if (ntiles > 1) gload(rk1, rv1, 1);
   for (int it = 0; it < ntiles; it += 2) {
-    lstore(rk0, rv0, 0, it);
+    lstore(rk0, rv0, 0);
     __syncthreads();
     if (it + 2 < ntiles) gload(rk0, rv0, it + 2);
     compute(0);
     if (it + 1 < ntiles) {
-      lstore(rk1, rv1, 1, it + 1);
+      lstore(rk1, rv1, 1);
       __syncthreads();
       if (it + 3 < ntiles) gload(rk1, rv1, it + 3);
       compute(1);
@@ -327,6 +374,8 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_rop
   const int sig = 4 * (n & 3) + (n >> 2);
   // read only after the first item's barriers
   if (tid < D / 2) ftab[tid] = rope_freq<D>(tid, rg.theta);
+  // a lane's token moves S tiles per step of an item
+  const RopeStep tstep = rope_step(rg, S * TT);
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const RowItem w = row_item(item, S, nblk, N, TB, TT);
@@ -344,6 +393,10 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_rop
 #pragma unroll
       for (int s = 0; s < KS; ++s) qa[s] = qb[static_cast<size_t>(tc) * UPR + 4 * s + g];
     };
+    // the lane's row position for tiles 0, 1, 2, ... of the item (unclamped:
+    // rows past the block are never stored)
+    RopeTrack trk;
+    trk.init(rg, tile_base(0) + 16 * wave + sig);
     if (w.mine > 0) {
       gload(0, qa0);
       gload(1, qa1);
@@ -365,7 +418,8 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_rop
       asm volatile("" ::: "memory");
       const int tb = tile_base(j);
       const rsrc_t ro = tile_rsrc(out, (row0 + tb) * D, OE, max(0, min(TT, w.c1 - tb)) * D * OE);
-      const RopePos pp = rope_pos(rg, row_token(j));
+      const RopePos pp = trk.pos();
+      trk.advance(rg, tstep);
       uint4 qp[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) qp[s] = relu_bf16x8(qa[s]);
