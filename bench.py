@@ -25,6 +25,7 @@ their inputs are seeded normals drawn on the GPU.
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -49,16 +50,24 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text):
+    """Source text without comments and blank space, so that a comment edit
+    does not count as a kernel change."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_causal_linear_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
-    with open(os.path.join(csrc, "linattn.hip"), "rb") as f:
+        with open(os.path.join(csrc, name)) as f:
+            h.update(_code_only(f.read()).encode())
+    with open(os.path.join(csrc, "linattn.hip")) as f:
         for line in f:
-            if any(c.encode() in line for c in PLAN_CONSTANTS):
-                h.update(line)
+            if any(c in line for c in PLAN_CONSTANTS):
+                h.update(_code_only(line).encode())
     return h.hexdigest()[:16]
 
 

@@ -142,7 +142,7 @@ __device__ __forceinline__ rsrc_t tile_rsrc(void* base, size_t elem_off, int ele
 
 // W values at byte offset `off` of a tile descriptor (float32 or bfloat16).
 // NT: the non-temporal cache policy (the kernel never reads the rows back).
-// Judge it by whole calls, not one kernel's time: plain stores leave dirty
+// Time it by whole calls, not one kernel's time: plain stores leave dirty
 // lines that drain during whatever kernel runs next.
 template <int W, bool BF16, bool NT>
 __device__ __forceinline__ void store_row_buf(rsrc_t r, int off, const float (&x)[W]) {
