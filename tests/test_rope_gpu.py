@@ -100,10 +100,12 @@ def test_rope_global_form(dtype):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
-def test_rope_large_frame_offset():
-    """Tokens millions of frames into a stream: the angle reduction keeps
-    float resolution in turns (bf16 and f32 inputs, frame0 = 4,000,000)."""
-    B, H, L, d, gh, gw, f0 = 1, 2, 700, 64, 5, 7, 4_000_000
+@pytest.mark.parametrize("f0", [4_000_000, -3_000_001])
+def test_rope_large_frame_offset(f0):
+    """Tokens millions of frames into a stream (or before its origin, which
+    the ABI allows): the angle reduction keeps float resolution in turns
+    (bf16 and f32 inputs)."""
+    B, H, L, d, gh, gw = 1, 2, 700, 64, 5, 7
     for dtype in ("bf16", "f32"):
         Q, K, V = workloads.random_qkv(43, B, H, L, d, dtype=dtype)
         S_in, z_in = workloads.random_state(44, B, H, d)
