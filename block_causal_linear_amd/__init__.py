@@ -452,6 +452,47 @@ def global_backward(q, k, v, state, dout, eps=DEFAULT_EPS, dq=None, dk=None, dv=
     return dq, dk, dv
 
 
+class _BlockCausalFunction(torch.autograd.Function):
+    """Autograd glue: the forward is blockcausal_forward, the backward is
+    blockcausal_backward (both library calls); nothing is computed here."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, state_in, T, eps):
+        out, states = blockcausal_forward(q, k, v, T, state_in=state_in, eps=eps)
+        ctx.save_for_backward(q, k, v, states)
+        ctx.T, ctx.eps, ctx.has_state_in = T, eps, state_in is not None
+        ctx.state_dtype = None if state_in is None else state_in.dtype
+        return out, states
+
+    @staticmethod
+    def backward(ctx, dout, dstates):
+        q, k, v, states = ctx.saved_tensors
+        if dout is None:
+            dout = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+        dout = dout.contiguous()
+        if dout.dtype not in _DTYPE:
+            dout = dout.float()
+        if dstates is not None:
+            dstates = dstates.contiguous().float()
+        dq, dk, dv, dsi = blockcausal_backward(q, k, v, states, dout, ctx.T, dstates=dstates,
+                                               want_dstate_in=ctx.has_state_in, eps=ctx.eps)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dsi, None, None
+
+
+def linear_attention(q, k, v, T=None, state_in=None, eps=DEFAULT_EPS):
+    """Differentiable block-causal linear attention (torch autograd).
+
+    q, k, v [B, H, N, d] (float32 or bfloat16, contiguous, on one GPU); the N
+    tokens of every (b, h) are cut into blocks of T tokens (None: one block,
+    the global form).  state_in [B, H, d*d + d] float32 or None.  Returns
+    (out [B, H, N, d] float32, states [B, H, C, d*d + d]); gradients flow to
+    q, k, v and state_in through la_blockcausal_backward, including gradients
+    that reach the returned states."""
+    N = q.shape[2]
+    T = max(int(T if T is not None else N), 1)
+    return _BlockCausalFunction.apply(q, k, v, state_in, T, float(eps))
+
+
 def _prepare_tconv(x, weight, bias, cache_in, y, cache_out, out_dtype, want_cache):
     _need(x, "x")
     if x.dim() != 4 or x.dtype not in _DTYPE:
