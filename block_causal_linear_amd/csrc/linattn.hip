@@ -26,7 +26,7 @@ constexpr int kAbiVersion = 5;
 // splits x 32 heads), one per compute unit at d = 128 (sixteen waves each).
 constexpr int kKvTargetWorkgroups = 512;
 // The rotary KV kernel (bound by instruction issue, not bandwidth) gains from
-// a third workgroup per CU at d <= 64: 145 us against 155 us at the 720p
+// a third workgroup per CU at d <= 64: 134 us against 150 us at the 720p
 // chunk (24 splits against 16).
 constexpr int kKvRopeTargetWorkgroups = 768;
 // A split should carry at least this many tokens per (d + 1) so that its
@@ -35,9 +35,9 @@ constexpr int kKvMinTokensPerFeature = 4;
 // Readout workgroups the planner aims for.  The sweep readout (bf16 inputs)
 // runs three or four waves per SIMD at d <= 64: with its non-temporal stores
 // 512 workgroups of four waves measured best at the 720p shape (171 us
-// against 172-176 us for 768; 384 and 640 were slower).  The float32 readout gives each
-// workgroup a contiguous token range of one head (1024 workgroups, 512 at
-// d = 128 where each stages a 64 KB state).
+// against 172-176 us for 768; 384 and 640 were slower).  The float32 readout
+// gives each workgroup a contiguous token range of one head (1024
+// workgroups, 512 at d = 128 where each stages a 64 KB state).
 constexpr int kSweepWorkgroups = 512;
 // At d = 128 a sweep workgroup has eight waves and 144 KB of LDS: one per CU
 // (256 measured best at the long-horizon shape among 128..1024).  The
