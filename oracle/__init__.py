@@ -77,6 +77,7 @@ __all__ = [
     "rope_chunk_forward",
     "rope_prefix_forward",
     "rope_quadratic_forward",
+    "rope_blockcausal_backward",
 ]
 
 
@@ -520,3 +521,59 @@ def rope_quadratic_forward(Q, K, V, block_id, eps, frame0, grid_h, grid_w, theta
     W = np.matmul(rQ, np.swapaxes(rK, -1, -2)) * mask
     D = np.matmul(fQ, np.swapaxes(fK, -1, -2)) * mask
     return np.matmul(W, V) / (D.sum(axis=-1, keepdims=True) + float(eps))
+
+
+def rope_blockcausal_backward(Q, K, V, bounds, dO, eps, frame0, grid_h, grid_w, theta,
+                              S0=None, z0=None, dS=None, dz=None):
+    """Gradients of the RoPE'd block-causal form (``rope_prefix_forward``),
+    the chain rule through its definition.  With q~ = R phi(q), k~ = R phi(k)
+    (R the token's rotation; its transpose turns by the opposite angles):
+      block n, query i:  dnum_i = do_i / den_i,  dden_i = -(do_i . o_i) / den_i
+        dphi(q_i) = R_i^T (S_n dnum_i) + dden_i z_n,  dq_i = dphi(q_i) * [q_i > 0]
+        dS_n += sum_i q~_i dnum_i^T,  dz_n += sum_i dden_i phi(q_i)
+      suffixes G_m = sum_{n >= m} dS_n (with dL/dS_n), g_m likewise
+      block m, key j:  dphi(k_j) = R_j^T (G_m v_j) + g_m,  dk_j = dphi(k_j) * [k_j > 0]
+        dv_j = G_m^T k~_j
+    Arguments as ``rope_prefix_forward`` plus dO [B,H,T,d] and dS [C,B,H,d,d],
+    dz [C,B,H,d] (None: zero).  Returns (dQ, dK, dV, dS0, dz0)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    B, H, n, d = Q.shape
+    C = len(bounds) - 1
+    fQ, fK = phi(Q), phi(K)
+    ang = rope_angles(n, d, frame0, grid_h, grid_w, theta)
+    rQ, rK = rope_rotate(fQ, ang), rope_rotate(fK, ang)
+    if S0 is None:
+        S0, z0 = zero_state(B, H, d)
+    S, z = _f64(S0), _f64(z0)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(Q)
+    dV = np.zeros_like(Q)
+    GS, Gz = [], []
+    for c in range(C):
+        a, b = bounds[c], bounds[c + 1]
+        S = S + np.matmul(np.swapaxes(rK[:, :, a:b], -1, -2), V[:, :, a:b])
+        z = z + fK[:, :, a:b].sum(axis=-2)
+        den = np.matmul(fQ[:, :, a:b], z[..., :, None]) + float(eps)
+        O = np.matmul(rQ[:, :, a:b], S) / den
+        dnum = dO[:, :, a:b] / den
+        dden = -np.sum(dO[:, :, a:b] * O, axis=-1, keepdims=True) / den
+        drq = np.matmul(dnum, np.swapaxes(S, -1, -2))
+        dfq = rope_rotate(drq, -ang[a:b]) + dden * z[..., None, :]
+        dQ[:, :, a:b] = np.where(Q[:, :, a:b] > 0.0, dfq, 0.0)
+        dSn = np.matmul(np.swapaxes(rQ[:, :, a:b], -1, -2), dnum)
+        dzn = np.matmul(np.swapaxes(fQ[:, :, a:b], -1, -2), dden)[..., 0]
+        if dS is not None:
+            dSn = dSn + _f64(dS[c])
+            dzn = dzn + _f64(dz[c])
+        GS.append(dSn)
+        Gz.append(dzn)
+    RS, Rz = _suffix_sums(GS), _suffix_sums(Gz)
+    for c in range(C):
+        a, b = bounds[c], bounds[c + 1]
+        drk = np.matmul(V[:, :, a:b], np.swapaxes(RS[c], -1, -2))
+        dfk = rope_rotate(drk, -ang[a:b]) + Rz[c][..., None, :]
+        dK[:, :, a:b] = np.where(K[:, :, a:b] > 0.0, dfk, 0.0)
+        dV[:, :, a:b] = np.matmul(rK[:, :, a:b], RS[c])
+    if C == 0:
+        return dQ, dK, dV, np.zeros((B, H, d, d)), np.zeros((B, H, d))
+    return dQ, dK, dV, RS[0], Rz[0]
