@@ -351,6 +351,8 @@ BACKWARD = {
     "bwd_chunk720p": 3,
     "bwd_stream480p_onecall": 4,
     "bwd_longhorizon_onecall": 5,
+    "rope_bwd_chunk720p": 3,
+    "rope_bwd_stream480p_onecall": 4,
 }
 
 
@@ -371,15 +373,18 @@ def bwd_bytes(B, H, N, d, C, s_in=2, s_g=4):
 def bench_backward(args):
     """One step = one backward call over resident inputs and forward states
     (the 720p chunk with gradients on its state, or a whole stream in one
-    la_blockcausal_backward)."""
+    la_blockcausal_backward), plain or rotary (la_blockcausal_backward_rope,
+    the chunk at frame0 = 21 against the rotated state of frames 0..20)."""
     import torch
 
     import block_causal_linear_amd as la
     import workloads
 
-    w = workloads.CHUNK_720P if args.workload == "bwd_chunk720p" else \
-        workloads.WORKLOADS[BACKWARD[args.workload]]
-    chunked = args.workload == "bwd_chunk720p"
+    chunked = args.workload in ("bwd_chunk720p", "rope_bwd_chunk720p")
+    rope = args.workload.startswith("rope_")
+    w = workloads.CHUNK_720P if chunked else workloads.WORKLOADS[BACKWARD[args.workload]]
+    gh, gw = workloads.GRIDS[w.cid]
+    f0 = workloads.chunk_frame0(w, 1) if chunked and rope else 0
     B, H, d = w.B, w.H, w.d
     C = 1 if chunked else w.chunks
     T = w.L
@@ -397,9 +402,17 @@ def bench_backward(args):
     q, k, v = draw(), draw(), draw()
     dout = draw(torch.float32, 1.0)
     state_in = None
-    if chunked:
+    if chunked and rope:
+        _, st = la.blockcausal_forward_rope(draw(), draw(), draw(), N, 0, gh, gw,
+                                            workloads.ROPE_THETA, eps=workloads.EPS)
+        state_in = st[:, :, 0].contiguous()
+    elif chunked:
         _, state_in = la.global_forward(draw(), draw(), draw(), eps=workloads.EPS)
-    _, states = la.blockcausal_forward(q, k, v, T, state_in=state_in, eps=workloads.EPS)
+    if rope:
+        _, states = la.blockcausal_forward_rope(q, k, v, T, f0, gh, gw, workloads.ROPE_THETA,
+                                                state_in=state_in, eps=workloads.EPS)
+    else:
+        _, states = la.blockcausal_forward(q, k, v, T, state_in=state_in, eps=workloads.EPS)
     dstates = torch.randn(states.shape, generator=gen, device=dev).mul_(1e-5) if chunked else None
     dq, dk, dv = (torch.empty((B, H, N, d), dtype=torch.float32, device=dev) for _ in range(3))
     dsi = torch.empty((B, H, d * d + d), dtype=torch.float32, device=dev) if chunked else None
@@ -407,9 +420,16 @@ def bench_backward(args):
     torch.cuda.synchronize()
 
     def step(ev=None):
-        la.blockcausal_backward(q, k, v, states, dout, T, dstates=dstates, eps=workloads.EPS,
-                                dq=dq, dk=dk, dv=dv, dstate_in=dsi, workspace=ws,
-                                kv_splits=args.kv_splits, stage_events=ev)
+        if rope:
+            la.blockcausal_backward_rope(q, k, v, states, dout, T, f0, gh, gw,
+                                         workloads.ROPE_THETA, dstates=dstates,
+                                         eps=workloads.EPS, dq=dq, dk=dk, dv=dv, dstate_in=dsi,
+                                         workspace=ws, kv_splits=args.kv_splits,
+                                         stage_events=ev)
+        else:
+            la.blockcausal_backward(q, k, v, states, dout, T, dstates=dstates, eps=workloads.EPS,
+                                    dq=dq, dk=dk, dv=dv, dstate_in=dsi, workspace=ws,
+                                    kv_splits=args.kv_splits, stage_events=ev)
 
     for _ in range(args.warmup):
         step()
@@ -435,12 +455,15 @@ def bench_backward(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name + (" backward" if chunked else "-one-call backward"),
+        "config": {"workload": ("rotary " if rope else "") + w.name
+                   + (" backward" if chunked else "-one-call backward"),
                    "B": B, "H": H, "d": d, "N": N, "T": T, "blocks": C, "q_k_v": "bf16",
-                   "grads": "f32", "state_grads": chunked},
+                   "grads": "f32", "state_grads": chunked,
+                   **({"frame0": f0, "grid": [gh, gw]} if rope else {})},
         "hbm_frac": call_b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "us_per_block": ms * 1e3 / C,
-        "roofline": {"bound": "hbm", "kernel": f"bwd_key_bf16<{d}>",
+        "roofline": {"bound": "hbm",
+                     "kernel": f"bwd_key_{'rope_' if rope else ''}bf16<{d}>",
                      "achieved": k_b / (k_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": k_b / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": None, "bytes_alg_per_launch": k_b, "launch_us": k_ms * 1e3},

@@ -69,6 +69,11 @@ _SIGNATURES = {
                                 _I, _I, _F, _P, _Z, _P],
     "la_blockcausal_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                    _I, _I, _I, _F, _P, _Z, ctypes.POINTER(LaunchOpts), _P],
+    "la_blockcausal_backward_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                     _I, _I, _F, _P, _Z, _I, _I, _I, _F, _P],
+    "la_blockcausal_backward_rope_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                        _I, _I, _I, _F, _P, _Z, _I, _I, _I, _F,
+                                        ctypes.POINTER(LaunchOpts), _P],
     "la_chunk_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
                           _P, _Z, _P],
     "la_global_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
@@ -411,6 +416,45 @@ def blockcausal_backward(q, k, v, states, dout, T, dstates=None, want_dstate_in=
     return dq, dk, dv, dstate_in
 
 
+def blockcausal_backward_rope(q, k, v, states, dout, T, frame0, grid_h, grid_w,
+                              theta=DEFAULT_THETA, dstates=None, want_dstate_in=False,
+                              eps=DEFAULT_EPS, dq=None, dk=None, dv=None, dstate_in=None,
+                              workspace=None, kv_splits=0, readout_workgroups=0,
+                              stage_events=None):
+    """Gradients of blockcausal_forward_rope(q, k, v, T, frame0, grid_h,
+    grid_w, theta, ...) for the upstream gradient dout (and dstates, the
+    gradient of the returned states, or None).  Returns (dq, dk, dv,
+    dstate_in) as blockcausal_backward; launch options as there."""
+    dq, dk, dv = _prepare_grads(q, k, v, dout, dq, dk, dv)
+    B, H, N, d = q.shape
+    T = int(T)
+    if T < 1:
+        raise ValueError("T must be >= 1")
+    C = -(-N // T) if N > 0 else 0
+    _state_like(states, (B, H, C, d * d + d), "states", q.device)
+    if dstates is not None:
+        _state_like(dstates, (B, H, C, d * d + d), "dstates", q.device)
+    if want_dstate_in and dstate_in is None:
+        dstate_in = torch.empty((B, H, d * d + d), dtype=torch.float32, device=q.device)
+    if dstate_in is not None:
+        _state_like(dstate_in, (B, H, d * d + d), "dstate_in", q.device)
+    need = backward_workspace_size(B, H, N, T, d, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    o = _opts(kv_splits, readout_workgroups, stage_events)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(states), _ptr(dout), _ptr(dstates), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dstate_in), B, H, N, T, d, _DTYPE[q.dtype],
+            _DTYPE[dout.dtype], float(eps), _ptr(workspace), ws_bytes, int(frame0), int(grid_h),
+            int(grid_w), float(theta))
+    L_ = lib()
+    if o is None:
+        rc = L_.la_blockcausal_backward_rope(*args, _stream(q.device))
+    else:
+        rc = L_.la_blockcausal_backward_rope_ex(*args, ctypes.byref(o), _stream(q.device))
+    _check(rc, "la_blockcausal_backward_rope")
+    return dq, dk, dv, dstate_in
+
+
 def chunk_backward(q, k, v, state_out, dout, dstate_out=None, want_dstate_in=True,
                    eps=DEFAULT_EPS, dq=None, dk=None, dv=None, dstate_in=None, workspace=None):
     """Gradients of chunk_forward(q, k, v, state_in) -> (out, state_out) for
@@ -453,15 +497,19 @@ def global_backward(q, k, v, state, dout, eps=DEFAULT_EPS, dq=None, dk=None, dv=
 
 
 class _BlockCausalFunction(torch.autograd.Function):
-    """Autograd glue: the forward is blockcausal_forward, the backward is
-    blockcausal_backward (both library calls); nothing is computed here."""
+    """Autograd glue: the forward is blockcausal_forward (or
+    blockcausal_forward_rope), the backward blockcausal_backward (or
+    blockcausal_backward_rope), all library calls; nothing is computed
+    here."""
 
     @staticmethod
-    def forward(ctx, q, k, v, state_in, T, eps):
-        out, states = blockcausal_forward(q, k, v, T, state_in=state_in, eps=eps)
+    def forward(ctx, q, k, v, state_in, T, eps, rope):
+        if rope is None:
+            out, states = blockcausal_forward(q, k, v, T, state_in=state_in, eps=eps)
+        else:
+            out, states = blockcausal_forward_rope(q, k, v, T, *rope, state_in=state_in, eps=eps)
         ctx.save_for_backward(q, k, v, states)
-        ctx.T, ctx.eps, ctx.has_state_in = T, eps, state_in is not None
-        ctx.state_dtype = None if state_in is None else state_in.dtype
+        ctx.T, ctx.eps, ctx.rope, ctx.has_state_in = T, eps, rope, state_in is not None
         return out, states
 
     @staticmethod
@@ -474,23 +522,38 @@ class _BlockCausalFunction(torch.autograd.Function):
             dout = dout.float()
         if dstates is not None:
             dstates = dstates.contiguous().float()
-        dq, dk, dv, dsi = blockcausal_backward(q, k, v, states, dout, ctx.T, dstates=dstates,
-                                               want_dstate_in=ctx.has_state_in, eps=ctx.eps)
-        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dsi, None, None
+        if ctx.rope is None:
+            dq, dk, dv, dsi = blockcausal_backward(q, k, v, states, dout, ctx.T,
+                                                   dstates=dstates,
+                                                   want_dstate_in=ctx.has_state_in, eps=ctx.eps)
+        else:
+            dq, dk, dv, dsi = blockcausal_backward_rope(q, k, v, states, dout, ctx.T, *ctx.rope,
+                                                        dstates=dstates,
+                                                        want_dstate_in=ctx.has_state_in,
+                                                        eps=ctx.eps)
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dsi, None, None, None
 
 
-def linear_attention(q, k, v, T=None, state_in=None, eps=DEFAULT_EPS):
+def linear_attention(q, k, v, T=None, state_in=None, eps=DEFAULT_EPS, rope=None):
     """Differentiable block-causal linear attention (torch autograd).
 
     q, k, v [B, H, N, d] (float32 or bfloat16, contiguous, on one GPU); the N
     tokens of every (b, h) are cut into blocks of T tokens (None: one block,
-    the global form).  state_in [B, H, d*d + d] float32 or None.  Returns
-    (out [B, H, N, d] float32, states [B, H, C, d*d + d]); gradients flow to
-    q, k, v and state_in through la_blockcausal_backward, including gradients
-    that reach the returned states."""
+    the global form).  state_in [B, H, d*d + d] float32 or None.  rope: None,
+    or (frame0, grid_h, grid_w) or (frame0, grid_h, grid_w, theta) for the
+    rotary form (blockcausal_forward_rope).  Returns (out [B, H, N, d]
+    float32, states [B, H, C, d*d + d]); gradients flow to q, k, v and
+    state_in through la_blockcausal_backward (la_blockcausal_backward_rope),
+    including gradients that reach the returned states."""
     N = q.shape[2]
     T = max(int(T if T is not None else N), 1)
-    return _BlockCausalFunction.apply(q, k, v, state_in, T, float(eps))
+    if rope is not None:
+        rope = tuple(rope)
+        if len(rope) not in (3, 4):
+            raise ValueError("rope must be (frame0, grid_h, grid_w[, theta])")
+        theta = float(rope[3]) if len(rope) == 4 else DEFAULT_THETA
+        rope = (int(rope[0]), int(rope[1]), int(rope[2]), theta)
+    return _BlockCausalFunction.apply(q, k, v, state_in, T, float(eps), rope)
 
 
 def _prepare_tconv(x, weight, bias, cache_in, y, cache_out, out_dtype, want_cache):

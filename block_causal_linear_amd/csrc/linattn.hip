@@ -16,10 +16,11 @@
 #include "backward.h"
 #include "temporal_conv.h"
 #include "rope.h"
+#include "rope_bwd.h"
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -460,7 +461,23 @@ BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest
 template <int D, bool GO_BF16>
 int launch_bwd_query(const BwdPlan& p, const void* q, const void* dout, const float* states,
                      void* dq, int in_dt, int B, int H, int N, float eps, float* dst,
-                     hipStream_t stream) {
+                     const la::RopeGrid* rope, hipStream_t stream) {
+  if (rope != nullptr) {
+    if (in_dt == LA_BF16) {
+      const int items = B * H * p.nblk * p.qs;
+      la::bwd_query_rope_bf16<D, GO_BF16><<<p.qgrid, la::RowTile<D>::NT, 0, stream>>>(
+          static_cast<const uint16_t*>(q), dout, states, dq, N, p.T, p.nblk, p.qs, items, eps,
+          dst, *rope);
+    } else {
+      const dim3 grid(p.nblk * p.qs, H, B);
+      constexpr size_t smem = la::bwd_query_rope_f32_smem<D>();
+      const int rc = allow_smem(&la::bwd_query_rope_f32<D, GO_BF16>, smem);
+      if (rc != LA_OK) return rc;
+      la::bwd_query_rope_f32<D, GO_BF16><<<grid, la::kBlock, smem, stream>>>(
+          static_cast<const float*>(q), dout, states, dq, N, p.T, p.qs, p.qtps, eps, dst, *rope);
+    }
+    return launched();
+  }
   if (in_dt == LA_BF16) {
     const int items = B * H * p.nblk * p.qs;
     la::bwd_query_bf16<D, GO_BF16><<<p.qgrid, la::RowTile<D>::NT, 0, stream>>>(
@@ -478,7 +495,25 @@ int launch_bwd_query(const BwdPlan& p, const void* q, const void* dout, const fl
 
 template <int D, bool GO_BF16>
 int launch_bwd_key(const BwdPlan& p, const void* k, const void* v, const float* R, void* dk,
-                   void* dv, int in_dt, int B, int H, int N, hipStream_t stream) {
+                   void* dv, int in_dt, int B, int H, int N, const la::RopeGrid* rope,
+                   hipStream_t stream) {
+  if (rope != nullptr) {
+    if (in_dt == LA_BF16) {
+      const int items = B * H * p.nblk * p.ks;
+      la::bwd_key_rope_bf16<D, GO_BF16><<<p.kgrid, la::RowTile<D>::NT, 0, stream>>>(
+          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), R, dk, dv, N, p.T,
+          p.nblk, p.ks, items, *rope);
+    } else {
+      const dim3 grid(p.nblk * p.ks, H, B);
+      constexpr size_t smem = la::bwd_key_rope_f32_smem<D>();
+      const int rc = allow_smem(&la::bwd_key_rope_f32<D, GO_BF16>, smem);
+      if (rc != LA_OK) return rc;
+      la::bwd_key_rope_f32<D, GO_BF16><<<grid, la::kBlock, smem, stream>>>(
+          static_cast<const float*>(k), static_cast<const float*>(v), R, dk, dv, N, p.T, p.ks,
+          p.ktps, *rope);
+    }
+    return launched();
+  }
   if (in_dt == LA_BF16) {
     const int items = B * H * p.nblk * p.ks;
     la::bwd_key_bf16<D, GO_BF16><<<p.kgrid, la::RowTile<D>::NT, 0, stream>>>(
@@ -500,7 +535,7 @@ template <int D, bool GO_BF16>
 int run_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const float* states,
             const void* dout, const float* dstates, void* dq, void* dk, void* dv,
             float* dstate_in, int B, int H, int N, int in_dt, float eps, void* workspace,
-            const la_launch_opts* opts, hipStream_t stream) {
+            const la::RopeGrid* rope, const la_launch_opts* opts, hipStream_t stream) {
   constexpr int E = D * D + D;
   const int n4 = E / 4;
   float* R = static_cast<float*>(workspace);
@@ -508,7 +543,7 @@ int run_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const
   int rc;
   if ((rc = record(opts, 0, stream)) != LA_OK) return rc;
   if ((rc = launch_bwd_query<D, GO_BF16>(p, q, dout, states, dq, in_dt, B, H, N, eps, partials,
-                                         stream)) != LA_OK)
+                                         rope, stream)) != LA_OK)
     return rc;
   if ((rc = record(opts, 1, stream)) != LA_OK) return rc;
   const dim3 grid((n4 + la::kBlock - 1) / la::kBlock, H, B);
@@ -518,9 +553,25 @@ int run_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const
       reinterpret_cast<float4*>(dstate_in));
   if ((rc = launched()) != LA_OK) return rc;
   if ((rc = record(opts, 2, stream)) != LA_OK) return rc;
-  if ((rc = launch_bwd_key<D, GO_BF16>(p, k, v, R, dk, dv, in_dt, B, H, N, stream)) != LA_OK)
+  if ((rc = launch_bwd_key<D, GO_BF16>(p, k, v, R, dk, dv, in_dt, B, H, N, rope, stream)) !=
+      LA_OK)
     return rc;
   return record(opts, 3, stream);
+}
+
+// Checks of a rotary call's grid (none for a plain call): token indices (plus
+// a tile of padding) below 2^22, where the kernels' float divisions are
+// exact, and every frame index exact in float.
+int check_rope(const la::RopeGrid* rope, int N) {
+  if (rope == nullptr) return LA_OK;
+  if (rope->gh <= 0 || rope->gw <= 0 ||
+      static_cast<long long>(rope->gh) * rope->gw >= kRopeMaxTokens)
+    return LA_E_INVAL;
+  if (N >= kRopeMaxTokens - 64 || rope->frame0 <= -kRopeMaxTokens ||
+      rope->frame0 >= kRopeMaxTokens)
+    return LA_E_INVAL;
+  if (!(rope->theta > 0.0f) || !isfinite(rope->theta)) return LA_E_INVAL;
+  return LA_OK;
 }
 
 // Checks shared by every backward call, then the launches.  The sequence of
@@ -531,10 +582,11 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
              const float* dstates, void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
              int N, int T, int d, int in_dt, int grad_dt, float eps, void* workspace,
              size_t workspace_bytes, bool empty_block, const la_launch_opts* opts,
-             hipStream_t stream) {
+             hipStream_t stream, const la::RopeGrid* rope = nullptr) {
   int rc = check_shape(B, H, N, d, in_dt, grad_dt);
   if (rc != LA_OK) return rc;
   if (T <= 0) return LA_E_INVAL;
+  if ((rc = check_rope(rope, N)) != LA_OK) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
   if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || states == nullptr ||
                 dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr))
@@ -589,9 +641,9 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
   const bool gb = grad_dt == LA_BF16;
 #define LA_RUN_BWD(DD)                                                                          \
   return gb ? run_bwd<DD, true>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, \
-                                N, in_dt, eps, workspace, opts, stream)                         \
+                                N, in_dt, eps, workspace, rope, opts, stream)                   \
             : run_bwd<DD, false>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H,\
-                                 N, in_dt, eps, workspace, opts, stream)
+                                 N, in_dt, eps, workspace, rope, opts, stream)
   switch (d) {
     case 32:
       LA_RUN_BWD(32);
@@ -663,15 +715,7 @@ int forward(const void* q, const void* k, const void* v, const float* state_in,
   int rc = check_shape(B, H, N, d, in_dt, out_dt);
   if (rc != LA_OK) return rc;
   if (T <= 0) return LA_E_INVAL;
-  if (rope != nullptr) {
-    // token indices (plus a tile of padding) below 2^22, where the kernels'
-    // float divisions are exact, and every frame index exact in float
-    if (rope->gh <= 0 || rope->gw <= 0 || static_cast<long long>(rope->gh) * rope->gw >= kRopeMaxTokens)
-      return LA_E_INVAL;
-    if (N >= kRopeMaxTokens - 64 || rope->frame0 <= -kRopeMaxTokens || rope->frame0 >= kRopeMaxTokens)
-      return LA_E_INVAL;
-    if (!(rope->theta > 0.0f) || !isfinite(rope->theta)) return LA_E_INVAL;
-  }
+  if ((rc = check_rope(rope, N)) != LA_OK) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
   if (states == nullptr || (need_state_in && state_in == nullptr)) return LA_E_INVAL;
   if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr)) return LA_E_INVAL;
@@ -875,6 +919,29 @@ int la_global_backward(const void* q, const void* k, const void* v, const float*
                        size_t workspace_bytes, hipStream_t stream) {
   return backward(q, k, v, state, dout, nullptr, dq, dk, dv, nullptr, B, H, N, N > 0 ? N : 1, d,
                   in_dt, grad_dt, eps, workspace, workspace_bytes, false, nullptr, stream);
+}
+
+int la_blockcausal_backward_rope(const void* q, const void* k, const void* v,
+                                 const float* states, const void* dout, const float* dstates,
+                                 void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
+                                 int N, int T, int d, int in_dt, int grad_dt, float eps,
+                                 void* workspace, size_t workspace_bytes, int frame0, int grid_h,
+                                 int grid_w, float theta, hipStream_t stream) {
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return backward(q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, N, T, d, in_dt,
+                  grad_dt, eps, workspace, workspace_bytes, false, nullptr, stream, &g);
+}
+
+int la_blockcausal_backward_rope_ex(const void* q, const void* k, const void* v,
+                                    const float* states, const void* dout, const float* dstates,
+                                    void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
+                                    int N, int T, int d, int in_dt, int grad_dt, float eps,
+                                    void* workspace, size_t workspace_bytes, int frame0,
+                                    int grid_h, int grid_w, float theta,
+                                    const la_launch_opts* opts, hipStream_t stream) {
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return backward(q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, N, T, d, in_dt,
+                  grad_dt, eps, workspace, workspace_bytes, false, opts, stream, &g);
 }
 
 int la_temporal_conv_chunk(const void* x, const void* cache_in, const float* weight,

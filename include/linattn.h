@@ -310,6 +310,39 @@ int la_global_backward(const void* q, const void* k, const void* v, const float*
                        size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * la_blockcausal_backward_rope - gradients of la_blockcausal_forward_rope
+ * (training with the rotary form; the chain rule of the forward stated with
+ * la_chunk_forward_rope, q~ = R phi(q), k~ = R phi(k), R^T the turn by the
+ * opposite angles):
+ *   u_i  = R_i^T (S_n do_i),  t_i = phi(q_i) . u_i
+ *   dq_i = (u_i - (t_i / den_i) z_n) / den_i * [q_i > 0]
+ *   G_m  = sum over blocks n >= m of ( sum_{i in n} q~_i do_i^T / den_i + dL/dS_n )
+ *   g_m  = sum over blocks n >= m of ( -sum_{i in n} t_i / den_i^2 phi(q_i) + dL/dz_n )
+ *   dk_j = (R_j^T (G_m v_j) + g_m) * [k_j > 0],   dv_j = G_m^T k~_j
+ *   dS_in = G_1, dz_in = g_1
+ * Arguments and rules as la_blockcausal_backward (the same workspace size,
+ * la_backward_workspace_size) plus frame0, grid_h, grid_w, theta and their
+ * checks as la_chunk_forward_rope; `states` is what the rotary forward
+ * returned.
+ */
+int la_blockcausal_backward_rope(const void* q, const void* k, const void* v,
+                                 const float* states, const void* dout, const float* dstates,
+                                 void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
+                                 int N, int T, int d, int in_dt, int grad_dt, float eps,
+                                 void* workspace, size_t workspace_bytes, int frame0, int grid_h,
+                                 int grid_w, float theta, hipStream_t stream);
+
+/* As la_blockcausal_backward_rope, with launch options as
+ * la_blockcausal_backward_ex. */
+int la_blockcausal_backward_rope_ex(const void* q, const void* k, const void* v,
+                                    const float* states, const void* dout, const float* dstates,
+                                    void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
+                                    int N, int T, int d, int in_dt, int grad_dt, float eps,
+                                    void* workspace, size_t workspace_bytes, int frame0,
+                                    int grid_h, int grid_w, float theta,
+                                    const la_launch_opts* opts, hipStream_t stream);
+
+/*
  * Temporal convolution of the Spatial-Temporal Mix-FFN with its
  * chunk-boundary cache ([TR] section "Verimli doğrusal DiT": the MLP
  * alternates 1x3x3 spatial and 3x1x1 temporal convolutions; [ZH] section 1:

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 5
+    assert la.abi_version() == 6
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -236,6 +236,34 @@ def bwd(q=A, k=2 * A, v=3 * A, sts=4 * A, do=5 * A, dsts=None, dq=6 * A, dk=7 * 
 ])
 def test_backward_rejects(kw, code):
     assert bwd(**kw) == code
+
+
+def rope_bwd(q=A, k=2 * A, v=3 * A, sts=4 * A, do=5 * A, dsts=None, dq=6 * A, dk=7 * A,
+             dv=8 * A, dsi=None, B=1, H=2, N=640, T=64, d=64, idt=BF16, gdt=F32, eps=1e-6,
+             ws=9 * A, wsb=1 << 20, f0=0, gh=4, gw=4, theta=10000.0, ex=False):
+    args = (q, k, v, sts, do, dsts, dq, dk, dv, dsi, B, H, N, T, d, idt, gdt, eps, ws, wsb, f0,
+            gh, gw, theta)
+    if ex:
+        return la.lib().la_blockcausal_backward_rope_ex(*args, None, None)
+    return la.lib().la_blockcausal_backward_rope(*args, None)
+
+
+@pytest.mark.parametrize("ex", [False, True])
+@pytest.mark.parametrize("kw,code", [
+    (dict(gh=0), la.LA_E_INVAL),
+    (dict(gw=-1), la.LA_E_INVAL),
+    (dict(theta=0.0), la.LA_E_INVAL),
+    (dict(theta=float("nan")), la.LA_E_INVAL),
+    (dict(f0=1 << 22), la.LA_E_INVAL),
+    (dict(N=1 << 22), la.LA_E_INVAL),
+    (dict(T=0), la.LA_E_INVAL),
+    (dict(d=48), la.LA_E_UNSUPPORTED),
+    (dict(ws=None), la.LA_E_INVAL),
+    (dict(dq=6 * A + 8), la.LA_E_ALIGN),
+    (dict(dk=5 * A + 512), la.LA_E_ALIAS),
+])
+def test_rope_backward_rejects(kw, code, ex):
+    assert rope_bwd(ex=ex, **kw) == code
 
 
 def test_backward_entry_points_reject():

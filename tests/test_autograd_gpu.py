@@ -2,7 +2,8 @@
 its gradients equal the direct backward call's bit for bit, and the fp64
 oracle's chain rule (``oracle.blockcausal_backward``) within the backward
 bounds, for the global and the block-causal form, with and without a state
-input, and with a loss that also reads the returned states."""
+input, and with a loss that also reads the returned states; the same for the
+rotary form against ``oracle.rope_blockcausal_backward``."""
 
 import numpy as np
 import pytest
@@ -81,6 +82,61 @@ def test_autograd_equals_direct_backward_bf16():
     dq, dk, dv, _ = la.blockcausal_backward(qd, kd, vd, st2, dO, T, eps=EPS)
     torch.cuda.synchronize()
     assert q.grad.dtype == torch.bfloat16
+    assert torch.equal(q.grad, dq.to(torch.bfloat16))
+    assert torch.equal(k.grad, dk.to(torch.bfloat16))
+    assert torch.equal(v.grad, dv.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("T,with_state", [(None, False), (100, True)])
+def test_autograd_rope_matches_oracle(T, with_state):
+    """The rotary form through linear_attention(rope=...) against the oracle's
+    rotary chain rule (``oracle.rope_blockcausal_backward``)."""
+    B, H, N, d, f0, gh, gw = 1, 2, 300, 64, 3, 4, 6
+    Q, K, V = workloads.random_qkv(521 + N, B, H, N, d, dtype="f32")
+    dO = workloads.random_grads(522, B, H, N, d)
+    q, k, v = (dev(x, "f32").requires_grad_() for x in (Q, K, V))
+    S0 = z0 = st = None
+    if with_state:
+        S0, z0 = workloads.random_state(523, B, H, d)
+        S0, z0 = S0.astype(np.float64), z0.astype(np.float64)
+        st = torch.from_numpy(state_np(S0, z0)).cuda().requires_grad_()
+    out, states = la.linear_attention(q, k, v, T=T, state_in=st, eps=EPS, rope=(f0, gh, gw))
+    w = torch.from_numpy(np.random.default_rng(8).standard_normal(states.shape[-1]) * 1e-3).float().cuda()
+    loss = (out * dev(dO, "f32")).sum() + (states[:, :, -1] * w).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+
+    Tb = N if T is None else T
+    bounds = list(range(0, N, Tb)) + [N]
+    C = len(bounds) - 1
+    dS = np.zeros((C, B, H, d, d))
+    dz = np.zeros((C, B, H, d))
+    wn = host(w)
+    dS[-1] = np.broadcast_to(wn[: d * d].reshape(d, d), (B, H, d, d))
+    dz[-1] = np.broadcast_to(wn[d * d:], (B, H, d))
+    dQ, dK, dV, dS0, dz0 = oracle.rope_blockcausal_backward(
+        Q, K, V, bounds, dO, EPS, f0, gh, gw, workloads.ROPE_THETA, S0, z0, dS, dz)
+    errs = [_err(host(q.grad), dQ), _err(host(k.grad), dK), _err(host(v.grad), dV)]
+    if with_state:
+        g = host(st.grad)
+        errs += [_err(g[..., : d * d].reshape(dS0.shape), dS0), _err(g[..., d * d:], dz0)]
+    print(f"[parity] autograd rope T={T} state={with_state} "
+          + " ".join(f"{e:.2e}" for e in errs), flush=True)
+    assert max(errs) <= TOL["f32"], errs
+
+
+def test_autograd_rope_equals_direct_backward_bf16():
+    B, H, N, d, T = 1, 4, 2000, 128, 500
+    rope = (2, 5, 8, 2000.0)
+    Q, K, V = workloads.random_qkv(531, B, H, N, d)
+    dO = dev(workloads.random_grads(532, B, H, N, d), "f32")
+    q, k, v = (dev(x, "bf16").requires_grad_() for x in (Q, K, V))
+    out, states = la.linear_attention(q, k, v, T=T, eps=EPS, rope=rope)
+    (out * dO).sum().backward()
+    qd, kd, vd = (dev(x, "bf16") for x in (Q, K, V))
+    _, st2 = la.blockcausal_forward_rope(qd, kd, vd, T, *rope, eps=EPS)
+    dq, dk, dv, _ = la.blockcausal_backward_rope(qd, kd, vd, st2, dO, T, *rope, eps=EPS)
+    torch.cuda.synchronize()
     assert torch.equal(q.grad, dq.to(torch.bfloat16))
     assert torch.equal(k.grad, dk.to(torch.bfloat16))
     assert torch.equal(v.grad, dv.to(torch.bfloat16))

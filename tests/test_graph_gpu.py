@@ -47,6 +47,7 @@ def test_graph_replays_match_eager():
 
     out_r = torch.empty_like(out)
     st_r = torch.empty_like(st)
+    dq_r, dk_r, dv_r = (torch.empty_like(dq) for _ in range(3))
 
     def calls():
         la.state_reset(fresh)
@@ -55,8 +56,10 @@ def test_graph_replays_match_eager():
         la.chunk_backward(q, k, v, st, do, eps=EPS, dq=dq, dk=dk, dv=dv, dstate_in=dsi,
                           workspace=ws)
         la.temporal_conv_chunk(xt, wt, bt, cache_in=ct, y=y, cache_out=co)
+        la.blockcausal_backward_rope(q, k, v, st_r.view(B, H, 1, d * d + d), do, L, 3, 20, 25,
+                                     eps=EPS, dq=dq_r, dk=dk_r, dv=dv_r, workspace=ws)
 
-    results = [out, st, dq, dk, dv, dsi, y, co, fresh, out_r, st_r]
+    results = [out, st, dq, dk, dv, dsi, y, co, fresh, out_r, st_r, dq_r, dk_r, dv_r]
     calls()
     torch.cuda.synchronize()
     eager = [r.clone() for r in results]
@@ -76,8 +79,8 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, r, e in zip("out st dq dk dv dsi y co fresh out_r st_r".split(), results,
-                              eager):
+        names = "out st dq dk dv dsi y co fresh out_r st_r dq_r dk_r dv_r".split()
+        for name, r, e in zip(names, results, eager):
             assert torch.equal(r, e), (rep, name)
         # eager work between replays
         la.chunk_forward(q, k, v, state_in, eps=EPS)

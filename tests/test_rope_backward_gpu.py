@@ -1,0 +1,191 @@
+"""GPU parity of the rotary-position gradients (la_blockcausal_backward_rope,
+through the C ABI) against the fp64 oracle's ``rope_blockcausal_backward``
+on the same seeded inputs.
+
+Error: normwise per (b, h, block) slice, max |got - ref| / max |ref|, the
+largest over slices.  Bounds as for the plain backward: 2e-3 for bfloat16
+inputs, 1e-5 for float32 inputs (float32 gradients), 2^-8 for bfloat16
+gradients.  The backward reads the states the GPU's rotary forward wrote.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from helpers import TOL, dev, host, normwise, report, state_err, state_np
+
+import block_causal_linear_amd as la
+
+pytestmark = pytest.mark.gpu
+EPS = workloads.EPS
+THETA = workloads.ROPE_THETA
+BF16_OUT_TOL = 2.0 ** -8
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def bounds_of(N, T):
+    return list(range(0, N, T)) + [N]
+
+
+def grad_err(got, ref, bounds):
+    return max(normwise(got[:, :, a:b], ref[:, :, a:b], axes=(2, 3))
+               for a, b in zip(bounds[:-1], bounds[1:]))
+
+
+def pack_dstates(dS, dz):
+    """[C, B, H, d, d], [C, B, H, d] -> [B, H, C, d*d + d] float32."""
+    C, B, H, d, _ = dS.shape
+    x = np.concatenate([dS.reshape(C, B, H, d * d), dz], axis=-1)
+    return np.ascontiguousarray(np.transpose(x, (1, 2, 0, 3)), dtype=np.float32)
+
+
+def gpu_backward(Q, K, V, dO, T, dtype, f0, gh, gw, gdt="f32", state_in=None, dstates=None,
+                 want_dstate_in=False, theta=THETA):
+    q, k, v = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    st_in = None if state_in is None else torch.from_numpy(state_in).cuda()
+    _, states = la.blockcausal_forward_rope(q, k, v, T, f0, gh, gw, theta, state_in=st_in,
+                                            eps=EPS)
+    ds = None if dstates is None else torch.from_numpy(dstates).cuda()
+    dq, dk, dv, dsi = la.blockcausal_backward_rope(q, k, v, states, dev(dO, gdt), T, f0, gh, gw,
+                                                   theta, dstates=ds,
+                                                   want_dstate_in=want_dstate_in, eps=EPS)
+    torch.cuda.synchronize()
+    return host(dq), host(dk), host(dv), None if dsi is None else host(dsi)
+
+
+def check(name, got, ref, bounds, tol, dsi=None, dsi_ref=None):
+    vals = dict(zip(("dq", "dk", "dv"), (grad_err(g, r, bounds) for g, r in zip(got, ref))))
+    if dsi is not None:
+        es, ez = state_err(dsi, dsi_ref[0], dsi_ref[1])
+        vals.update(dS_in=es, dz_in=ez)
+    report(name, **vals)
+    assert max(vals.values()) <= tol, vals
+
+
+# ---------------------------------------------------------------------------
+# small shapes: several tiles, ragged tails, frames that do not divide the
+# block, one-token blocks, a state input and gradients on every block's state
+
+CASES = [(1000, 64, 4, 4, 0), (2085, 500, 5, 10, 3), (777, 7, 1, 7, 11), (1300, 256, 8, 8, 0),
+         (300, 1, 1, 1, 2), (100, 33, 2, 3, 5)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("N,T,gh,gw,f0", CASES)
+def test_rope_backward_small(dtype, d, N, T, gh, gw, f0):
+    B, H = 2, 3
+    Q, K, V = workloads.random_qkv(5000 + N + d, B, H, N, d, dtype=dtype)
+    dO = workloads.random_grads(5100 + N + d, B, H, N, d)
+    S0, z0 = workloads.random_state(N + T + d, B, H, d)
+    bounds = bounds_of(N, T)
+    C = len(bounds) - 1
+    dS, dz = workloads.random_state_grads(N + 5 * d, B, H, C, d)
+    got = gpu_backward(Q, K, V, dO, T, dtype, f0, gh, gw, state_in=state_np(S0, z0),
+                       dstates=pack_dstates(dS, dz), want_dstate_in=True)
+    ref = oracle.rope_blockcausal_backward(Q, K, V, bounds, dO, EPS, f0, gh, gw, THETA,
+                                           S0.astype(np.float64), z0.astype(np.float64),
+                                           dS.astype(np.float64), dz.astype(np.float64))
+    check(f"rope backward {dtype} d={d} N={N} T={T} grid={gh}x{gw} f0={f0}", got[:3], ref[:3],
+          bounds, TOL[dtype], got[3], ref[3:])
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_rope_backward_bf16_gradients(d):
+    """bfloat16 dO in, bfloat16 dq/dk/dv out."""
+    B, H, N, T, gh, gw = 1, 2, 1300, 300, 6, 9
+    Q, K, V = workloads.random_qkv(51 + d, B, H, N, d)
+    dO = workloads.random_grads(52 + d, B, H, N, d, dtype="bf16")
+    got = gpu_backward(Q, K, V, dO, T, "bf16", 4, gh, gw, gdt="bf16")
+    ref = oracle.rope_blockcausal_backward(Q, K, V, bounds_of(N, T), dO, EPS, 4, gh, gw, THETA)
+    check(f"rope backward bf16 grads d={d}", got[:3], ref[:3], bounds_of(N, T), BF16_OUT_TOL)
+
+
+@pytest.mark.parametrize("f0", [4_000_000, -3_000_001])
+def test_rope_backward_large_frame_offset(f0):
+    """Frame indices in the millions (and negative): the angles are reduced
+    to turns in two parts, so the gradients keep their accuracy."""
+    B, H, N, T, d, gh, gw = 1, 2, 1500, 400, 64, 3, 7
+    Q, K, V = workloads.random_qkv(61, B, H, N, d)
+    dO = workloads.random_grads(62, B, H, N, d)
+    S0, z0 = workloads.random_state(63, B, H, d)
+    C = len(bounds_of(N, T)) - 1
+    dS, dz = workloads.random_state_grads(64, B, H, C, d)
+    got = gpu_backward(Q, K, V, dO, T, "bf16", f0, gh, gw, state_in=state_np(S0, z0),
+                       dstates=pack_dstates(dS, dz), want_dstate_in=True)
+    ref = oracle.rope_blockcausal_backward(Q, K, V, bounds_of(N, T), dO, EPS, f0, gh, gw, THETA,
+                                           S0.astype(np.float64), z0.astype(np.float64),
+                                           dS.astype(np.float64), dz.astype(np.float64))
+    check(f"rope backward f0={f0}", got[:3], ref[:3], bounds_of(N, T), TOL["bf16"], got[3],
+          ref[3:])
+
+
+def test_rope_backward_theta_and_one_frame_blocks():
+    """Another base (theta = 500) and blocks of exactly one frame."""
+    B, H, d, gh, gw = 1, 3, 64, 4, 5
+    T, N = gh * gw, 7 * gh * gw
+    Q, K, V = workloads.random_qkv(71, B, H, N, d)
+    dO = workloads.random_grads(72, B, H, N, d)
+    got = gpu_backward(Q, K, V, dO, T, "bf16", 1, gh, gw, theta=500.0)
+    ref = oracle.rope_blockcausal_backward(Q, K, V, bounds_of(N, T), dO, EPS, 1, gh, gw, 500.0)
+    check("rope backward theta=500", got[:3], ref[:3], bounds_of(N, T), TOL["bf16"])
+
+
+def test_rope_backward_reproducible():
+    """The same launch twice gives identical bits."""
+    B, H, N, T, d = 1, 2, 20000, 20000, 64
+    Q, K, V = workloads.random_qkv(81, B, H, N, d)
+    dO = workloads.random_grads(82, B, H, N, d)
+    a = gpu_backward(Q, K, V, dO, T, "bf16", 0, 30, 52, want_dstate_in=True)
+    b = gpu_backward(Q, K, V, dO, T, "bf16", 0, 30, 52, want_dstate_in=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_rope_backward_empty():
+    """N = 0: no blocks, nothing to write; the call succeeds."""
+    e = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    states = torch.empty((1, 2, 0, 64 * 64 + 64), dtype=torch.float32, device="cuda")
+    dq, dk, dv, _ = la.blockcausal_backward_rope(e, e, e, states, e.float(), 16, 0, 4, 4, THETA,
+                                                 eps=EPS)
+    torch.cuda.synchronize()
+    assert dq.shape == e.shape and dk.shape == e.shape and dv.shape == e.shape
+
+
+# ---------------------------------------------------------------------------
+# full size
+
+
+def test_rope_backward_720p_chunk():
+    """Chunk 1 of a 720p latent (B=1, H=32, d=64, 75,600 tokens, frames
+    21..41 of 45 x 80 tokens) against the rotated state left by chunk 0, with
+    a gradient on state_out: every element."""
+    w = workloads.CHUNK_720P
+    gh, gw = workloads.GRIDS[w.cid]
+    Q0, K0, V0 = workloads.chunk_qkv(w, 0)
+    S0, z0 = oracle.zero_state(w.B, w.H, w.d)
+    _, S0, z0 = oracle.rope_chunk_forward(Q0, K0, V0, S0, z0, EPS, 0, gh, gw, THETA)
+    del Q0, K0, V0
+    st0 = state_np(S0, z0)  # the float32 state the GPU receives
+    d = w.d
+    S0 = st0[..., : d * d].reshape(S0.shape).astype(np.float64)
+    z0 = st0[..., d * d:].astype(np.float64)
+    Q, K, V = workloads.chunk_qkv(w, 1)
+    f1 = workloads.chunk_frame0(w, 1)
+    dO = workloads.random_grads(3, w.B, w.H, w.L, w.d, chunk=1)
+    dS, dz = workloads.random_state_grads(3, w.B, w.H, 1, w.d, scale=1e-5)
+    got = gpu_backward(Q, K, V, dO, w.L, "bf16", f1, gh, gw, state_in=st0,
+                       dstates=pack_dstates(dS, dz), want_dstate_in=True)
+    ref = oracle.rope_blockcausal_backward(Q, K, V, [0, w.L], dO, EPS, f1, gh, gw, THETA, S0, z0,
+                                           dS.astype(np.float64), dz.astype(np.float64))
+    check("rope 720p chunk backward", got[:3], ref[:3], [0, w.L], TOL["bf16"], got[3], ref[3:])
