@@ -63,7 +63,11 @@ int bwd_query_capacity(int d) {
                  : d == 64 ? la::bwd_query_min_waves<64>()
                            : la::bwd_query_min_waves<32>());
 }
-int bwd_key_capacity(int d) {
+int bwd_key_capacity(int d, bool rope) {
+  if (rope)
+    return kCUs * (d == 128 ? la::bwd_key_rope_min_waves<128>()
+                   : d == 64 ? la::bwd_key_rope_min_waves<64>()
+                             : la::bwd_key_rope_min_waves<32>());
   return kCUs * (d == 128 ? la::bwd_key_min_waves<128>()
                  : d == 64 ? la::bwd_key_min_waves<64>()
                            : la::bwd_key_min_waves<32>());
@@ -391,8 +395,10 @@ struct BwdPlan {
 };
 
 // ws_avail: the caller's workspace size (SIZE_MAX when planning the size).
+// rope: the rotary kernels (the key kernel's grid differs; the workspace,
+// set by the query splits alone, does not).
 BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest, int krequest,
-                      size_t ws_avail) {
+                      size_t ws_avail, bool rope = false) {
   BwdPlan p{};
   p.T = T < N ? T : N;
   p.nblk = N == 0 ? 0 : (N + p.T - 1) / p.T;
@@ -440,7 +446,7 @@ BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest
   if (krequest > 0) {
     kw = (krequest + pairs - 1) / pairs;
   } else if (bf) {
-    kw = items_per_block(pairs, bwd_key_capacity(d));
+    kw = items_per_block(pairs, bwd_key_capacity(d, rope));
   } else {
     kw = (kBwdF32TargetWorkgroups + pairs - 1) / pairs;
   }
@@ -449,7 +455,8 @@ BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest
   if (bf) {
     p.ks = static_cast<int>(kw);
     const long long items = pairs * kw;
-    p.kgrid = static_cast<int>(items < bwd_key_capacity(d) ? items : bwd_key_capacity(d));
+    const int cap = bwd_key_capacity(d, rope);
+    p.kgrid = static_cast<int>(items < cap ? items : cap);
   } else {
     const int per = static_cast<int>((Tb + kw - 1) / kw);
     p.ktps = (per + tile - 1) / tile * tile;
@@ -604,7 +611,8 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
   BwdPlan p = empty_block
                   ? make_bwd_plan(B, H, 1, 1, d, in_dt, 1, 1, SIZE_MAX)
                   : make_bwd_plan(B, H, N, T, d, in_dt, opts ? opts->kv_splits : 0,
-                                  opts ? opts->readout_workgroups : 0, workspace_bytes);
+                                  opts ? opts->readout_workgroups : 0, workspace_bytes,
+                                  rope != nullptr);
   if (empty_block) {
     p.T = 1;  // one block of no tokens: every workgroup's range is empty
   }

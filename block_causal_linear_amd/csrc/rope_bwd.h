@@ -256,6 +256,22 @@ constexpr size_t bwd_key_rope_f32_smem() {
   return sizeof(float) * (D * D + D + 4 * 16 * D + D);
 }
 
+// Waves per SIMD of the rotary key kernel (its launch bound, and with
+// four-wave workgroups its workgroups per CU).  Below the plain kernel's
+// bound at d <= 64: the rotation's extra registers would spill, and the
+// spill slots of every resident wave together exceed L2, so their reloads
+// in the tile loop would go to HBM.
+#ifndef LA_ROPE_BWDK_WAVES64
+#define LA_ROPE_BWDK_WAVES64 3
+#endif
+#ifndef LA_ROPE_BWDK_WAVES32
+#define LA_ROPE_BWDK_WAVES32 5
+#endif
+template <int D>
+constexpr int bwd_key_rope_min_waves() {
+  return D == 128 ? 1 : D == 64 ? LA_ROPE_BWDK_WAVES64 : LA_ROPE_BWDK_WAVES32;
+}
+
 // ---------------------------------------------------------------------------
 // bwd_key_rope_bf16: dK and dV with rotated keys (bf16 keys and values), the
 // structure of bwd_key_bf16.  Per tile each wave takes 16 tokens as MFMA rows:
@@ -266,7 +282,7 @@ constexpr size_t bwd_key_rope_f32_smem() {
 //                 A operand (three products): dv.
 // Token positions are carried from tile to tile (S tiles per step).
 template <int D, bool GO_BF16>
-__global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_rope_bf16(
+__global__ __launch_bounds__(256, bwd_key_rope_min_waves<D>()) void bwd_key_rope_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ R,
     void* __restrict__ dk, void* __restrict__ dv, int N, int TB, int nblk, int S, int items,
     RopeGrid rg) {
