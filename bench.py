@@ -11,7 +11,9 @@ Prints one JSON line.  `value` is latent tokens per second of the whole
 call; `roofline` covers the dominant kernel (the readout) with algorithmic
 bytes per launch over its average launch time from HIP events recorded on
 the library's stream inside the timed region; `cpu_baseline` times the fp64
-oracle on the same workload on the host.
+oracle on the same workload on the host; `per_call_us` gives the median and
+10th/90th percentiles of further calls (--spread-calls, default 60), each
+bracketed by its own events after the timed region (not part of `value`).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --workload {chunk720p,global480p,global720p,stream480p,longhorizon}
@@ -48,6 +50,13 @@ PLAN_CONSTANTS = ("kSweepWorkgroups", "LA_READOUT_ROWS", "LA_READOUT_STREAM")
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def spread_us(ms):
+    """Median, 10th and 90th percentile (us) of per-call times in ms."""
+    x = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median": float(np.median(x)), "p10": float(np.percentile(x, 10)),
+            "p90": float(np.percentile(x, 90)), "samples": int(x.size)}
 
 
 def _code_only(text):
@@ -552,6 +561,9 @@ def main():
                     help="record per-stage HIP events on every N-th timed step")
     ap.add_argument("--plain-steps", type=int, default=0,
                     help="also time this many steps without stage events (for comparison)")
+    ap.add_argument("--spread-calls", type=int, default=60,
+                    help="after the timed region, bracket this many calls each with events "
+                         "for the per-call median and 10th/90th percentiles")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -644,6 +656,19 @@ def main():
         plain_ms = start.elapsed_time(end) / args.plain_steps
         log(f"without stage events: {plain_ms * 1e3:.1f} us/step")
 
+    spread = None
+    if args.spread_calls > 0:
+        # not part of `value`: every call bracketed by its own events
+        sp = [la.StageEvents() for _ in range(args.spread_calls)]
+        torch.cuda.synchronize()
+        for i, e in enumerate(sp):
+            step(i, e)
+        torch.cuda.synchronize()
+        per = np.array([e.elapsed_ms() for e in sp])  # [calls, 3] ms
+        for e in sp:
+            e.close()
+        spread = {"call": spread_us(per.sum(axis=1)), "readout": spread_us(per[:, 2])}
+
     call_b, kv_b, ro_b = bytes_alg(B, H, L, d)
     kv_ms, red_ms, ro_ms = (float(x) for x in stages.mean(axis=0))
     tokens_per_s = B * L / (ms * 1e-3)
@@ -679,6 +704,8 @@ def main():
         "kv_partial_GBs": kv_gbs,
         "mfma_frac_call": flops(B, H, L, d) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
     }
+    if spread is not None:
+        result["per_call_us"] = spread
     if plain_ms is not None:
         result["ms_per_step_without_stage_events"] = plain_ms
     if not args.no_cpu_baseline:

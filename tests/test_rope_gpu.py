@@ -261,3 +261,55 @@ def test_rope_long_horizon_d128_one_call():
         report(f"rope long-horizon one-call head ({b},{h})", out=eo, states=es)
         worst = max(worst, eo, es)
     assert worst <= TOL["bf16"], worst
+
+
+# ---------------------------------------------------------------------------
+# the longest rotary sequence the ABI accepts: token indices below 2^22 - 64
+
+
+def test_rope_max_size_sequence():
+    """One head of 2^22 - 65 tokens at d = 64 on a 32 x 64 grid starting at
+    frame 1,000,003, drawn on the GPU: la_blockcausal_forward_rope with two
+    blocks of 2^21 tokens.  Both block states are compared whole against the
+    oracle's sums over frame-aligned host chunks (rope_chunk_forward carrying
+    the state); the outputs on whole sampled frames, including the last frame
+    of block 0, the first of block 1 and the ragged last frame, against
+    rope_chunk_forward of that frame with keys that phi maps to zero (so the
+    block's state is read unchanged)."""
+    d, gh, gw, f0 = 64, 32, 64, 1_000_003
+    hw = gh * gw
+    N, T = (1 << 22) - 65, 1 << 21
+    gen = torch.Generator(device="cuda").manual_seed(20261203)
+    q, k, v = (torch.randn((1, 1, N, d), generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    out, states = la.blockcausal_forward_rope(q, k, v, T, f0, gh, gw, THETA, eps=EPS)
+    torch.cuda.synchronize()
+
+    S, z = oracle.zero_state(1, 1, d)
+    block_states = []
+    step = 1 << 20  # a whole number of frames
+    for c0 in range(0, N, step):
+        Kc, Vc = host(k[:, :, c0:c0 + step]), host(v[:, :, c0:c0 + step])
+        _, S, z = oracle.rope_chunk_forward(-np.ones_like(Kc), Kc, Vc, S, z, EPS,
+                                            f0 + c0 // hw, gh, gw, THETA)
+        if c0 + step in (T, N) or c0 + step > N:
+            block_states.append((S.copy(), z.copy()))
+    assert len(block_states) == 2
+    es = [max(state_err(host(states[:, :, n]), *block_states[n])) for n in range(2)]
+
+    last = (N - 1) // hw
+    frames = sorted({0, T // hw - 1, T // hw, last} | set(
+        np.random.default_rng(9).integers(0, last, 3).tolist()))
+    worst = 0.0
+    for f in frames:
+        a, b = f * hw, min(N, (f + 1) * hw)
+        n = 0 if a < T else 1
+        Qf = host(q[:, :, a:b])
+        O_ref, S_chk, _ = oracle.rope_chunk_forward(Qf, -np.ones_like(Qf), np.zeros_like(Qf),
+                                                    *block_states[n], EPS, f0 + f, gh, gw, THETA)
+        assert np.array_equal(S_chk, block_states[n][0])
+        eo = out_err(host(out[:, :, a:b]), O_ref)
+        report(f"rope max-size frame {f} (block {n}, {b - a} tokens)", out=eo)
+        worst = max(worst, eo)
+    report("rope max-size states", S0=es[0], S1=es[1])
+    assert max(worst, *es) <= TOL["bf16"], (worst, es)
