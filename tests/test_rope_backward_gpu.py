@@ -189,3 +189,66 @@ def test_rope_backward_720p_chunk():
     ref = oracle.rope_blockcausal_backward(Q, K, V, [0, w.L], dO, EPS, f1, gh, gw, THETA, S0, z0,
                                            dS.astype(np.float64), dz.astype(np.float64))
     check("rope 720p chunk backward", got[:3], ref[:3], [0, w.L], TOL["bf16"], got[3], ref[3:])
+
+
+def test_rope_backward_max_size_sequence():
+    """The longest rotary sequence accepted (2^22 - 65 tokens at d = 64, a
+    32 x 64 grid from frame 1,000,003, two blocks of 2^21 tokens).  The
+    oracle runs per frame-aligned host chunk, from its own functions only:
+      * the block states: rope_chunk_forward carrying the state;
+      * dq of every query: rope_blockcausal_backward of the chunk as one
+        block whose keys phi maps to zero, reading the block's state; its
+        dS0, dz0 are the chunk's share of the block's state gradient;
+      * dk, dv of every key in two chunks (the last of block 0 and the ragged
+        last one): rope_blockcausal_backward with dO = 0 and the suffix of
+        the blocks' state gradients given as the block's state gradient."""
+    d, gh, gw, f0 = 64, 32, 64, 1_000_003
+    hw = gh * gw
+    N, T = (1 << 22) - 65, 1 << 21
+    gen = torch.Generator(device="cuda").manual_seed(20261204)
+    q, k, v = (torch.randn((1, 1, N, d), generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    do = torch.randn((1, 1, N, d), generator=gen, device="cuda")
+    _, states = la.blockcausal_forward_rope(q, k, v, T, f0, gh, gw, THETA, eps=EPS)
+    dq, dk, dv, _ = la.blockcausal_backward_rope(q, k, v, states, do, T, f0, gh, gw, THETA,
+                                                 eps=EPS)
+    torch.cuda.synchronize()
+    del states
+
+    step = 1 << 20  # a whole number of frames; blocks are two steps each
+    chunks = [(c0, min(N, c0 + step)) for c0 in range(0, N, step)]
+    block_of = [0 if c0 < T else 1 for c0, _ in chunks]
+    S, z = oracle.zero_state(1, 1, d)
+    block_states = []
+    for (a, b), n in zip(chunks, block_of):
+        Kc, Vc = host(k[:, :, a:b]), host(v[:, :, a:b])
+        _, S, z = oracle.rope_chunk_forward(-np.ones_like(Kc), Kc, Vc, S, z, EPS, f0 + a // hw,
+                                            gh, gw, THETA)
+        if b in (T, N):
+            block_states.append((S.copy(), z.copy()))
+
+    dSb = [np.zeros((1, 1, d, d)) for _ in range(2)]
+    dzb = [np.zeros((1, 1, d)) for _ in range(2)]
+    worst = 0.0
+    for (a, b), n in zip(chunks, block_of):
+        Qc, dOc = host(q[:, :, a:b]), host(do[:, :, a:b])
+        dQc, _, _, dS0, dz0 = oracle.rope_blockcausal_backward(
+            Qc, -np.ones_like(Qc), np.zeros_like(Qc), [0, b - a], dOc, EPS, f0 + a // hw, gh, gw,
+            THETA, *block_states[n])
+        dSb[n] += dS0
+        dzb[n] += dz0
+        e = normwise(host(dq[:, :, a:b]), dQc, axes=(2, 3))
+        report(f"rope max-size backward dq tokens {a}..{b}", dq=e)
+        worst = max(worst, e)
+    G = [dSb[0] + dSb[1], dSb[1]]
+    g = [dzb[0] + dzb[1], dzb[1]]
+    for (a, b), n in [(chunks[1], block_of[1]), (chunks[-1], block_of[-1])]:
+        Kc, Vc = host(k[:, :, a:b]), host(v[:, :, a:b])
+        _, dKc, dVc, _, _ = oracle.rope_blockcausal_backward(
+            -np.ones_like(Kc), Kc, Vc, [0, b - a], np.zeros_like(Kc), EPS, f0 + a // hw, gh, gw,
+            THETA, *block_states[n], G[n][None], g[n][None])
+        ek = normwise(host(dk[:, :, a:b]), dKc, axes=(2, 3))
+        ev = normwise(host(dv[:, :, a:b]), dVc, axes=(2, 3))
+        report(f"rope max-size backward dk/dv tokens {a}..{b}", dk=ek, dv=ev)
+        worst = max(worst, ek, ev)
+    assert worst <= TOL["bf16"], worst
