@@ -79,9 +79,14 @@ __device__ __forceinline__ int bwd_swizzle(int t) {
 #ifndef LA_BWDQ_DNB64
 #define LA_BWDQ_DNB64 2    // query kernel dnum tile buffers at d = 64
 #endif
+#ifndef LA_BWDQ_WAVES32
+// query kernel waves per SIMD at d = 32: at four it spills 100 B per lane,
+// ~26 MB over the resident waves; three need no spill slots
+#define LA_BWDQ_WAVES32 3
+#endif
 template <int D>
 constexpr int bwd_query_min_waves() {
-  return D == 128 ? 1 : D == 64 ? LA_BWDQ_WAVES64 : 4;
+  return D == 128 ? 1 : D == 64 ? LA_BWDQ_WAVES64 : LA_BWDQ_WAVES32;
 }
 
 template <int D, bool GO_BF16>
