@@ -130,9 +130,9 @@ def cpu_baseline(w, seconds_min=10.0):
     per = t_total / runs
     return {"value": B * L / per, "unit": "latent tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"the full 720p chunk (B=1, H=32, d=64, L=75,600), fp64 numpy, "
-                      f"{runs} run(s), {per:.2f} s each; host cpus visible: "
-                      f"{len(os.sched_getaffinity(0))}"}
+            "sample": f"the full 720p chunk (B=1, H=32, d=64, L=75,600), fp64 numpy "
+                      f"{np.__version__} ({threads} BLAS threads), {runs} run(s), {per:.2f} s "
+                      f"each; host cpus visible: {len(os.sched_getaffinity(0))}"}
 
 
 def copy_calibration(steps):

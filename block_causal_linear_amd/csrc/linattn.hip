@@ -8,6 +8,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "linattn.h"
 #include "la_common.h"
 #include "kv_reduce.h"
@@ -129,6 +131,35 @@ int check_shape(int B, int H, int N, int d, int in_dt, int out_dt) {
     return LA_E_UNSUPPORTED;
   // keep every per-head element index inside 31 bits
   if (static_cast<long long>(N) * d >= (1LL << 31)) return LA_E_INVAL;
+  return LA_OK;
+}
+
+// Every tensor a call touches stays below 1 TiB, more than one GPU holds:
+// byte counts, grid sizes and work-item counts then stay in range for any
+// int arguments.  `factors` multiply to a byte count.
+constexpr unsigned long long kMaxTensorBytes = 1ULL << 40;
+bool bytes_below_limit(std::initializer_list<unsigned long long> factors) {
+  for (unsigned long long f : factors)
+    if (f == 0) return true;
+  unsigned long long prod = 1;
+  for (unsigned long long f : factors) {
+    if (prod > (kMaxTensorBytes - 1) / f) return false;
+    prod *= f;
+  }
+  return true;
+}
+
+// The token tensors ([B][H][N][d], at most 4 bytes an element) and the block
+// states ([B][H][blocks][d*d + d] float32) of a call with blocks of T tokens.
+int check_sizes(int B, int H, int N, int T, int d) {
+  const int t = T < N ? T : N;
+  const unsigned long long nblk = N == 0 ? 1 : (static_cast<unsigned long long>(N) + t - 1) / t;
+  const unsigned long long st = (static_cast<unsigned long long>(d) * d + d) * sizeof(float);
+  const unsigned long long b = static_cast<unsigned long long>(B);
+  const unsigned long long h = static_cast<unsigned long long>(H);
+  if (!bytes_below_limit({b, h, static_cast<unsigned long long>(N) * d, 4}) ||
+      !bytes_below_limit({b, h, nblk, st}))
+    return LA_E_INVAL;
   return LA_OK;
 }
 
@@ -593,6 +624,7 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
   int rc = check_shape(B, H, N, d, in_dt, grad_dt);
   if (rc != LA_OK) return rc;
   if (T <= 0) return LA_E_INVAL;
+  if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
   if ((rc = check_rope(rope, N)) != LA_OK) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
   if (N > 0 && (q == nullptr || k == nullptr || v == nullptr || states == nullptr ||
@@ -671,6 +703,11 @@ int temporal_conv(const void* x, const void* cache_in, const float* w, const flo
                   hipStream_t stream) {
   if (B <= 0 || F < 0 || P <= 0 || C <= 0 || Tf <= 0) return LA_E_INVAL;
   if (C % 8 != 0) return LA_E_UNSUPPORTED;
+  using ull = unsigned long long;
+  if (!bytes_below_limit({static_cast<ull>(B), static_cast<ull>(F), static_cast<ull>(P),
+                          static_cast<ull>(C), 4}) ||
+      !bytes_below_limit({static_cast<ull>(B), static_cast<ull>(P), static_cast<ull>(C), 4}))
+    return LA_E_INVAL;
   if ((x_dt != LA_F32 && x_dt != LA_BF16) || (y_dt != LA_F32 && y_dt != LA_BF16))
     return LA_E_UNSUPPORTED;
   if (w == nullptr || (F > 0 && (x == nullptr || y == nullptr))) return LA_E_INVAL;
@@ -723,6 +760,7 @@ int forward(const void* q, const void* k, const void* v, const float* state_in,
   int rc = check_shape(B, H, N, d, in_dt, out_dt);
   if (rc != LA_OK) return rc;
   if (T <= 0) return LA_E_INVAL;
+  if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
   if ((rc = check_rope(rope, N)) != LA_OK) return rc;
   if (!(eps >= 0.0f) || !isfinite(eps)) return LA_E_INVAL;
   if (states == nullptr || (need_state_in && state_in == nullptr)) return LA_E_INVAL;
@@ -787,7 +825,7 @@ la::RopeGrid rope_grid(int frame0, int grid_h, int grid_w, float theta) {
 extern "C" {
 
 int la_state_reset(float* state, int B, int H, int d, hipStream_t stream) {
-  if (B <= 0 || H <= 0) return LA_E_INVAL;
+  if (B <= 0 || H <= 0 || B > 65535 || H > 65535) return LA_E_INVAL;
   if (d != 32 && d != 64 && d != 128) return LA_E_UNSUPPORTED;
   if (state == nullptr) return LA_E_INVAL;
   if (!aligned16(state)) return LA_E_ALIGN;
@@ -872,8 +910,9 @@ int la_blockcausal_forward_rope_ex(const void* q, const void* k, const void* v,
 
 int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_request,
             int readout_workgroups_request, int* kv_splits, int* readout_workgroups) {
-  const int rc = check_shape(B, H, L, d, in_dt, out_dt);
+  int rc = check_shape(B, H, L, d, in_dt, out_dt);
   if (rc != LA_OK) return rc;
+  if ((rc = check_sizes(B, H, L, L > 0 ? L : 1, d)) != LA_OK) return rc;
   if (kv_splits == nullptr || readout_workgroups == nullptr) return LA_E_INVAL;
   const Plan p = make_plan(B, H, L, L > 0 ? L : 1, d, in_dt, out_dt, kv_splits_request,
                            readout_workgroups_request);
@@ -883,9 +922,10 @@ int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_req
 }
 
 int la_backward_workspace_size(int B, int H, int N, int T, int d, int in_dt, size_t* bytes) {
-  const int rc = check_shape(B, H, N, d, in_dt, LA_F32);
+  int rc = check_shape(B, H, N, d, in_dt, LA_F32);
   if (rc != LA_OK) return rc;
   if (T <= 0 || bytes == nullptr) return LA_E_INVAL;
+  if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
   const BwdPlan p = N == 0 ? make_bwd_plan(B, H, 1, 1, d, in_dt, 1, 1, SIZE_MAX)
                            : make_bwd_plan(B, H, N, T, d, in_dt, 0, 0, SIZE_MAX);
   *bytes = p.ws_bytes;

@@ -44,7 +44,10 @@
  * Streams and errors: every call only enqueues work on `stream` (0 = the
  * null stream) and returns at once.  Arguments are checked before anything
  * is enqueued; a rejected call enqueues nothing and returns:
- *   LA_E_INVAL        null pointer where L > 0, B/H <= 0, L < 0, eps < 0 or not finite
+ *   LA_E_INVAL        null pointer where L > 0, B/H <= 0 or > 65535, L < 0,
+ *                     L * d >= 2^31, eps < 0 or not finite, or a tensor of 2^40
+ *                     bytes or more (B*H*L*d at 4 bytes an element, or the
+ *                     float32 states of every block): beyond any one GPU
  *   LA_E_UNSUPPORTED  d not in {32, 64, 128}, or an unknown dtype code
  *   LA_E_ALIGN        a pointer not 16-byte aligned
  *   LA_E_ALIAS        `out` overlaps an input or a state, or state_out overlaps
@@ -362,7 +365,7 @@ int la_blockcausal_backward_rope_ex(const void* q, const void* k, const void* v,
  *   cache_out : [B][P][C] x_dt, written with the last frame (NULL: not
  *               wanted); F = 0 copies cache_in (or zeros) into it.
  * Errors: LA_E_INVAL (B, P, C <= 0, F < 0, Tf <= 0, a needed pointer NULL,
- * more than 65535 chunks), LA_E_UNSUPPORTED (C not a multiple of 8, dtype),
+ * more than 65535 chunks, B*F*P*C*4 >= 2^40), LA_E_UNSUPPORTED (C not a multiple of 8, dtype),
  * LA_E_ALIGN, LA_E_ALIAS (y overlapping anything else; cache_out overlapping
  * x, weight, bias, or cache_in unless it is cache_in itself and the call has
  * one chunk).

@@ -266,6 +266,31 @@ def test_rope_backward_rejects(kw, code, ex):
     assert rope_bwd(ex=ex, **kw) == code
 
 
+def test_sizes_beyond_one_gpu_rejected():
+    """Shapes whose tensors reach 2^40 bytes are rejected before anything is
+    enqueued (the pointers here are not device memory)."""
+    L_ = la.lib()
+    # 65535 x 65535 heads of 64 tokens: 2^44 bytes of q alone
+    assert chunk(B=65535, H=65535, L=64) == la.LA_E_INVAL
+    assert bc(B=65535, H=2, N=1 << 24, T=1 << 20) == la.LA_E_INVAL
+    # one-token blocks: the states of 2^23 blocks x 16 heads at d = 128 are 8.9e12 bytes
+    assert bc(B=1, H=16, N=1 << 23, T=1, d=128) == la.LA_E_INVAL
+    assert bwd(B=65535, H=65535, N=64) == la.LA_E_INVAL
+    assert rope_bwd(B=65535, H=65535, N=64) == la.LA_E_INVAL
+    z = ctypes.c_size_t()
+    assert L_.la_backward_workspace_size(65535, 65535, 64, 64, 64, BF16,
+                                         ctypes.byref(z)) == la.LA_E_INVAL
+    k = ctypes.c_int()
+    assert L_.la_plan(65535, 65535, 64, 64, BF16, F32, 0, 0, ctypes.byref(k),
+                      ctypes.byref(k)) == la.LA_E_INVAL
+    assert L_.la_state_reset(A, 70000, 1, 64, None) == la.LA_E_INVAL
+    assert L_.la_temporal_conv_chunk(A, None, 2 * A, None, 3 * A, None, 1, 1 << 20, 1 << 20,
+                                     1024, BF16, BF16, None) == la.LA_E_INVAL
+    # below the limit (states 5.5e11 bytes) the call gets past the size check
+    # to the alignment check
+    assert bc(B=1, H=8, N=1 << 20, T=1, d=128, q=A + 8) == la.LA_E_ALIGN
+
+
 def test_backward_entry_points_reject():
     L_ = la.lib()
     # the chunk call needs state_out; the global call rejects a bad d
