@@ -252,3 +252,40 @@ def test_rope_backward_max_size_sequence():
         report(f"rope max-size backward dk/dv tokens {a}..{b}", dk=ek, dv=ev)
         worst = max(worst, ek, ev)
     assert worst <= TOL["bf16"], worst
+
+
+def test_rope_backward_degenerate_rows():
+    """A query row with no positive entry gets dq = 0 exactly; a key row with
+    no positive entry gets dk = 0 and dv = 0 exactly (its rotated phi(k) is
+    zero)."""
+    B, H, N, T, d, gh, gw = 1, 2, 1000, 300, 64, 6, 10
+    Q, K, V = workloads.random_qkv(141, B, H, N, d)
+    Q[:, :, 17] = -np.abs(Q[:, :, 17])
+    K[:, :, 450] = -np.abs(K[:, :, 450])
+    dO = workloads.random_grads(142, B, H, N, d)
+    dq, dk, dv, _ = gpu_backward(Q, K, V, dO, T, "bf16", 3, gh, gw)
+    assert np.all(dq[:, :, 17] == 0.0)
+    assert np.all(dk[:, :, 450] == 0.0) and np.all(dv[:, :, 450] == 0.0)
+    ref = oracle.rope_blockcausal_backward(Q, K, V, bounds_of(N, T), dO, EPS, 3, gh, gw, THETA)
+    check("rope backward degenerate rows", [dq, dk, dv], ref[:3], bounds_of(N, T), TOL["bf16"])
+
+
+def test_rope_backward_zero_eps_ragged():
+    """eps = 0 with every denominator kept > 0: the padding rows past a
+    ragged tile and block (whose positions are still turned) stay out of
+    every sum, so nothing turns into NaN."""
+    B, H, N, T, d, gh, gw = 1, 2, 1000, 300, 64, 7, 9
+    Q, K, V = workloads.random_qkv(143, B, H, N, d)
+    Q[..., 0] = np.abs(Q[..., 0]) + 0.25
+    K[..., 0] = np.abs(K[..., 0]) + 0.25
+    Q, K = workloads.bf16_round(Q), workloads.bf16_round(K)
+    dO = workloads.random_grads(144, B, H, N, d)
+    q, k, v = dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16")
+    _, states = la.blockcausal_forward_rope(q, k, v, T, 4, gh, gw, THETA, eps=0.0)
+    dq, dk, dv, _ = la.blockcausal_backward_rope(q, k, v, states, dev(dO, "f32"), T, 4, gh, gw,
+                                                 THETA, eps=0.0)
+    torch.cuda.synchronize()
+    got = [host(dq), host(dk), host(dv)]
+    assert all(np.all(np.isfinite(x)) for x in got)
+    ref = oracle.rope_blockcausal_backward(Q, K, V, bounds_of(N, T), dO, 0.0, 4, gh, gw, THETA)
+    check("rope backward eps=0", got, ref[:3], bounds_of(N, T), TOL["bf16"])

@@ -313,3 +313,46 @@ def test_rope_max_size_sequence():
         worst = max(worst, eo)
     report("rope max-size states", S0=es[0], S1=es[1])
     assert max(worst, *es) <= TOL["bf16"], (worst, es)
+
+
+def test_rope_degenerate_rows():
+    """With the rotation, as without: an all-non-positive query row gives
+    exactly 0, and all-non-positive key rows contribute nothing (the result
+    is bitwise unchanged whatever their values)."""
+    B, H, N, T, d, gh, gw, f0 = 1, 2, 700, 300, 64, 5, 8, 2
+    Q, K, V = workloads.random_qkv(131, B, H, N, d)
+    Q[:, :, 7] = -np.abs(Q[:, :, 7])
+    K[:, :, 100:150] = -np.abs(K[:, :, 100:150])
+    V2 = V.copy()
+    V2[:, :, 100:150] = workloads.random_qkv(132, B, H, 50, d)[2]
+    args = (T, f0, gh, gw, THETA)
+    out, st = la.blockcausal_forward_rope(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), *args,
+                                          eps=EPS)
+    out2, st2 = la.blockcausal_forward_rope(dev(Q, "bf16"), dev(K, "bf16"), dev(V2, "bf16"),
+                                            *args, eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[:, :, 7]) == 0
+    assert torch.equal(out, out2) and torch.equal(st, st2)
+    O_ref, _, _ = oracle.rope_prefix_forward(Q, K, V, _bounds(N, T), EPS, f0, gh, gw, THETA)
+    assert out_err(host(out), O_ref) <= TOL["bf16"]
+
+
+def test_rope_zero_eps_ragged():
+    """eps = 0 with every denominator kept > 0: rows past the ragged end of a
+    tile and of a block stay out of every sum, so nothing turns into NaN."""
+    B, H, N, T, d, gh, gw = 1, 2, 1000, 300, 64, 7, 9
+    Q, K, V = workloads.random_qkv(133, B, H, N, d)
+    Q[..., 0] = np.abs(Q[..., 0]) + 0.25
+    K[..., 0] = np.abs(K[..., 0]) + 0.25
+    Q, K = workloads.bf16_round(Q), workloads.bf16_round(K)
+    out, st = la.blockcausal_forward_rope(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), T, 4,
+                                          gh, gw, THETA, eps=0.0)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    O_ref, S_pre, z_pre = oracle.rope_prefix_forward(Q, K, V, _bounds(N, T), 0.0, 4, gh, gw,
+                                                     THETA)
+    eo = out_err(got, O_ref)
+    es = _states_err(host(st), S_pre, z_pre)
+    report("rope eps=0", out=eo, state=es)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
