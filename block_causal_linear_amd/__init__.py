@@ -76,6 +76,8 @@ _SIGNATURES = {
                                         ctypes.POINTER(LaunchOpts), _P],
     "la_chunk_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F,
                           _P, _Z, _P],
+    "la_chunk_backward_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                               _F, _P, _Z, _I, _I, _I, _F, _P],
     "la_global_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
                            _P],
     "la_temporal_conv_chunk": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
@@ -476,6 +478,32 @@ def chunk_backward(q, k, v, state_out, dout, dstate_out=None, want_dstate_in=Tru
         _ptr(q), _ptr(k), _ptr(v), _ptr(state_out), _ptr(dout), _ptr(dstate_out), _ptr(dq),
         _ptr(dk), _ptr(dv), _ptr(dstate_in), B, H, L, d, _DTYPE[q.dtype], _DTYPE[dout.dtype],
         float(eps), _ptr(workspace), ws_bytes, _stream(q.device)), "la_chunk_backward")
+    return dq, dk, dv, dstate_in
+
+
+def chunk_backward_rope(q, k, v, state_out, dout, frame0, grid_h, grid_w, theta=DEFAULT_THETA,
+                        dstate_out=None, want_dstate_in=True, eps=DEFAULT_EPS, dq=None, dk=None,
+                        dv=None, dstate_in=None, workspace=None):
+    """Gradients of chunk_forward_rope(q, k, v, state_in, frame0, grid_h,
+    grid_w, theta) -> (out, state_out) for the upstream gradients dout and
+    dstate_out (None: zero).  Returns (dq, dk, dv, dstate_in)."""
+    dq, dk, dv = _prepare_grads(q, k, v, dout, dq, dk, dv)
+    B, H, L, d = q.shape
+    _state_like(state_out, (B, H, d * d + d), "state_out", q.device)
+    if dstate_out is not None:
+        _state_like(dstate_out, (B, H, d * d + d), "dstate_out", q.device)
+    if want_dstate_in and dstate_in is None:
+        dstate_in = torch.empty((B, H, d * d + d), dtype=torch.float32, device=q.device)
+    if dstate_in is not None:
+        _state_like(dstate_in, (B, H, d * d + d), "dstate_in", q.device)
+    need = backward_workspace_size(B, H, L, L, d, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().la_chunk_backward_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state_out), _ptr(dout), _ptr(dstate_out), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(dstate_in), B, H, L, d, _DTYPE[q.dtype], _DTYPE[dout.dtype],
+        float(eps), _ptr(workspace), ws_bytes, int(frame0), int(grid_h), int(grid_w),
+        float(theta), _stream(q.device)), "la_chunk_backward_rope")
     return dq, dk, dv, dstate_in
 
 

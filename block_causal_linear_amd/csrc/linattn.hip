@@ -22,7 +22,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -959,6 +959,18 @@ int la_chunk_backward(const void* q, const void* k, const void* v, const float* 
   return backward(q, k, v, state_out, dout, dstate_out, dq, dk, dv, dstate_in, B, H, L,
                   L > 0 ? L : 1, d, in_dt, grad_dt, eps, workspace, workspace_bytes, L == 0,
                   nullptr, stream);
+}
+
+int la_chunk_backward_rope(const void* q, const void* k, const void* v, const float* state_out,
+                           const void* dout, const float* dstate_out, void* dq, void* dk,
+                           void* dv, float* dstate_in, int B, int H, int L, int d, int in_dt,
+                           int grad_dt, float eps, void* workspace, size_t workspace_bytes,
+                           int frame0, int grid_h, int grid_w, float theta, hipStream_t stream) {
+  if (state_out == nullptr) return LA_E_INVAL;
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return backward(q, k, v, state_out, dout, dstate_out, dq, dk, dv, dstate_in, B, H, L,
+                  L > 0 ? L : 1, d, in_dt, grad_dt, eps, workspace, workspace_bytes, L == 0,
+                  nullptr, stream, &g);
 }
 
 int la_global_backward(const void* q, const void* k, const void* v, const float* state,

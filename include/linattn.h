@@ -346,6 +346,19 @@ int la_blockcausal_backward_rope_ex(const void* q, const void* k, const void* v,
                                     const la_launch_opts* opts, hipStream_t stream);
 
 /*
+ * la_chunk_backward_rope - gradients of one la_chunk_forward_rope call, as
+ * la_chunk_backward is of la_chunk_forward: state_out (the state the
+ * queries read, keys rotated by absolute position) read, dstate_out read or
+ * NULL (zero), dstate_in written or NULL; frame0, grid_h, grid_w and theta
+ * as the forward call took them.  L = 0: dstate_in = dstate_out (or zeros).
+ */
+int la_chunk_backward_rope(const void* q, const void* k, const void* v, const float* state_out,
+                           const void* dout, const float* dstate_out, void* dq, void* dk,
+                           void* dv, float* dstate_in, int B, int H, int L, int d, int in_dt,
+                           int grad_dt, float eps, void* workspace, size_t workspace_bytes,
+                           int frame0, int grid_h, int grid_w, float theta, hipStream_t stream);
+
+/*
  * Temporal convolution of the Spatial-Temporal Mix-FFN with its
  * chunk-boundary cache ([TR] section "Verimli doğrusal DiT": the MLP
  * alternates 1x3x3 spatial and 3x1x1 temporal convolutions; [ZH] section 1:
@@ -396,7 +409,8 @@ int la_plan(int B, int H, int L, int d, int in_dt, int out_dt, int kv_splits_req
 /* Static text for a status code. */
 const char* la_status_string(int status);
 
-/* ABI version of this header (increases on incompatible change). */
+/* ABI version of this header (increases whenever a call is added or a call's
+ * arguments or behaviour change). */
 int la_abi_version(void);
 
 #ifdef __cplusplus

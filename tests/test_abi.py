@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 6
+    assert la.abi_version() == 7
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -264,6 +264,20 @@ def rope_bwd(q=A, k=2 * A, v=3 * A, sts=4 * A, do=5 * A, dsts=None, dq=6 * A, dk
 ])
 def test_rope_backward_rejects(kw, code, ex):
     assert rope_bwd(ex=ex, **kw) == code
+
+
+def test_rope_chunk_backward_rejects():
+    L_ = la.lib()
+
+    def call(so=4 * A, gh=4, theta=10000.0, L=64, d=64):
+        return L_.la_chunk_backward_rope(A, 2 * A, 3 * A, so, 5 * A, None, 6 * A, 7 * A, 8 * A,
+                                         None, 1, 2, L, d, BF16, F32, 1e-6, 9 * A, 1 << 20, 0,
+                                         gh, 4, theta, None)
+    assert call(so=None) == la.LA_E_INVAL          # the chunk call needs state_out
+    assert call(gh=0) == la.LA_E_INVAL
+    assert call(theta=float("nan")) == la.LA_E_INVAL
+    assert call(L=-1) == la.LA_E_INVAL
+    assert call(d=40) == la.LA_E_UNSUPPORTED
 
 
 def test_sizes_beyond_one_gpu_rejected():

@@ -289,3 +289,44 @@ def test_rope_backward_zero_eps_ragged():
     assert all(np.all(np.isfinite(x)) for x in got)
     ref = oracle.rope_blockcausal_backward(Q, K, V, bounds_of(N, T), dO, 0.0, 4, gh, gw, THETA)
     check("rope backward eps=0", got, ref[:3], bounds_of(N, T), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# the chunk form: la_chunk_backward_rope
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_rope_chunk_backward(dtype, d):
+    """One chunk against a carried state, with a gradient on state_out."""
+    B, H, L, gh, gw, f0 = 2, 2, 1500, 6, 11, 9
+    Q, K, V = workloads.random_qkv(151 + d, B, H, L, d, dtype=dtype)
+    dO = workloads.random_grads(152 + d, B, H, L, d)
+    S0, z0 = workloads.random_state(153 + d, B, H, d, tokens=5000)
+    dS, dz = workloads.random_state_grads(154 + d, B, H, 1, d)
+    q, k, v = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    _, st = la.chunk_forward_rope(q, k, v, torch.from_numpy(state_np(S0, z0)).cuda(), f0, gh, gw,
+                                  THETA, eps=EPS)
+    dso = torch.from_numpy(state_np(dS[0], dz[0])).cuda()
+    dq, dk, dv, dsi = la.chunk_backward_rope(q, k, v, st, dev(dO, "f32"), f0, gh, gw, THETA,
+                                             dstate_out=dso, eps=EPS)
+    torch.cuda.synchronize()
+    ref = oracle.rope_blockcausal_backward(Q, K, V, [0, L], dO, EPS, f0, gh, gw, THETA,
+                                           S0.astype(np.float64), z0.astype(np.float64),
+                                           dS.astype(np.float64), dz.astype(np.float64))
+    check(f"rope chunk backward {dtype} d={d}", [host(dq), host(dk), host(dv)], ref[:3], [0, L],
+          TOL[dtype], host(dsi), ref[3:])
+
+
+def test_rope_chunk_backward_empty_passes_state_gradient():
+    """L = 0: state_out = state_in, so dstate_in = dstate_out exactly."""
+    B, H, d = 1, 3, 64
+    S0, z0 = workloads.random_state(161, B, H, d)
+    st = torch.from_numpy(state_np(S0, z0)).cuda()
+    dS, dz = workloads.random_state_grads(162, B, H, 1, d)
+    dso = torch.from_numpy(state_np(dS[0], dz[0])).cuda()
+    e = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    _, _, _, dsi = la.chunk_backward_rope(e, e, e, st, e.float(), 5, 4, 4, THETA, dstate_out=dso,
+                                          eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.equal(dsi, dso)
