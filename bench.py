@@ -45,7 +45,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "readout_720p_chunk_traffic.json")
 # What defines the readout kernel's HBM traffic at the 720p chunk: its
 # sources, and the planner constants that set its grid.
 KERNEL_SOURCES = ["la_common.h", "row_tiles.h", "readout.h"]
-PLAN_CONSTANTS = ("kSweepWorkgroups", "LA_READOUT_ROWS", "LA_READOUT_STREAM")
+PLAN_CONSTANTS = ("kSweepWorkgroups", "LA_READOUT_ROWS", "LA_READOUT_STREAM", "LA_READOUT_RUN")
 
 
 def log(msg):

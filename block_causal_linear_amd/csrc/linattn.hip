@@ -227,8 +227,9 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
     long long wgs = readout_request > 0 ? readout_request
                     : d == 128          ? kSweepWorkgroups128
                                         : kSweepWorkgroups;
-    const long long most = pairs * p.units_per_block;
-    if (wgs > most) wgs = most;
+    // workgroup steps take runs of LA_READOUT_RUN units
+    const long long runs = (pairs * p.units_per_block + LA_READOUT_RUN - 1) / LA_READOUT_RUN;
+    if (wgs > runs) wgs = runs;
     if (wgs < 1) wgs = 1;
     p.readout_wgs = static_cast<int>(wgs);
   } else {

@@ -22,6 +22,10 @@
 #ifndef LA_READOUT_ROWS
 #define LA_READOUT_ROWS 2
 #endif
+// Consecutive units per workgroup step run in the sweep readout.
+#ifndef LA_READOUT_RUN
+#define LA_READOUT_RUN 2
+#endif
 
 namespace la {
 
@@ -253,32 +257,46 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
     t0 = blk * T + ((rem - blk * upb) * 4 + tw) * Sh::TILE;
     te = min(N, (blk + 1) * T);
   };
-  int unit = blockIdx.x;
+  // Step j of workgroup w takes unit (w + (j / M) G) M + j % M: runs of M
+  // consecutive units, the runs of all workgroups sweeping together.  Within
+  // a run the state usually stays the same; its operands are then neither
+  // reloaded nor rebuilt, and no barrier is taken.
+  constexpr int M = LA_READOUT_RUN;
+  auto unit_of = [&](int j) {
+    return (static_cast<int>(blockIdx.x) + (j / M) * static_cast<int>(gridDim.x)) * M + j % M;
+  };
+  int unit = unit_of(0);
   if (unit >= total_units) return;
   int bh, sb, t0, te;
   locate(unit, bh, sb, t0, te);
   uint4 a[R][KS];
   load_state(sb);
   load_a(a, bh, t0, te);
-  for (int i = 0;; ++i) {
-    const int buf = NBUF == 2 ? (i & 1) : 0;
-    // With two buffers, buf was last read before the previous iteration's
-    // barrier; with one, wait until every wave has consumed the last unit.
-    if (NBUF == 1 && i > 0) __syncthreads();
-    build(buf);
-    __syncthreads();
-    const int next = unit + gridDim.x;
+  int built = -1;  // the state whose operands the current buffer holds
+  int buf = 1;
+  for (int j = 0;; ++j) {
+    if (sb != built) {
+      buf = NBUF == 2 ? buf ^ 1 : 0;
+      // With two buffers, buf was last read before the previous build's
+      // barrier; with one, wait until every wave has consumed the last unit.
+      if (NBUF == 1 && built >= 0) __syncthreads();
+      build(buf);
+      __syncthreads();
+      built = sb;
+    }
+    const int next = unit_of(j + 1);
     const bool more = next < total_units;
     const int nu = more ? next : unit;
     int nbh, nsb, nt0, nte;
     locate(nu, nbh, nsb, nt0, nte);
     uint4 an[R][KS];
-    load_state(nsb);
+    if (nsb != sb) load_state(nsb);
     load_a(an, nbh, nt0, nte);
     consume(buf, a, bh, t0, te);
     if (!more) break;
     unit = next;
     bh = nbh;
+    sb = nsb;
     t0 = nt0;
     te = nte;
 #pragma unroll
