@@ -188,6 +188,17 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
                              : rope    ? kKvRopeTargetWorkgroups
                                        : kKvTargetWorkgroups;
     s = (target + pairs - 1) / pairs;
+    // of s - 1, s, s + 1 take the count whose grid ends closest to a whole
+    // round of the CUs (ties: s); a grid of 2.25 workgroups per CU leaves
+    // most of its last round idle
+    const auto idle = [&](long long c) {
+      const long long wg = pairs * c;
+      return (kCUs - wg % kCUs) % kCUs;
+    };
+    long long best = s;
+    for (long long c = s - 1; c <= s + 1; ++c)
+      if (c >= 1 && idle(c) < idle(best)) best = c;
+    s = best;
     const long long by_size = Tb / (kKvMinTokensPerFeature * (d + 1));
     s = s < by_size ? s : by_size;
   }
