@@ -62,6 +62,8 @@ _SIGNATURES = {
                               _P],
     "la_blockcausal_forward_rope": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                     _I, _I, _F, _P],
+    "la_global_forward_rope": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _F,
+                               _P],
     "la_blockcausal_forward_rope_ex": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                        _I, _I, _I, _F, ctypes.POINTER(LaunchOpts), _P],
     "la_backward_workspace_size": [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)],
@@ -245,6 +247,20 @@ def global_forward(q, k, v, out=None, state_out=None, eps=DEFAULT_EPS,
     else:
         rc = L_.la_global_forward_ex(*args, ctypes.byref(o), _stream(q.device))
     _check(rc, "la_global_forward")
+    return out, state_out
+
+
+def global_forward_rope(q, k, v, frame0, grid_h, grid_w, theta=DEFAULT_THETA, out=None,
+                        state_out=None, eps=DEFAULT_EPS, out_dtype=torch.float32):
+    """global_forward with rotary position embedding on the numerator
+    (token 0 at frame frame0 of grid_h x grid_w tokens); state_out holds S
+    with every key turned by its position, and z."""
+    out, state_out = _prepare(q, k, v, out, out_dtype, state_out)
+    B, H, L, d = q.shape
+    _check(lib().la_global_forward_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_out), B, H, L, d, _DTYPE[q.dtype],
+        _DTYPE[out.dtype], float(eps), int(frame0), int(grid_h), int(grid_w), float(theta),
+        _stream(q.device)), "la_global_forward_rope")
     return out, state_out
 
 

@@ -22,7 +22,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -898,6 +898,15 @@ int la_chunk_forward_rope(const void* q, const void* k, const void* v, const flo
                           hipStream_t stream) {
   const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
   return forward(q, k, v, state_in, true, false, out, state_out, B, H, L, L > 0 ? L : 1, d,
+                 in_dt, out_dt, eps, nullptr, stream, &g);
+}
+
+int la_global_forward_rope(const void* q, const void* k, const void* v, void* out,
+                           float* state_out, int B, int H, int N, int d, int in_dt, int out_dt,
+                           float eps, int frame0, int grid_h, int grid_w, float theta,
+                           hipStream_t stream) {
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return forward(q, k, v, nullptr, false, false, out, state_out, B, H, N, N > 0 ? N : 1, d,
                  in_dt, out_dt, eps, nullptr, stream, &g);
 }
 

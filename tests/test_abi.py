@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 7
+    assert la.abi_version() == 8
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -264,6 +264,19 @@ def rope_bwd(q=A, k=2 * A, v=3 * A, sts=4 * A, do=5 * A, dsts=None, dq=6 * A, dk
 ])
 def test_rope_backward_rejects(kw, code, ex):
     assert rope_bwd(ex=ex, **kw) == code
+
+
+def test_rope_global_rejects():
+    L_ = la.lib()
+
+    def call(out=5 * A, so=6 * A, gh=4, N=640, d=64, f0=0):
+        return L_.la_global_forward_rope(A, 2 * A, 3 * A, out, so, 1, 2, N, d, BF16, F32, 1e-6,
+                                         f0, gh, 4, 10000.0, None)
+    assert call(so=None) == la.LA_E_INVAL
+    assert call(gh=0) == la.LA_E_INVAL
+    assert call(f0=1 << 22) == la.LA_E_INVAL
+    assert call(d=96) == la.LA_E_UNSUPPORTED
+    assert call(out=A) == la.LA_E_ALIAS
 
 
 def test_rope_chunk_backward_rejects():

@@ -100,6 +100,32 @@ def test_rope_global_form(dtype):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_global_call(dtype):
+    """la_global_forward_rope against the oracle, and bit for bit against the
+    block-causal call with one block (the same kernels)."""
+    B, H, N, d, gh, gw, f0 = 2, 2, 2500, 64, 7, 9, 3
+    Q, K, V = workloads.random_qkv(45, B, H, N, d, dtype=dtype)
+    O_ref, S_pre, z_pre = oracle.rope_prefix_forward(Q, K, V, [0, N], EPS, f0, gh, gw, THETA)
+    q, k, v = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    out, st = la.global_forward_rope(q, k, v, f0, gh, gw, THETA, eps=EPS)
+    out2, sts = la.blockcausal_forward_rope(q, k, v, N, f0, gh, gw, THETA, eps=EPS)
+    torch.cuda.synchronize()
+    eo = out_err(host(out), O_ref)
+    es, ez = state_err(host(st), S_pre[0], z_pre[0])
+    report(f"rope global call {dtype}", out=eo, S=es, z=ez)
+    assert max(eo, es, ez) <= TOL[dtype]
+    assert torch.equal(out, out2) and torch.equal(st, sts[:, :, 0])
+
+
+def test_rope_global_call_empty():
+    """N = 0: the state is zero."""
+    e = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device="cuda")
+    _, st = la.global_forward_rope(e, e, e, 0, 4, 4, THETA, eps=EPS)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st) == 0
+
+
 @pytest.mark.parametrize("f0", [4_000_000, -3_000_001])
 def test_rope_large_frame_offset(f0):
     """Tokens millions of frames into a stream (or before its origin, which
