@@ -3,7 +3,8 @@ its gradients equal the direct backward call's bit for bit, and the fp64
 oracle's chain rule (``oracle.blockcausal_backward``) within the backward
 bounds, for the global and the block-causal form, with and without a state
 input, and with a loss that also reads the returned states; the same for the
-rotary form against ``oracle.rope_blockcausal_backward``."""
+rotary form against ``oracle.rope_blockcausal_backward``; and two chained calls
+(the second reading the first's state) against the two-block sequence."""
 
 import numpy as np
 import pytest
@@ -140,3 +141,36 @@ def test_autograd_rope_equals_direct_backward_bf16():
     assert torch.equal(q.grad, dq.to(torch.bfloat16))
     assert torch.equal(k.grad, dk.to(torch.bfloat16))
     assert torch.equal(v.grad, dv.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_autograd_chained_calls_equal_one_sequence(rope):
+    """Streaming training: two calls, the second reading the state the first
+    returned, and one loss over both outputs.  Gradients reach the first
+    call's q, k, v through the carried state and equal the oracle's on the
+    two-block sequence."""
+    B, H, L, d, gh, gw = 1, 2, 400, 64, 4, 10
+    Q, K, V = workloads.random_qkv(541, B, H, 2 * L, d, dtype="f32")
+    dO = workloads.random_grads(542, B, H, 2 * L, d)
+    f1 = L // (gh * gw)  # the second chunk starts at frame 10
+    q1, k1, v1 = (dev(x[:, :, :L], "f32").requires_grad_() for x in (Q, K, V))
+    q2, k2, v2 = (dev(x[:, :, L:], "f32").requires_grad_() for x in (Q, K, V))
+    r1 = (0, gh, gw) if rope else None
+    r2 = (f1, gh, gw) if rope else None
+    o1, s1 = la.linear_attention(q1, k1, v1, eps=EPS, rope=r1)
+    o2, _ = la.linear_attention(q2, k2, v2, state_in=s1[:, :, -1], eps=EPS, rope=r2)
+    loss = (o1 * dev(dO[:, :, :L], "f32")).sum() + (o2 * dev(dO[:, :, L:], "f32")).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    if rope:
+        ref = oracle.rope_blockcausal_backward(Q, K, V, [0, L, 2 * L], dO, EPS, 0, gh, gw,
+                                               workloads.ROPE_THETA)
+    else:
+        ref = oracle.blockcausal_backward(Q, K, V, [0, L, 2 * L], dO, EPS)
+    errs = []
+    for (a, b), grads in (((0, L), (q1, k1, v1)), ((L, 2 * L), (q2, k2, v2))):
+        for g, r in zip(grads, ref[:3]):
+            errs.append(_err(host(g.grad), r[:, :, a:b]))
+    print(f"[parity] autograd chained rope={rope} " + " ".join(f"{e:.2e}" for e in errs),
+          flush=True)
+    assert max(errs) <= TOL["f32"], errs
