@@ -82,6 +82,8 @@ _SIGNATURES = {
                                _F, _P, _Z, _I, _I, _I, _F, _P],
     "la_global_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _Z,
                            _P],
+    "la_global_backward_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P,
+                                _Z, _I, _I, _I, _F, _P],
     "la_temporal_conv_chunk": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P],
     "la_temporal_conv_blockcausal": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P],
     "la_plan": [_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)],
@@ -521,6 +523,25 @@ def chunk_backward_rope(q, k, v, state_out, dout, frame0, grid_h, grid_w, theta=
         float(eps), _ptr(workspace), ws_bytes, int(frame0), int(grid_h), int(grid_w),
         float(theta), _stream(q.device)), "la_chunk_backward_rope")
     return dq, dk, dv, dstate_in
+
+
+def global_backward_rope(q, k, v, state, dout, frame0, grid_h, grid_w, theta=DEFAULT_THETA,
+                         eps=DEFAULT_EPS, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of global_forward_rope(q, k, v, frame0, grid_h, grid_w,
+    theta) -> (out, state) for the upstream gradient dout.  Returns
+    (dq, dk, dv)."""
+    dq, dk, dv = _prepare_grads(q, k, v, dout, dq, dk, dv)
+    B, H, N, d = q.shape
+    _state_like(state, (B, H, d * d + d), "state", q.device)
+    need = backward_workspace_size(B, H, N, N, d, q.dtype)
+    workspace = _workspace(workspace, need, q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().la_global_backward_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, N, d, _DTYPE[q.dtype], _DTYPE[dout.dtype], float(eps), _ptr(workspace), ws_bytes,
+        int(frame0), int(grid_h), int(grid_w), float(theta), _stream(q.device)),
+        "la_global_backward_rope")
+    return dq, dk, dv
 
 
 def global_backward(q, k, v, state, dout, eps=DEFAULT_EPS, dq=None, dk=None, dv=None,

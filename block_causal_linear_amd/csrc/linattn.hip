@@ -22,7 +22,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -992,6 +992,16 @@ int la_chunk_backward_rope(const void* q, const void* k, const void* v, const fl
   return backward(q, k, v, state_out, dout, dstate_out, dq, dk, dv, dstate_in, B, H, L,
                   L > 0 ? L : 1, d, in_dt, grad_dt, eps, workspace, workspace_bytes, L == 0,
                   nullptr, stream, &g);
+}
+
+int la_global_backward_rope(const void* q, const void* k, const void* v, const float* state,
+                            const void* dout, void* dq, void* dk, void* dv, int B, int H, int N,
+                            int d, int in_dt, int grad_dt, float eps, void* workspace,
+                            size_t workspace_bytes, int frame0, int grid_h, int grid_w,
+                            float theta, hipStream_t stream) {
+  const la::RopeGrid g = rope_grid(frame0, grid_h, grid_w, theta);
+  return backward(q, k, v, state, dout, nullptr, dq, dk, dv, nullptr, B, H, N, N > 0 ? N : 1, d,
+                  in_dt, grad_dt, eps, workspace, workspace_bytes, false, nullptr, stream, &g);
 }
 
 int la_global_backward(const void* q, const void* k, const void* v, const float* state,

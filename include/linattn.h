@@ -367,6 +367,15 @@ int la_chunk_backward_rope(const void* q, const void* k, const void* v, const fl
                            int grad_dt, float eps, void* workspace, size_t workspace_bytes,
                            int frame0, int grid_h, int grid_w, float theta, hipStream_t stream);
 
+/* la_global_backward_rope - gradients of la_global_forward_rope, as
+ * la_global_backward is of la_global_forward (state: the forward's
+ * state_out; no state gradient). */
+int la_global_backward_rope(const void* q, const void* k, const void* v, const float* state,
+                            const void* dout, void* dq, void* dk, void* dv, int B, int H, int N,
+                            int d, int in_dt, int grad_dt, float eps, void* workspace,
+                            size_t workspace_bytes, int frame0, int grid_h, int grid_w,
+                            float theta, hipStream_t stream);
+
 /*
  * Temporal convolution of the Spatial-Temporal Mix-FFN with its
  * chunk-boundary cache ([TR] section "Verimli doğrusal DiT": the MLP

@@ -30,7 +30,7 @@ int main(void) {
   la_launch_opts opts;
   memset(&opts, 0, sizeof opts);
 
-  expect("abi version", la_abi_version(), 8);
+  expect("abi version", la_abi_version(), 9);
   expect("status string", strcmp(la_status_string(LA_E_ALIAS), "illegal buffer overlap"), 0);
   expect("chunk d=48", la_chunk_forward(A, B, C, S, O, S2, 1, 2, 64, 48, LA_BF16, LA_F32, 1e-6f, 0),
          LA_E_UNSUPPORTED);

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 8
+    assert la.abi_version() == 9
     for code in range(6):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -277,6 +277,18 @@ def test_rope_global_rejects():
     assert call(f0=1 << 22) == la.LA_E_INVAL
     assert call(d=96) == la.LA_E_UNSUPPORTED
     assert call(out=A) == la.LA_E_ALIAS
+
+
+def test_rope_global_backward_rejects():
+    L_ = la.lib()
+
+    def call(st=4 * A, gh=4, N=640, d=64):
+        return L_.la_global_backward_rope(A, 2 * A, 3 * A, st, 5 * A, 6 * A, 7 * A, 8 * A, 1, 2,
+                                          N, d, BF16, F32, 1e-6, 9 * A, 1 << 20, 0, gh, 4,
+                                          10000.0, None)
+    assert call(st=None) == la.LA_E_INVAL
+    assert call(gh=-1) == la.LA_E_INVAL
+    assert call(d=48) == la.LA_E_UNSUPPORTED
 
 
 def test_rope_chunk_backward_rejects():

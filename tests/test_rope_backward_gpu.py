@@ -330,3 +330,18 @@ def test_rope_chunk_backward_empty_passes_state_gradient():
                                           eps=EPS)
     torch.cuda.synchronize()
     assert torch.equal(dsi, dso)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rope_global_backward(dtype):
+    """la_global_backward_rope against the oracle (one block, no state)."""
+    B, H, N, d, gh, gw, f0 = 1, 3, 2000, 64, 5, 9, 2
+    Q, K, V = workloads.random_qkv(171, B, H, N, d, dtype=dtype)
+    dO = workloads.random_grads(172, B, H, N, d)
+    q, k, v = dev(Q, dtype), dev(K, dtype), dev(V, dtype)
+    _, st = la.global_forward_rope(q, k, v, f0, gh, gw, THETA, eps=EPS)
+    dq, dk, dv = la.global_backward_rope(q, k, v, st, dev(dO, "f32"), f0, gh, gw, THETA, eps=EPS)
+    torch.cuda.synchronize()
+    ref = oracle.rope_blockcausal_backward(Q, K, V, [0, N], dO, EPS, f0, gh, gw, THETA)
+    check(f"rope global backward {dtype}", [host(dq), host(dk), host(dv)], ref[:3], [0, N],
+          TOL[dtype])
