@@ -112,15 +112,16 @@ __device__ float2 rope_freq(int m, float theta) {
 }
 
 // p * f in turns reduced to [0, 1) (plus a correction of a few ulp of the
-// product): the fractional part of the rounded product is exact, and the
+// product): the fractional part of the rounded product is exact
+// (`v_fract_f32`: h - floor(h), one instruction, clamped below 1.0), and the
 // product's rounding error and the lo part are added after it.  Contraction
-// is off here: fusing p * f.x into h - floor(h) would add the rounding error
+// is off here: fusing p * f.x into the reduction would add the rounding error
 // twice (0.03 turns at frame 4,000,000).
 __device__ __forceinline__ float rope_turns(float p, float2 f) {
 #pragma clang fp contract(off)
   const float h = p * f.x;
   const float e = fmaf(p, f.x, -h);
-  return (h - floorf(h)) + fmaf(p, f.y, e);
+  return __builtin_amdgcn_fractf(h) + fmaf(p, f.y, e);
 }
 
 template <bool PRECISE>
