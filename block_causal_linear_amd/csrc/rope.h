@@ -34,6 +34,15 @@
 
 namespace la {
 
+// Waves per SIMD kv_partial_rope_bf16 is built for.  Its LDS (48 KB a
+// workgroup at d = 64) allows three workgroups per CU, so at d = 64 the
+// bound says so: without it the compiler kept the accumulators in AGPRs and
+// moved them every tile (32 v_accvgpr moves per two tiles).
+template <int D>
+constexpr int kv_rope_min_waves() {
+  return D == 64 ? 3 : 1;
+}
+
 // ---------------------------------------------------------------------------
 // KV reduction with rotated keys (bfloat16 inputs).  The tiling, grid and
 // partial layout are those of kv_partial_bf16; what changes is the staging
@@ -43,7 +52,7 @@ namespace la {
 // sums eight features; the partial sums meet in LDS at the end and are
 // added in a fixed order).
 template <int D>
-__global__ __launch_bounds__(kv_threads<D>()) void kv_partial_rope_bf16(
+__global__ __launch_bounds__(kv_threads<D>(), kv_rope_min_waves<D>()) void kv_partial_rope_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int TB, int splits,
     int tps, const float* state_in, float* dst, RopeGrid rg) {
   constexpr int WR = KvWaves<D>::WR, WC = KvWaves<D>::WC;
