@@ -59,6 +59,16 @@ constexpr int kv_threads() {
   return KvTile<D, KvWaves<D>::WR, KvWaves<D>::WC>::NT;
 }
 
+// Waves per SIMD kv_partial_bf16 is built for (its launch bound).  Without a
+// bound the compiler kept the MFMA accumulators in AGPRs at d <= 64 and moved
+// them every tile (32 v_accvgpr moves per loop iteration at d = 64, whose
+// loop body has 118 VALU instructions); with it they stay in VGPRs (88 at
+// d = 64, five waves per SIMD instead of four).
+template <int D>
+constexpr int kv_min_waves() {
+  return D == 128 ? 1 : D == 64 ? 4 : 8;
+}
+
 template <int UPR>
 __device__ __forceinline__ int unit_swizzle(int t) {
   return ((t & 3) * 2) & (UPR - 1);
@@ -100,7 +110,7 @@ __device__ __forceinline__ uint4 tile_column8(const uint16_t* tile, int ks, int 
 // single block and a single split, dst is the state itself and state_in (if
 // any) is added.
 template <int D>
-__global__ __launch_bounds__(kv_threads<D>()) void kv_partial_bf16(
+__global__ __launch_bounds__(kv_threads<D>(), kv_min_waves<D>()) void kv_partial_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int TB, int splits,
     int tps, const float* state_in, float* dst) {
   constexpr int WR = KvWaves<D>::WR, WC = KvWaves<D>::WC;

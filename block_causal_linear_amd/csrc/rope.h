@@ -35,12 +35,13 @@
 namespace la {
 
 // Waves per SIMD kv_partial_rope_bf16 is built for.  Its LDS (48 KB a
-// workgroup at d = 64) allows three workgroups per CU, so at d = 64 the
-// bound says so: without it the compiler kept the accumulators in AGPRs and
-// moved them every tile (32 v_accvgpr moves per two tiles).
+// workgroup at d = 64, 24 KB at d = 32) allows three (six) workgroups per
+// CU, and the bound says so: without it the compiler kept the accumulators
+// in AGPRs and moved them every tile (32 v_accvgpr moves per two tiles at
+// d = 64).
 template <int D>
 constexpr int kv_rope_min_waves() {
-  return D == 64 ? 3 : 1;
+  return D == 128 ? 1 : D == 64 ? 3 : 6;
 }
 
 // ---------------------------------------------------------------------------
