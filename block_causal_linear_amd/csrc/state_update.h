@@ -96,24 +96,35 @@ __global__ __launch_bounds__(kBlock) void state_scan(const float4* partials,
   float4 run = state_in != nullptr ? state_in[bh * n4 + e] : make_float4(0.f, 0.f, 0.f, 0.f);
   const float4* p = partials + bh * static_cast<size_t>(nblk) * splits * n4 + e;
   float4* out = states + bh * static_cast<size_t>(nblk) * n4 + e;
-  constexpr int U = 4;
-  for (int c0 = 0; c0 < nblk; c0 += U) {
-    float4 kv[U];
+  // The (block, split) partials of this element, block-major: taken in
+  // batches of Q independent loads (latency, not bandwidth, bounds this
+  // kernel), then added in order; a block's sum joins the running state
+  // after its last split.  Every load of a batch precedes the stores of the
+  // batch (partials may be states itself).
+  constexpr int Q = 16;
+  const int total = nblk * splits;
+  float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sc = 0, c = 0;
+  for (int t0 = 0; t0 < total; t0 += Q) {
+    float4 x[Q];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      kv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c0 + u < nblk)
-        for (int s = 0; s < splits; ++s)
-          add(kv[u], p[(static_cast<size_t>(c0 + u) * splits + s) * n4]);
-    }
+    for (int j = 0; j < Q; ++j)
+      x[j] = t0 + j < total ? p[static_cast<size_t>(t0 + j) * n4] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (c0 + u >= nblk) break;
-      run.x = run.x + kv[u].x;
-      run.y = run.y + kv[u].y;
-      run.z = run.z + kv[u].z;
-      run.w = run.w + kv[u].w;
-      out[static_cast<size_t>(c0 + u) * n4] = run;
+    for (int j = 0; j < Q; ++j) {
+      if (t0 + j < total) {
+        add(kv, x[j]);
+        if (++sc == splits) {
+          run.x = run.x + kv.x;
+          run.y = run.y + kv.y;
+          run.z = run.z + kv.z;
+          run.w = run.w + kv.w;
+          out[static_cast<size_t>(c) * n4] = run;
+          kv = make_float4(0.f, 0.f, 0.f, 0.f);
+          sc = 0;
+          ++c;
+        }
+      }
     }
   }
 }
@@ -143,13 +154,47 @@ __global__ __launch_bounds__(kBlock) void state_suffix_scan(const float4* partia
   const float4* p = partials + bh * static_cast<size_t>(nblk) * splits * n4 + e;
   const float4* ds = dS != nullptr ? dS + bh * static_cast<size_t>(nblk) * n4 + e : nullptr;
   float4* out = R + bh * static_cast<size_t>(nblk) * n4 + e;
-  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c = nblk - 1; c >= 0; --c) {
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < splits; ++s) add(x, p[(static_cast<size_t>(c) * splits + s) * n4]);
-    if (ds != nullptr) add(x, ds[static_cast<size_t>(c) * n4]);
-    add(run, x);
-    out[static_cast<size_t>(c) * n4] = run;
+  // Blocks from the last to the first, each block's splits in order: taken
+  // in batches of Q independent loads (with the state gradient of every
+  // block a batch closes), then added in that order.  Every load of a batch
+  // precedes the stores of the batch (partials may be R itself).
+  constexpr int Q = 16;
+  const int total = nblk * splits;
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 run = zero, x = zero;
+  int sc = 0, c = nblk - 1;
+  for (int k0 = 0; k0 < total; k0 += Q) {
+    float4 v[Q], g[Q];
+    // k = k0 + j is split (k mod splits) of block nblk - 1 - k / splits
+    int cj = c, sj = sc;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const bool in = k0 + j < total;
+      // (a temporary, not `zero`, on the right: a conditional of two lvalues
+      // would select between a global and a private address)
+      v[j] = in ? p[(static_cast<size_t>(cj) * splits + sj) * n4]
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+      g[j] = in && ds != nullptr && sj == splits - 1 ? ds[static_cast<size_t>(cj) * n4]
+                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (++sj == splits) {
+        sj = 0;
+        --cj;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      if (k0 + j < total) {
+        add(x, v[j]);
+        if (++sc == splits) {
+          if (ds != nullptr) add(x, g[j]);
+          add(run, x);
+          out[static_cast<size_t>(c) * n4] = run;
+          x = zero;
+          sc = 0;
+          --c;
+        }
+      }
+    }
   }
   if (d_in != nullptr) d_in[bh * n4 + e] = run;
 }
