@@ -227,6 +227,12 @@ int la_blockcausal_forward_rope(const void* q, const void* k, const void* v,
                                 float eps, int frame0, int grid_h, int grid_w, float theta,
                                 hipStream_t stream);
 
+int la_blockcausal_forward_rope_ex(const void* q, const void* k, const void* v,
+                                   const float* state_in, void* out, float* states,
+                                   int B, int H, int N, int T, int d, int in_dt, int out_dt,
+                                   float eps, int frame0, int grid_h, int grid_w, float theta,
+                                   const la_launch_opts* opts, hipStream_t stream);
+
 /* la_global_forward_rope - the global form with the rotation: as
  * la_global_forward (one block of all N tokens, no state input; state_out
  * receives S with every key turned by its position, and z), token 0 at
@@ -235,12 +241,6 @@ int la_global_forward_rope(const void* q, const void* k, const void* v, void* ou
                            float* state_out, int B, int H, int N, int d, int in_dt, int out_dt,
                            float eps, int frame0, int grid_h, int grid_w, float theta,
                            hipStream_t stream);
-
-int la_blockcausal_forward_rope_ex(const void* q, const void* k, const void* v,
-                                   const float* state_in, void* out, float* states,
-                                   int B, int H, int N, int T, int d, int in_dt, int out_dt,
-                                   float eps, int frame0, int grid_h, int grid_w, float theta,
-                                   const la_launch_opts* opts, hipStream_t stream);
 
 /*
  * Gradients (training uses the same attention: [EN] abstract; [TR] trains
