@@ -700,7 +700,7 @@ def _hiplib():
     global _hip
     if _hip is None:
         h = ctypes.CDLL("libamdhip64.so")
-        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         h.hipEventDestroy.argtypes = [ctypes.c_void_p]
         h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -708,6 +708,12 @@ def _hiplib():
         h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         _hip = h
     return _hip
+
+
+# hipEventDisableSystemFence from HIP's runtime header: the event takes its time stamp without
+# the system-scope cache write-back and invalidate of a default event, which would otherwise
+# lengthen the interval of the kernel after it.  These events only time; they order nothing.
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
 class StageEvents:
@@ -719,8 +725,8 @@ class StageEvents:
         self._arr = (ctypes.c_void_p * 4)()
         for i in range(4):
             ev = ctypes.c_void_p()
-            if h.hipEventCreate(ctypes.byref(ev)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if h.hipEventCreateWithFlags(ctypes.byref(ev), _HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self._arr[i] = ev.value
 
     def as_ctypes(self):
