@@ -194,7 +194,7 @@ def test_backward_480p_one_call():
 
 
 def test_backward_long_horizon_d128_one_call():
-    """Config 5 (B=4, H=16, d=128, 40 blocks of 4,096 tokens, 1% outlier
+    """The long-horizon stream (B=4, H=16, d=128, 40 blocks of 4,096 tokens, 1% outlier
     rows) in one call.  The oracle is composed block by block from its own
     steps (readout_backward per block, suffix sums, kv_backward), so the
     fp64 tensors never exist whole; dQ of every block and dK, dV of every

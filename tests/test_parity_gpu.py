@@ -81,7 +81,7 @@ def test_global_small(dtype, d):
 # the five workloads at full size
 
 
-def test_config1_tiny_f32_stream():
+def test_tiny_f32_stream_4x64():
     w = workloads.WORKLOADS[1]
     state = la.new_state(w.B, w.H, w.d)
     blocks = [workloads.chunk_qkv(w, n) for n in range(w.chunks)]
@@ -92,7 +92,7 @@ def test_config1_tiny_f32_stream():
         torch.cuda.synchronize()
         eo = out_err(host(out), outs[n])
         es, ez = state_err(host(state), *states[n])
-        report(f"config1 chunk {n}", out=eo, S=es, z=ez)
+        report(f"tiny f32 stream chunk {n}", out=eo, S=es, z=ez)
         assert eo <= TOL["f32"] and es <= TOL["f32"] and ez <= TOL["f32"]
 
 
