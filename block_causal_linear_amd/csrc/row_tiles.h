@@ -127,17 +127,32 @@ __device__ __forceinline__ float row16_sum(float t) {
   return t;
 }
 
-// Stores of gradient rows go through a raw buffer descriptor that covers the
-// valid rows of one tile only: the hardware drops stores past num_records, so
-// the rows past the end of a block need no branch (a branch around stores
-// makes the compiler wait for every outstanding load, prefetches included).
+// Rows of a tile are stored (and, where a kernel says so, loaded) through a
+// raw buffer descriptor that covers the tile's valid rows only: the hardware
+// drops stores past num_records and returns zero for loads past it, so the
+// rows past the end of a block need no branch (a branch around stores makes
+// the compiler wait for every outstanding load, prefetches included).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-__device__ __forceinline__ rsrc_t tile_rsrc(void* base, size_t elem_off, int elem_size,
+// Cache-policy bit 1 of a buffer access: non-temporal (data used once).
+constexpr int kBufNt = 2;
+
+// The descriptor of `bytes` bytes from element `elem_off` of `base`.  The
+// base, offset and size must be the same in every lane of the wave: they are
+// taken through readfirstlane so that the descriptor stays in scalar
+// registers.  Built inside a loop without it, the compiler could carry the
+// descriptor in vector registers and wrap every access in a loop over its
+// distinct values (four readfirstlanes, two compares and two exec-mask
+// switches per access, even when all lanes agree).
+__device__ __forceinline__ rsrc_t tile_rsrc(const void* base, size_t elem_off, int elem_size,
                                             int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base) + elem_off * elem_size;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
   // word 3: 32-bit data format, as raw (untyped) buffer accesses expect
-  return __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(base) + elem_off * elem_size, 0,
-                                           bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, __builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
 }
 
 // W values at byte offset `off` of a tile descriptor (float32 or bfloat16).
@@ -146,7 +161,7 @@ __device__ __forceinline__ rsrc_t tile_rsrc(void* base, size_t elem_off, int ele
 // lines that drain during whatever kernel runs next.
 template <int W, bool BF16, bool NT>
 __device__ __forceinline__ void store_row_buf(rsrc_t r, int off, const float (&x)[W]) {
-  constexpr int AUX = NT ? 2 : 0;  // cache-policy bit 1: nt
+  constexpr int AUX = NT ? kBufNt : 0;
   if constexpr (BF16) {
     if constexpr (W == 4) {
       __builtin_amdgcn_raw_buffer_store_b64(
