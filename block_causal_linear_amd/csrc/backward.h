@@ -478,7 +478,11 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
 #pragma unroll
           for (int e = 0; e < W; ++e) {
             const int nb = gr * W + e;
-            xk[e] = kacc[nb][i] > 0.f ? acck[nb][i] + rsh[col + e] : 0.f;
+            // r read outside the select: with the LDS read inside one arm
+            // the compiler branched around it (an exec-mask switch per value)
+            const float r = rsh[col + e];
+            const float gk = acck[nb][i] + r;
+            xk[e] = kacc[nb][i] > 0.f ? gk : 0.f;
             xv[e] = accv[nb][i];
           }
           // non-temporal: by itself this kernel measures slower with it at

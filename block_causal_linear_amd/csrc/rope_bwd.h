@@ -407,8 +407,11 @@ __global__ __launch_bounds__(256, bwd_key_rope_min_waves<D>()) void bwd_key_rope
             const int m = (col + e) / 2;  // the feature pair (col + e, col + e + 1)
             float x = acck[nb][i], y = acck[nb + 1][i];
             rope_turn_back<false>(rope_turns(rope_axis_pos<D>(pc, m), ftab[m]), x, y);
-            xk[e] = kacc[nb][i] > 0.f ? x + rsh[col + e] : 0.f;
-            xk[e + 1] = kacc[nb + 1][i] > 0.f ? y + rsh[col + e + 1] : 0.f;
+            // the LDS reads outside the selects (inside, the compiler
+            // branched around them)
+            const float gx = x + rsh[col + e], gy = y + rsh[col + e + 1];
+            xk[e] = kacc[nb][i] > 0.f ? gx : 0.f;
+            xk[e + 1] = kacc[nb + 1][i] > 0.f ? gy : 0.f;
             xv[e] = accv[nb][i];
             xv[e + 1] = accv[nb + 1][i];
           }
