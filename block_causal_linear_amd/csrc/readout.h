@@ -60,15 +60,6 @@ struct ReadoutShape {
   static constexpr int UPR = D / 8;              // 16-byte units per query row
 };
 
-template <typename T>
-__device__ __forceinline__ void store_out(T v, T* p) {
-#if LA_READOUT_STREAM_STORES
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
-}
-
 __device__ __forceinline__ uint4 load_q(const uint4* p) {
 #if LA_READOUT_STREAM_LOADS
   return load_stream(p);
@@ -115,6 +106,7 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
   constexpr int E = D * D + D;
   constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, R = Sh::R;
   constexpr int NW = Sw::NW, CB = Sw::CB;
+  static_assert(CB == W, "a lane stores W consecutive columns, one from each column block");
   constexpr int NF = KS * (NBK + 1) * 2;  // operands: [k-step][column block, z last][hi, lo]
   constexpr int PAIRS = KS * NBK;         // (k-step, column block) pairs
   constexpr int PW = PAIRS >= NW ? PAIRS / NW : 1;  // pairs per wave
@@ -213,34 +205,23 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
         }
       }
     }
+    // Rows go out through a descriptor that covers the tile's rows inside the
+    // block: the hardware drops the stores past te, so no lane branches (a
+    // per-row branch cost an exec-mask switch around every store).
+    constexpr int OE = OUT_BF16 ? 2 : 4;
+    const int valid = max(0, min(Sh::TILE, te - t0));
+    const rsrc_t ro = tile_rsrc(out, (static_cast<size_t>(bh) * N + t0) * D, OE, valid * D * OE);
+    const int col = 16 * W * (ch * CB / W) + W * n;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * r + 4 * i + g;
-        if (tok >= te) continue;
+        const int tt = 16 * r + 4 * i + g;  // row within the wave's tile
         const float inv = fast_rcp(accz[r][i] + eps);
-        const size_t row0 = (static_cast<size_t>(bh) * N + tok) * D;
-        const int col = 16 * W * (ch * CB / W) + W * n;
-        if constexpr (W == 4) {
-          const float o0 = acc[r][0][i] * inv, o1 = acc[r][1][i] * inv;
-          const float o2 = acc[r][2][i] * inv, o3 = acc[r][3][i] * inv;
-          if constexpr (OUT_BF16) {
-            const u32x2 pk = {pack2(to_bf16(o0), to_bf16(o1)), pack2(to_bf16(o2), to_bf16(o3))};
-            store_out(pk, reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + row0 + col));
-          } else {
-            store_out(f32x4{o0, o1, o2, o3},
-                      reinterpret_cast<f32x4*>(static_cast<float*>(out) + row0 + col));
-          }
-        } else {
-          const float o0 = acc[r][0][i] * inv, o1 = acc[r][1][i] * inv;
-          if constexpr (OUT_BF16) {
-            store_out(pack2(to_bf16(o0), to_bf16(o1)),
-                      reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + row0 + col));
-          } else {
-            store_out(f32x2{o0, o1}, reinterpret_cast<f32x2*>(static_cast<float*>(out) + row0 + col));
-          }
-        }
+        float o[W];
+#pragma unroll
+        for (int e = 0; e < W; ++e) o[e] = acc[r][e][i] * inv;
+        store_row_buf<W, OUT_BF16, LA_READOUT_STREAM_STORES != 0>(ro, (tt * D + col) * OE, o);
       }
   };
 
