@@ -13,6 +13,7 @@
 #pragma once
 
 #include "la_common.h"
+#include "row_tiles.h"
 
 namespace la {
 
@@ -150,20 +151,21 @@ __global__ __launch_bounds__(kv_threads<D>(), kv_min_waves<D>()) void kv_partial
   // Two register stages: while tile i is in LDS and being multiplied, the
   // loads of tiles i + 1 and i + 2 are in flight.
   uint4 rk0[T::CPT], rv0[T::CPT], rk1[T::CPT], rv1[T::CPT];
+  // K and V through descriptors that cover the tile's rows inside the split:
+  // rows past t1 read as zero in hardware, so no load needs a branch.
   auto gload = [&](uint4 (&rk)[T::CPT], uint4 (&rv)[T::CPT], int tile) {
     const int base = t0 + tile * T::TT;
+    const int bytes = (min(t1, base + T::TT) - base) * T::UPR * 16;
+    const size_t first = static_cast<size_t>(base) * T::UPR;
+    const rsrc_t ksrc = tile_rsrc(kb, first, 16, bytes);
+    const rsrc_t vsrc = tile_rsrc(vb, first, 16, bytes);
 #pragma unroll
     for (int i = 0; i < T::CPT; ++i) {
-      const int u = tid + T::NT * i;
-      const int t = u / T::UPR;
-      if (base + t < t1) {
-        const size_t idx = static_cast<size_t>(base) * T::UPR + u;
-        rk[i] = load_stream(kb + idx);
-        rv[i] = load_stream(vb + idx);
-      } else {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int off = (tid + T::NT * i) * 16;
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(ksrc, off, 0, kBufNt);
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(vsrc, off, 0, kBufNt);
+      rk[i] = make_uint4(a.x, a.y, a.z, a.w);
+      rv[i] = make_uint4(b.x, b.y, b.z, b.w);
     }
   };
   auto lstore = [&](const uint4 (&rk)[T::CPT], const uint4 (&rv)[T::CPT], int buf) {
