@@ -1,4 +1,5 @@
-"""Builds liblinattn.so in-tree for gfx950 with hipcc.
+"""Builds liblinattn.so (the library) and libla_probes.so (the benchmark's
+HBM stream probes) in-tree for gfx950 with hipcc.
 
     python -m block_causal_linear_amd.build
 """
@@ -14,6 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "liblinattn.so")
 SOURCES = [os.path.join(CSRC, "linattn.hip")]
+PROBE_LIB_PATH = os.path.join(HERE, "libla_probes.so")
+PROBE_SOURCES = [os.path.join(CSRC, "probes.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -35,8 +38,14 @@ def hipcc():
 
 
 def build(verbose=False, extra_flags=()):
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
+    """Builds both libraries; returns the attention library's path."""
+    _build_one(PROBE_LIB_PATH, PROBE_SOURCES, verbose, extra_flags)
+    return _build_one(LIB_PATH, SOURCES, verbose, extra_flags)
+
+
+def _build_one(lib_path, sources, verbose, extra_flags):
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,8 +58,8 @@ def build(verbose=False, extra_flags=()):
         lines = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
         if lines:
             print("\n".join(lines))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
