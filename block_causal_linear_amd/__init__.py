@@ -22,7 +22,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
-LA_OK, LA_E_INVAL, LA_E_UNSUPPORTED, LA_E_ALIGN, LA_E_ALIAS, LA_E_HIP = range(6)
+LA_OK, LA_E_INVAL, LA_E_UNSUPPORTED, LA_E_ALIGN, LA_E_ALIAS, LA_E_HIP, LA_E_SCRATCH = range(7)
+# static device scratch of la_blockcausal_backward_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 LA_F32, LA_BF16 = 0, 1
 DEFAULT_EPS = 1e-6
 DEFAULT_THETA = 10000.0
@@ -71,6 +73,8 @@ _SIGNATURES = {
                                 _I, _I, _F, _P, _Z, _P],
     "la_blockcausal_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                    _I, _I, _I, _F, _P, _Z, ctypes.POINTER(LaunchOpts), _P],
+    "la_blockcausal_backward_noalloc": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I,
+                                        _I, _I, _I, _I, _F, _P],
     "la_blockcausal_backward_rope": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                      _I, _I, _F, _P, _Z, _I, _I, _I, _F, _P],
     "la_blockcausal_backward_rope_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -433,6 +437,33 @@ def blockcausal_backward(q, k, v, states, dout, T, dstates=None, want_dstate_in=
     else:
         rc = L_.la_blockcausal_backward_ex(*args, ctypes.byref(o), _stream(q.device))
     _check(rc, "la_blockcausal_backward")
+    return dq, dk, dv, dstate_in
+
+
+def blockcausal_backward_noalloc(q, k, v, states, dout, T, dstates=None, want_dstate_in=False,
+                                 eps=DEFAULT_EPS, dq=None, dk=None, dv=None, dstate_in=None):
+    """blockcausal_backward through la_blockcausal_backward_noalloc: the
+    library's static device scratch instead of a workspace (the library
+    allocates nothing; pass dq, dk, dv (and dstate_in) to allocate nothing
+    here either).  Calls that overlap in time on one GPU race."""
+    dq, dk, dv = _prepare_grads(q, k, v, dout, dq, dk, dv)
+    B, H, N, d = q.shape
+    T = int(T)
+    if T < 1:
+        raise ValueError("T must be >= 1")
+    C = -(-N // T) if N > 0 else 0
+    _state_like(states, (B, H, C, d * d + d), "states", q.device)
+    if dstates is not None:
+        _state_like(dstates, (B, H, C, d * d + d), "dstates", q.device)
+    if want_dstate_in and dstate_in is None:
+        dstate_in = torch.empty((B, H, d * d + d), dtype=torch.float32, device=q.device)
+    if dstate_in is not None:
+        _state_like(dstate_in, (B, H, d * d + d), "dstate_in", q.device)
+    rc = lib().la_blockcausal_backward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(states), _ptr(dout), _ptr(dstates), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dstate_in), B, H, N, T, d, _DTYPE[q.dtype], _DTYPE[dout.dtype], float(eps),
+        _stream(q.device))
+    _check(rc, "la_blockcausal_backward_noalloc")
     return dq, dk, dv, dstate_in
 
 

@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "linattn.h"
 #include "la_common.h"
@@ -20,9 +21,46 @@
 #include "rope.h"
 #include "rope_bwd.h"
 
+// Device scratch of the allocation-free backward entry point
+// (la_blockcausal_backward_noalloc): a fixed array in the code object, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never passes `scratch` itself to a kernel (on the host the name is only a
+// stand-in for the symbol): it takes each device's address once, through
+// hipGetSymbolAddress with that device current, and passes that pointer.
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
+
+// The address of `scratch` on the device of `stream` (the current device for
+// the null stream), looked up on that device's first call and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return LA_E_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return LA_E_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return LA_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return LA_E_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return LA_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return LA_E_HIP;
+    if (e != hipSuccess || p == nullptr) return LA_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LA_OK;
+}
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
 // MI355X at d <= 64 (four waves each; measured best at the 720p chunk: 16
@@ -632,7 +670,8 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
              const float* dstates, void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
              int N, int T, int d, int in_dt, int grad_dt, float eps, void* workspace,
              size_t workspace_bytes, bool empty_block, const la_launch_opts* opts,
-             hipStream_t stream, const la::RopeGrid* rope = nullptr) {
+             hipStream_t stream, const la::RopeGrid* rope = nullptr,
+             bool static_scratch = false) {
   int rc = check_shape(B, H, N, d, in_dt, grad_dt);
   if (rc != LA_OK) return rc;
   if (T <= 0) return LA_E_INVAL;
@@ -650,6 +689,12 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
   const int nblk = N == 0 ? (empty_block ? 1 : 0) : (N + (T < N ? T : N) - 1) / (T < N ? T : N);
   const size_t bh = static_cast<size_t>(B) * H;
   const size_t st = (static_cast<size_t>(d) * d + d) * sizeof(float);
+  // static_scratch: the workspace is this device's `scratch` (the caller
+  // passes none); the plan fits its split count to that array
+  if (static_scratch) {
+    if (workspace != nullptr || workspace_bytes != 0) return LA_E_INVAL;
+    workspace_bytes = LA_NOALLOC_SCRATCH_BYTES;
+  }
   const size_t in_bytes = bh * N * d * elem_size(in_dt);
   const size_t g_bytes = bh * N * d * elem_size(grad_dt);
   BwdPlan p = empty_block
@@ -661,7 +706,11 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
     p.T = 1;  // one block of no tokens: every workgroup's range is empty
   }
   const size_t need = nblk == 0 ? 0 : p.ws_bytes;
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LA_E_INVAL;
+  if (static_scratch) {
+    if (need > LA_NOALLOC_SCRATCH_BYTES) return LA_E_SCRATCH;
+  } else if (need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return LA_E_INVAL;
+  }
 
   // outputs against inputs and against each other
   struct Buf {
@@ -690,6 +739,7 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
     }
     return LA_OK;
   }
+  if (static_scratch && (rc = device_scratch(stream, &workspace)) != LA_OK) return rc;
   const bool gb = grad_dt == LA_BF16;
 #define LA_RUN_BWD(DD)                                                                          \
   return gb ? run_bwd<DD, true>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, \
@@ -972,6 +1022,15 @@ int la_blockcausal_backward_ex(const void* q, const void* k, const void* v, cons
                   grad_dt, eps, workspace, workspace_bytes, false, opts, stream);
 }
 
+int la_blockcausal_backward_noalloc(const void* q, const void* k, const void* v,
+                                    const float* states, const void* dout, const float* dstates,
+                                    void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
+                                    int N, int T, int d, int in_dt, int grad_dt, float eps,
+                                    hipStream_t stream) {
+  return backward(q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, N, T, d, in_dt,
+                  grad_dt, eps, nullptr, 0, false, nullptr, stream, nullptr, true);
+}
+
 int la_chunk_backward(const void* q, const void* k, const void* v, const float* state_out,
                       const void* dout, const float* dstate_out, void* dq, void* dk, void* dv,
                       float* dstate_in, int B, int H, int L, int d, int in_dt, int grad_dt,
@@ -1056,6 +1115,7 @@ const char* la_status_string(int status) {
     case LA_E_ALIGN: return "pointer not 16-byte aligned";
     case LA_E_ALIAS: return "illegal buffer overlap";
     case LA_E_HIP: return "HIP launch error";
+    case LA_E_SCRATCH: return "needs more scratch than the static device buffer holds";
     default: return "unknown status";
   }
 }

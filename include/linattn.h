@@ -53,6 +53,8 @@
  *   LA_E_ALIAS        `out` overlaps an input or a state, or state_out overlaps
  *                     q/k/v/out, or state_out partially overlaps state_in
  *   LA_E_HIP          a kernel launch failed (hipGetLastError after launch)
+ *   LA_E_SCRATCH      the allocation-free backward call needs more device
+ *                     scratch than its static buffer holds
  * Faults inside kernels surface at the caller's next synchronisation.
  * Calls are thread-safe; calls on different streams may run concurrently
  * as long as their buffers are disjoint.
@@ -73,6 +75,7 @@ extern "C" {
 #define LA_E_ALIGN 3
 #define LA_E_ALIAS 4
 #define LA_E_HIP 5
+#define LA_E_SCRATCH 6
 
 #define LA_F32 0
 #define LA_BF16 1
@@ -299,6 +302,29 @@ int la_blockcausal_backward_ex(const void* q, const void* k, const void* v, cons
                                int in_dt, int grad_dt, float eps, void* workspace,
                                size_t workspace_bytes, const la_launch_opts* opts,
                                hipStream_t stream);
+
+/*
+ * la_blockcausal_backward_noalloc - la_blockcausal_backward for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels and results.  Its workspace is a static device
+ * array of LA_NOALLOC_SCRATCH_BYTES (32 MiB) in the library's code object,
+ * one per GPU, held until the process ends; the call allocates nothing and
+ * fits the query-gradient split count to that size.  A call whose smallest
+ * plan needs more (the suffix states alone, B*H*ceil(N/T)*(d*d+d)*4 bytes,
+ * exceed it) returns LA_E_SCRATCH and enqueues nothing.  The array keeps the
+ * last call's contents; every byte a call reads from it, that call wrote
+ * first.  All calls on one GPU share the array: two such calls that overlap
+ * in time on one GPU (concurrent streams, or threads) race and give wrong
+ * results; serialise them.  Other arguments, rules and errors as
+ * la_blockcausal_backward.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int la_blockcausal_backward_noalloc(const void* q, const void* k, const void* v,
+                                    const float* states, const void* dout, const float* dstates,
+                                    void* dq, void* dk, void* dv, float* dstate_in, int B, int H,
+                                    int N, int T, int d, int in_dt, int grad_dt, float eps,
+                                    hipStream_t stream);
 
 /*
  * la_chunk_backward - gradients of one la_chunk_forward call.

@@ -34,8 +34,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 9
-    for code in range(6):
+    assert la.abi_version() == 10
+    for code in range(7):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
 
@@ -381,3 +381,34 @@ def tconv(x=A, ci=2 * A, w=3 * A, b=4 * A, y=5 * A, co=6 * A, B=1, F=21, P=36, C
 ])
 def test_temporal_conv_rejects(kw, code):
     assert tconv(**kw) == code
+
+
+def bwd_noalloc(q=A, k=2 * A, v=3 * A, sts=4 * A, do=5 * A, dsts=None, dq=6 * A, dk=7 * A,
+                dv=8 * A, dsi=None, B=1, H=2, N=640, T=64, d=64, idt=BF16, gdt=F32, eps=1e-6):
+    return la.lib().la_blockcausal_backward_noalloc(q, k, v, sts, do, dsts, dq, dk, dv, dsi, B, H,
+                                                    N, T, d, idt, gdt, eps, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), la.LA_E_INVAL),
+    (dict(N=-2), la.LA_E_INVAL),
+    (dict(d=48), la.LA_E_UNSUPPORTED),
+    (dict(q=None), la.LA_E_INVAL),
+    (dict(dq=6 * A + 8), la.LA_E_ALIGN),
+    (dict(dk=5 * A + 512), la.LA_E_ALIAS),
+    # the suffix states of 64 heads x 40 blocks at d = 128 (169 MB) do not fit
+    (dict(B=4, H=16, N=40 * 4096, T=4096, d=128), la.LA_E_SCRATCH),
+    # one state slot per (b, h, block) over the 32 MiB: 2,017 heads x 1 block at d = 64
+    (dict(B=1, H=2017, N=64, T=64), la.LA_E_SCRATCH),
+])
+def test_backward_noalloc_rejects(kw, code):
+    """The allocation-free backward: argument errors as the workspace call,
+    and a clear LA_E_SCRATCH (before any HIP call) when even its smallest plan
+    does not fit the static scratch."""
+    assert bwd_noalloc(**kw) == code
+
+
+def test_backward_noalloc_scratch_limit():
+    # the largest head count whose suffix states fit one 32 MiB scratch
+    E = 64 * 64 + 64
+    assert la.NOALLOC_SCRATCH_BYTES // (E * 4) == 2016
