@@ -20,7 +20,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+# LINATTN_LIB names another build of the same library (the sanitizer build of
+# the host code, for the CPU contract tests); by default the in-tree one.
+LIB_PATH = os.environ.get("LINATTN_LIB") or os.path.join(_HERE, "liblinattn.so")
 
 LA_OK, LA_E_INVAL, LA_E_UNSUPPORTED, LA_E_ALIGN, LA_E_ALIAS, LA_E_HIP, LA_E_SCRATCH = range(7)
 # static device scratch of la_blockcausal_backward_noalloc
