@@ -425,7 +425,8 @@ def bench_other(args):
         chunks = [tuple(draw() for _ in range(3)) for _ in range(C)]
     out = torch.empty((B, H, L, d), dtype=torch.float32, device=dev)
     state = torch.empty((B, H, d * d + d), dtype=torch.float32, device=dev)
-    splits, rwg = la.plan(B, H, L, d, kv_splits=args.kv_splits)
+    splits, rwg = la.plan(B, H, L, d, kv_splits=args.kv_splits,
+                          readout_workgroups=args.readout_workgroups)
     log(f"plan (per chunk call): kv_splits={splits} readout_workgroups={rwg}")
 
     calls = 1 if (onecall or w.form == "global") else C
@@ -435,18 +436,21 @@ def bench_other(args):
         if onecall:
             la.blockcausal_forward(seq[0], seq[1], seq[2], L, out=out_seq, states=states,
                                    eps=workloads.EPS, kv_splits=args.kv_splits,
+                                   readout_workgroups=args.readout_workgroups,
                                    stage_events=None if evs is None else evs[0])
             return
         if w.form == "global":
             q, k, v = chunks[0]
             la.global_forward(q, k, v, out=out, state_out=state, eps=workloads.EPS,
                               kv_splits=args.kv_splits,
+                              readout_workgroups=args.readout_workgroups,
                               stage_events=None if evs is None else evs[0])
             return
         la.state_reset(state)
         for n, (q, k, v) in enumerate(chunks):
             la.chunk_forward(q, k, v, state, out=out, state_out=state, eps=workloads.EPS,
                              kv_splits=args.kv_splits,
+                             readout_workgroups=args.readout_workgroups,
                              stage_events=None if evs is None else evs[n])
 
     steps = max(1, args.steps // calls) if calls > 1 else args.steps
@@ -933,6 +937,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
+    ap.add_argument("--readout-workgroups", type=int, default=0,
+                    help="launch option of the forward calls (0: the planner's choice)")
     ap.add_argument("--workload", default="chunk720p",
                     choices=["chunk720p", "ceiling"] + list(OTHER) + list(BACKWARD)
                     + list(TCONV) + list(ROPE))
@@ -990,13 +996,15 @@ def main():
     _, state0 = la.global_forward(q0, k0, v0, eps=workloads.EPS)
     del q0, k0, v0
     torch.cuda.synchronize()
-    splits, rtok = la.plan(B, H, L, d, kv_splits=args.kv_splits)
+    splits, rtok = la.plan(B, H, L, d, kv_splits=args.kv_splits,
+                           readout_workgroups=args.readout_workgroups)
     log(f"plan: kv_splits={splits} readout_workgroups={rtok}")
 
     def step(i, ev=None):
         q, k, v, out, st = sets[i & 1]
         la.chunk_forward(q, k, v, state0, out=out, state_out=st, eps=workloads.EPS,
-                         kv_splits=args.kv_splits, stage_events=ev)
+                         kv_splits=args.kv_splits, readout_workgroups=args.readout_workgroups,
+                         stage_events=ev)
 
     wcalls = warm_up(step, args.warmup, args.min_warmup_s)
     log(f"warm-up done ({wcalls} calls); timing {args.steps} steps")

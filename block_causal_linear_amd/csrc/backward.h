@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
       if (PF == 2) gload(1, qa1, da1);
     }
 
-    __syncthreads();  // the previous item's LDS readers are done
+    lds_barrier();  // the previous item's LDS readers are done
     build_row_frags<D>(st, sfrag, wave, lane);
     if (wave < KS) {
       const float* zp = st + D * D + 32 * wave + 8 * g;
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
 #pragma unroll
       for (int c = 0; c < NR; ++c) accG[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
+    lds_barrier();
 
     auto tile = [&](int k, uint4 (&qa)[KS], DoRow<GO_BF16> (&da)[KS]) {
       const int buf = k & 1;
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
         }
         if (n == 0) sdd[buf][tt] = -c * rd;
       }
-      if constexpr (DNB == 1) __syncthreads();
+      if constexpr (DNB == 1) lds_barrier();
 
       // 2. dnum = dO / den as a bf16 hi/lo pair, token-major.  This lane's
       // A row, token 4 (n % 4) + n / 4, is row n % 4 of lane group n / 4.
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_bf16(
           dnl[db][u] = make_uint4(l[0], l[1], l[2], l[3]);
         }
       }
-      __syncthreads();
+      lds_barrier();
 
       // 3. G += phi(Q)^T dnum, g += phi(Q)^T dden over the tile's tokens
       const uint16_t* lq = reinterpret_cast<const uint16_t*>(qt[buf]);
@@ -425,11 +425,11 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
       if (PF == 2) gload(1, ka1, va1);
     }
 
-    __syncthreads();  // the previous item's LDS readers are done
+    lds_barrier();  // the previous item's LDS readers are done
     build_row_frags<D>(rs, rrow, wave, lane);
     build_col_frags<D>(rs, rcol, wave, lane);
     if (tid < D) rsh[tid] = rs[D * D + tid];
-    __syncthreads();
+    lds_barrier();
 
     auto step = [&](int j, uint4 (&ka)[KS], uint4 (&va)[KS]) {
       // read the operand fragments from LDS where they are used instead of

@@ -248,6 +248,191 @@ __global__ __launch_bounds__(kv_threads<D>(), kv_min_waves<D>()) void kv_partial
 }
 
 // ---------------------------------------------------------------------------
+// One block at d = 128 with enough heads to fill the GPU: quadrants instead of
+// token splits.  Workgroup (pair, quadrant) computes the 64 x 64 quadrant
+// rows [a0, a0 + 64) x columns [c0, c0 + 64) of phi(K)^T V over every token
+// of the block, from the 64-feature halves K[:, a0:] and V[:, c0:] of each
+// token row (one 128-byte cache line each), and writes S_in + that quadrant
+// straight into the state: no partial sums and no reduce launch.  The
+// quadrants with c0 = 0 also write z_out[a0 .. a0 + 63].  Each element of the
+// state is read and written by the same thread, so state_out may be state_in.
+//
+// The four quadrants of a head read the same halves twice over (K[:, a0:] by
+// the two quadrants of row half a0, V[:, c0:] by those of column half c0):
+// workgroups are numbered so that a head's four land on one XCD (workgroups
+// are dealt to the eight XCDs round robin), where the second read of a line
+// hits that XCD's L2.  With one four-wave workgroup per CU, the loads run
+// KvQuad::PF tiles ahead.
+#ifndef LA_KV_QUAD_PF
+#define LA_KV_QUAD_PF 4
+#endif
+// 1: number the quadrant workgroups so that a head's four share an XCD.
+#ifndef LA_KV_QUAD_XCD
+#define LA_KV_QUAD_XCD 1
+#endif
+struct KvQuad {
+  static constexpr int D = 128;
+  static constexpr int F = 64;            // features of a half row
+  static constexpr int TT = 64;           // tokens per tile
+  static constexpr int UPR = F / 8;       // 16-byte units per half row
+  static constexpr int RS = D / 8;        // 16-byte units per whole row
+  static constexpr int NT = 4 * kWave;    // 2 x 2 waves, 32 x 32 outputs each
+  static constexpr int UNITS = TT * UPR;
+  static constexpr int CPT = UNITS / NT;
+  static constexpr int PF = LA_KV_QUAD_PF;  // tiles in flight (registers)
+  static constexpr int XCD = 8;
+  // launch bound: waves per SIMD the registers must allow (keeps the MFMA
+  // accumulators in VGPRs instead of moving them through AGPRs every tile)
+  static constexpr int MIN_WAVES = 2;
+  static_assert(UNITS % NT == 0, "tile must split evenly over the workgroup");
+};
+
+// Workgroups in the grid for BH (b, h) pairs: four per pair, rounded up to
+// whole groups of eight pairs (the extra workgroups return at once).
+__host__ __device__ constexpr long long kv_quad_workgroups(long long bh) {
+  return 4 * KvQuad::XCD * ((bh + KvQuad::XCD - 1) / KvQuad::XCD);
+}
+
+__global__ __launch_bounds__(KvQuad::NT, KvQuad::MIN_WAVES) void kv_quad_bf16(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int N, int BH,
+    const float* state_in, float* state_out) {
+  using Q = KvQuad;
+  constexpr int D = Q::D, E = D * D + D;
+  constexpr int NR = 2, NC = 2;  // 16 x 16 blocks per wave (32 x 32)
+  __shared__ uint4 lds[2][2][Q::UNITS];  // [buffer][K, V][unit]
+
+  // workgroup w -> XCD w % 8; the four quadrants of a pair share an XCD
+  const int w = blockIdx.x;
+  const int xcd = w % Q::XCD, r = w / Q::XCD;
+  const int quad = LA_KV_QUAD_XCD ? r % 4 : w % 4;
+  const int pair = LA_KV_QUAD_XCD ? (r / 4) * Q::XCD + xcd : w / 4;
+  if (pair >= BH) return;
+  const int a0 = (quad >> 1) * Q::F, c0 = (quad & 1) * Q::F;
+  const size_t bh = static_cast<size_t>(pair);
+  const uint4* kb = reinterpret_cast<const uint4*>(k + bh * static_cast<size_t>(N) * D) + a0 / 8;
+  const uint4* vb = reinterpret_cast<const uint4*>(v + bh * static_cast<size_t>(N) * D) + c0 / 8;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wi = wave / 2, wj = wave % 2;
+  const int n = lane & 15, g = lane >> 4;
+
+  f32x4 acc[NR][NC];
+  f32x4 accz[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    accz[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NC; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+  const bool zcols = c0 == 0 && wj == 0;
+
+  uint4 rk[Q::PF][Q::CPT], rv[Q::PF][Q::CPT];
+  // half rows of tile `tile` through descriptors that end at the last token:
+  // rows past N read as zero
+  auto gload = [&](uint4 (&ck)[Q::CPT], uint4 (&cv)[Q::CPT], int tile) {
+    const int base = tile * Q::TT;
+    const int rows = max(0, min(N, base + Q::TT) - base);
+    const size_t first = static_cast<size_t>(base) * Q::RS;
+    const rsrc_t ksrc = tile_rsrc(kb, first, 16, rows * Q::RS * 16);
+    const rsrc_t vsrc = tile_rsrc(vb, first, 16, rows * Q::RS * 16);
+#pragma unroll
+    for (int i = 0; i < Q::CPT; ++i) {
+      const int u = tid + Q::NT * i;
+      const int off = ((u / Q::UPR) * Q::RS + u % Q::UPR) * 16;
+      const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(ksrc, off, 0, kBufNt);
+      const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(vsrc, off, 0, kBufNt);
+      ck[i] = make_uint4(a.x, a.y, a.z, a.w);
+      cv[i] = make_uint4(b.x, b.y, b.z, b.w);
+    }
+  };
+  auto lstore = [&](const uint4 (&ck)[Q::CPT], const uint4 (&cv)[Q::CPT], int buf) {
+#pragma unroll
+    for (int i = 0; i < Q::CPT; ++i) {
+      const int u = tid + Q::NT * i;
+      const int t = u / Q::UPR;
+      const int c = u % Q::UPR;
+      const int sl = t * Q::UPR + (c ^ unit_swizzle<Q::UPR>(t));
+      lds[buf][0][sl] = relu_bf16x8(ck[i]);
+      lds[buf][1][sl] = cv[i];
+    }
+  };
+  auto compute = [&](int buf) {
+    const uint16_t* lk = reinterpret_cast<const uint16_t*>(lds[buf][0]);
+    const uint16_t* lv = reinterpret_cast<const uint16_t*>(lds[buf][1]);
+#pragma unroll
+    for (int ks = 0; ks < Q::TT; ks += 32) {
+      uint4 a[NR], b[NC];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) a[i] = tile_column8<Q::UPR>(lk, ks, wi * 32 + i * 16, lane);
+#pragma unroll
+      for (int j = 0; j < NC; ++j) b[j] = tile_column8<Q::UPR>(lv, ks, wj * 32 + j * 16, lane);
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) acc[i][j] = mfma_16x16x32(a[i], b[j], acc[i][j]);
+      if (zcols) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) accz[i] = mfma_16x16x32(a[i], ones, accz[i]);
+      }
+    }
+  };
+
+  // PF register stages, two LDS buffers, one barrier per tile: tile i + 2
+  // overwrites the LDS buffer tile i was read from only after every thread
+  // has passed tile i + 1's barrier, which follows its reads of tile i.
+  // Stages run unconditionally in groups of PF: tiles past the last read
+  // zeros through their empty descriptors and add exactly nothing, and no
+  // load is conditional (a conditional load would make the compiler wait
+  // for every load in flight before the barrier).
+  const int ntiles = (N + Q::TT - 1) / Q::TT;
+  // issued in tile order (the scheduler may not reorder them): the first
+  // stage then waits for the oldest loads only
+#pragma unroll
+  for (int st = 0; st < Q::PF; ++st) {
+    gload(rk[st], rv[st], st);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int it = 0; it < ntiles; it += Q::PF) {
+#pragma unroll
+    for (int st = 0; st < Q::PF; ++st) {
+      lstore(rk[st], rv[st], st & 1);
+      lds_barrier();
+      gload(rk[st], rv[st], it + st + Q::PF);
+      compute(st & 1);
+    }
+  }
+
+  float* o = state_out + bh * E;
+  const float* si = state_in != nullptr ? state_in + bh * E : nullptr;
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ra = a0 + wi * 32 + i * 16 + 4 * g + e;
+        const int cc = c0 + wj * 32 + j * 16 + n;
+        float x = acc[i][j][e];
+        if (si) x = si[ra * D + cc] + x;
+        o[ra * D + cc] = x;
+      }
+  if (zcols && n == 0) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ra = a0 + wi * 32 + i * 16 + 4 * g + e;
+        float x = accz[i][e];
+        if (si) x = si[D * D + ra] + x;
+        o[D * D + ra] = x;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // float32 inputs: plain VALU outer-product accumulation (the float32 path is
 // for exactness checks and small problems; bfloat16 is the bandwidth path).
 template <int D>

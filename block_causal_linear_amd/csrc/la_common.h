@@ -69,6 +69,21 @@ __device__ __forceinline__ float from_bf16(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
+// Workgroup barrier for data exchanged through LDS only.  __syncthreads()
+// also orders global memory, so the compiler waits for every outstanding
+// global load (s_waitcnt vmcnt(0)) before it, including prefetches whose
+// registers are not yet used: a kernel that loads tiles ahead in registers
+// and stages them through LDS would drain its prefetch at every barrier.
+// Fences on the LDS address space only leave "s_waitcnt lgkmcnt(0);
+// s_barrier", and the global loads keep flying until their registers are
+// read.  Use it only where no wave reads global memory another wave of the
+// workgroup wrote before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Streaming (non-temporal) 16-byte load: data read exactly once.
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

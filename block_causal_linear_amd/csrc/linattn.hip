@@ -80,12 +80,6 @@ constexpr int kKvMinTokensPerFeature = 4;
 // gives each workgroup a contiguous token range of one head (1024
 // workgroups, 512 at d = 128 where each stages a 64 KB state).
 constexpr int kSweepWorkgroups = 512;
-// At d = 128 a sweep workgroup has eight waves and 144 KB of LDS: one per CU
-// (256 measured best at the long-horizon shape among 128..1024).  The
-// default build reads out d = 128 with readout_items_bf16 instead (faster at
-// every long-horizon shape measured); building with LA_READOUT_ITEMS_MIN_D
-// above 128 restores the sweep there.
-constexpr int kSweepWorkgroups128 = 256;
 constexpr int kReadoutTargetWorkgroups = 1024;
 // Shortest item of the item readout (d = 128): at the long-horizon chunk
 // (64 heads x 4,096 tokens) items of 1,024 tokens on 256 workgroups measured
@@ -94,6 +88,9 @@ constexpr int kReadoutItemMinTokens = 1024;
 // Compute units of an MI355X: the persistent grids below are sized to the
 // resident workgroups of one round.
 constexpr int kCUs = 256;
+// One block at d = 128 takes the quadrant KV kernel (four workgroups per
+// head, no token split) from this many (b, h) pairs: one workgroup per CU.
+constexpr long long kKvQuadMinPairs = 64;
 // Resident workgroups of the two bf16 backward kernels on a 256-CU MI355X:
 // their persistent grids.  Each kernel is compiled for a number of waves
 // per SIMD (its launch bound), which with four-wave workgroups is the
@@ -152,9 +149,10 @@ struct Plan {
   int tps;             // tokens per split
   int kv_tile;         // tokens per KV tile
   bool direct;         // one block, one split: the KV kernel writes the state
+  bool quad;           // one block at d = 128: kv_quad_bf16 writes the state
   bool in_place;       // several blocks, one split: partials live in `states`
   bool sweep;          // readout_sweep_bf16 (bf16 inputs, d < LA_READOUT_ITEMS_MIN_D)
-  bool items;          // readout_items_bf16 (bf16 inputs, larger d); else readout_f32
+  bool items;          // readout_items_bf16 (bf16 inputs, larger d or rotary); else readout_f32
   int ro_splits;       // readout_items_bf16: items per block
   int readout_tpw;     // readout_f32: tokens per workgroup
   int readout_wgs;     // readout workgroups in the grid
@@ -252,6 +250,16 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
   p.splits = (Tb + p.tps - 1) / p.tps;
   p.direct = p.nblk == 1 && p.splits == 1;
   p.in_place = p.nblk > 1 && p.splits == 1;
+  // One block at d = 128 over enough heads to give every CU a workgroup:
+  // quadrants of the state instead of token splits (no partials, no reduce).
+  // A split request keeps the split path.
+  if (in_dt == LA_BF16 && d == 128 && p.nblk == 1 && !rope && request <= 0 &&
+      la::kv_quad_workgroups(bhc) >= kCUs && bhc >= kKvQuadMinPairs) {
+    p.quad = true;
+    p.splits = 1;
+    p.tps = ((Tb + p.kv_tile - 1) / p.kv_tile) * p.kv_tile;
+    p.direct = true;
+  }
 
   // readout
   if (p.items) {
@@ -271,11 +279,9 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
     p.ro_splits = static_cast<int>(s2);
     p.readout_wgs = static_cast<int>(pairs * s2 < cap ? pairs * s2 : cap);
   } else if (p.sweep) {
-    const int unit = 4 * 16 * (d == 128 ? 2 : LA_READOUT_ROWS);
+    const int unit = 4 * 16 * LA_READOUT_ROWS;
     p.units_per_block = (Tb + unit - 1) / unit;
-    long long wgs = readout_request > 0 ? readout_request
-                    : d == 128          ? kSweepWorkgroups128
-                                        : kSweepWorkgroups;
+    long long wgs = readout_request > 0 ? readout_request : kSweepWorkgroups;
     // workgroup steps take runs of LA_READOUT_RUN units
     const long long runs = (pairs * p.units_per_block + LA_READOUT_RUN - 1) / LA_READOUT_RUN;
     if (wgs > runs) wgs = runs;
@@ -327,6 +333,16 @@ int launch_kv(const Plan& p, const void* k, const void* v, int in_dt, int B, int
           static_cast<const float*>(k), static_cast<const float*>(v), N, p.T, p.splits, p.tps,
           state_in, dst, *rope);
     return launched();
+  }
+  if (p.quad) {
+    if constexpr (D == 128) {
+      const long long wgs = la::kv_quad_workgroups(static_cast<long long>(B) * H);
+      la::kv_quad_bf16<<<static_cast<unsigned>(wgs), la::KvQuad::NT, 0, stream>>>(
+          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, B * H, state_in,
+          dst);
+      return launched();
+    }
+    return LA_E_UNSUPPORTED;
   }
   if (in_dt == LA_BF16)
     la::kv_partial_bf16<D><<<grid, la::kv_threads<D>(), 0, stream>>>(
@@ -388,16 +404,20 @@ int launch_readout(const Plan& p, const void* q, int out_dt, int B, int H, int N
     return launched();
   }
   if (p.sweep) {
-    const uint16_t* qq = static_cast<const uint16_t*>(q);
-    const int total = B * H * p.nblk * p.units_per_block;
-    constexpr int nt = la::sweep_threads<D>();
-    if (out_dt == LA_BF16)
-      la::readout_sweep_bf16<D, true><<<p.readout_wgs, nt, 0, stream>>>(
-          qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
-    else
-      la::readout_sweep_bf16<D, false><<<p.readout_wgs, nt, 0, stream>>>(
-          qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
-    return launched();
+    // only d below LA_READOUT_ITEMS_MIN_D plans the sweep: nothing else is built
+    if constexpr (D < LA_READOUT_ITEMS_MIN_D) {
+      const uint16_t* qq = static_cast<const uint16_t*>(q);
+      const int total = B * H * p.nblk * p.units_per_block;
+      constexpr int nt = la::sweep_threads<D>();
+      if (out_dt == LA_BF16)
+        la::readout_sweep_bf16<D, true><<<p.readout_wgs, nt, 0, stream>>>(
+            qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
+      else
+        la::readout_sweep_bf16<D, false><<<p.readout_wgs, nt, 0, stream>>>(
+            qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
+      return launched();
+    }
+    return LA_E_UNSUPPORTED;
   }
   // float32 queries: workgroups over contiguous token ranges of one block
   const dim3 grid(p.nblk * ((p.T + p.readout_tpw - 1) / p.readout_tpw), H, B);

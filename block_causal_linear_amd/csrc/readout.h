@@ -68,9 +68,10 @@ __device__ __forceinline__ uint4 load_q(const uint4* p) {
 #endif
 }
 
-// Sweep readout: at d = 128 the output columns split into two 64-column
-// halves; waves 0-3 and 4-7 of a workgroup take the same four tiles, one
-// half each (the second read of a query row hits L2).
+// Sweep readout shape (built for d <= 64 only: at d = 128 the per-unit
+// rebuild of a 66 KB state's operands dominated, and readout_items_bf16 reads
+// out there).  The NCH = 2 column split below is the layout the sweep had at
+// d = 128 and is kept only as the generic form of the template.
 template <int D>
 struct SweepShape {
   static constexpr int NCH = D == 128 ? 2 : 1;          // column halves
@@ -78,9 +79,7 @@ struct SweepShape {
   static constexpr int NT = kWave * NW;                 // threads per workgroup
   static constexpr int CB = ReadoutShape<D>::NBK / NCH;  // column blocks per half
   static constexpr int MIN_WAVES = D == 128 ? 2 : 3;
-  // Operand buffers in LDS (two: one barrier per unit).  At d = 128 they take
-  // 144 KB, one eight-wave workgroup per CU; a single 72 KB buffer with two
-  // barriers per unit (two workgroups per CU) measured no faster.
+  // Operand buffers in LDS (two: one barrier per unit).
   static constexpr int NBUF = 2;
 };
 
@@ -260,9 +259,9 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
       buf = NBUF == 2 ? buf ^ 1 : 0;
       // With two buffers, buf was last read before the previous build's
       // barrier; with one, wait until every wave has consumed the last unit.
-      if (NBUF == 1 && built >= 0) __syncthreads();
+      if (NBUF == 1 && built >= 0) lds_barrier();
       build(buf);
-      __syncthreads();
+      lds_barrier();
       built = sb;
     }
     const int next = unit_of(j + 1);
@@ -299,7 +298,7 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
 // backward kernels (rows past the block hold copies of its last row and are
 // dropped by the descriptor), so the loop has no branch.
 #ifndef LA_READOUT_ITEMS_MIN_D
-#define LA_READOUT_ITEMS_MIN_D 128  // smallest d that uses readout_items_bf16
+#define LA_READOUT_ITEMS_MIN_D 128  // smallest d that leaves the sweep readout
 #endif
 
 // Waves per SIMD the kernel is compiled for; with four waves per workgroup
@@ -323,7 +322,7 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_ite
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int n = lane & 15, g = lane >> 4;
   const int sig = 4 * (n & 3) + (n >> 2);
 
@@ -347,7 +346,7 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_ite
       gload(1, qa1);
     }
 
-    __syncthreads();  // the previous item's LDS readers are done
+    lds_barrier();  // the previous item's LDS readers are done
     build_col_frags<D>(st, scol, wave, lane);
     if (wave < KS) {
       const float* zp = st + D * D + 32 * wave + 8 * g;
@@ -357,7 +356,7 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_ite
       zfrag[2 * wave][lane] = make_uint4(h[0], h[1], h[2], h[3]);
       zfrag[2 * wave + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     auto tile = [&](int j, uint4 (&qa)[KS]) {
       // read the operands from LDS where they are used instead of holding

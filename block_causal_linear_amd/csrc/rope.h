@@ -177,23 +177,23 @@ __global__ __launch_bounds__(kv_threads<D>(), kv_rope_min_waves<D>()) void kv_pa
   if (ntiles > 1) gload(rk1, rv1, 1);
   for (int it = 0; it < ntiles; it += 2) {
     lstore(rk0, rv0, 0);
-    __syncthreads();
+    lds_barrier();
     if (it + 2 < ntiles) gload(rk0, rv0, it + 2);
     compute(0);
     if (it + 1 < ntiles) {
       lstore(rk1, rv1, 1);
-      __syncthreads();
+      lds_barrier();
       if (it + 3 < ntiles) gload(rk1, rv1, it + 3);
       compute(1);
     }
   }
 
   // z: the threads of one column hold disjoint token rows
-  __syncthreads();  // every wave is past its last LDS read
+  lds_barrier();  // every wave is past its last LDS read
   float* zl = reinterpret_cast<float*>(&lds[0][0][0]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) zl[tid * 8 + j] = zacc[j];
-  __syncthreads();
+  lds_barrier();
 
   const bool direct = nblk == 1 && splits == 1;
   float* o = dst + ((bh * nblk + blk) * splits + split) * static_cast<size_t>(E);
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_rop
       gload(1, qa1);
     }
 
-    __syncthreads();  // the previous item's LDS readers are done
+    lds_barrier();  // the previous item's LDS readers are done
     build_col_frags<D>(st, scol, wave, lane);
     if (wave < KS) {
       const float* zp = st + D * D + 32 * wave + 8 * g;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256, readout_items_min_waves<D>()) void readout_rop
       zfrag[2 * wave][lane] = make_uint4(h[0], h[1], h[2], h[3]);
       zfrag[2 * wave + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
     }
-    __syncthreads();
+    lds_barrier();
 
     auto tile = [&](int j, uint4 (&qa)[KS]) {
       asm volatile("" ::: "memory");

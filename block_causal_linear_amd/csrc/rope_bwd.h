@@ -330,11 +330,11 @@ __global__ __launch_bounds__(256, bwd_key_rope_min_waves<D>()) void bwd_key_rope
 #pragma unroll
     for (int i = 0; i < 4; ++i) trc[i].init(rg, wave_base(0) + 4 * i + g);
 
-    __syncthreads();  // the previous item's LDS readers are done
+    lds_barrier();  // the previous item's LDS readers are done
     build_row_frags<D>(rs, rrow, wave, lane);
     build_col_frags<D>(rs, rcol, wave, lane);
     if (tid < D) rsh[tid] = rs[D * D + tid];
-    __syncthreads();
+    lds_barrier();
 
     auto step = [&](int j, uint4 (&ka)[KS], uint4 (&va)[KS]) {
       asm volatile("" ::: "memory");
@@ -494,7 +494,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_rope_
 #pragma unroll
     for (int i = 0; i < 4; ++i) trc[i].init(rg, tile_base(0) + 16 * wave + 4 * i + g);
 
-    __syncthreads();  // the previous item's LDS readers are done
+    lds_barrier();  // the previous item's LDS readers are done
     build_row_frags<D>(st, sfrag, wave, lane);
     if (wave < KS) {
       const float* zp = st + D * D + 32 * wave + 8 * g;
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_rope_
     float gacc[NBK];  // dz over this lane's rows, per accumulator column
 #pragma unroll
     for (int nb = 0; nb < NBK; ++nb) gacc[nb] = 0.f;
-    __syncthreads();
+    lds_barrier();
 
     auto tile = [&](int kk, uint4 (&qa)[KS], DoRow<GO_BF16> (&da)[KS]) {
       const int base = tile_base(kk);
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_rope_
 #pragma unroll
         for (int nb = 0; nb < NBK; ++nb) gacc[nb] = fmaf(qacc[nb][i], dden, gacc[nb]);
       }
-      __syncthreads();  // every wave is done with the previous tile's LDS tiles
+      lds_barrier();  // every wave is done with the previous tile's LDS tiles
 
       // 3. q~ and dnum = dO / den as bf16 hi/lo, token-major.  This lane's A
       // row, token 4 (n % 4) + n / 4, is row n % 4 of lane group n / 4.
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_rope_
           qtl[u] = rql[s];
         }
       }
-      __syncthreads();
+      lds_barrier();
 
       // 4. dS += q~^T dnum over the tile's tokens
       const uint16_t* lqh = reinterpret_cast<const uint16_t*>(qth);
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(256, bwd_query_min_waves<D>()) void bwd_query_rope_
       x += __shfl_xor(x, 32);
       if (g == 0) gred[wave][acc_col<D>(nb, n)] = x;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < D) o[D * D + tid] = ((gred[0][tid] + gred[1][tid]) + gred[2][tid]) + gred[3][tid];
   }
 }

@@ -49,3 +49,42 @@ def report(name, **vals):
     msg = " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}" for k, v in vals.items())
     print(f"[parity] {name} {msg}", flush=True)
     sys.stdout.flush()
+
+
+def bf16_rne(x):
+    """float64 values rounded to bfloat16 (ties to even) through float32,
+    the way a float32 result is stored as bfloat16; returned as float64."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).copy()
+    u = (u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).astype(np.float64)
+
+
+def bf16_ulp(r):
+    """Spacing of bfloat16 at each bfloat16 value r (toward larger magnitude)."""
+    f = np.ascontiguousarray(np.asarray(r, dtype=np.float32))
+    u = f.view(np.uint32)
+    nxt = ((u & np.uint32(0x7FFFFFFF)) + np.uint32(0x10000)).view(np.float32)
+    return np.abs(nxt.astype(np.float64)) - np.abs(f.astype(np.float64))
+
+
+def bf16_rounding(got, ref, axes, rel_err):
+    """A bfloat16 result against the fp64 oracle rounded to bfloat16 (ties to
+    even).  Each element may differ from the rounded oracle by at most one
+    bfloat16 ulp plus the float32 arithmetic error before rounding
+    (rel_err x max|ref| over the slice reduced by `axes`): the float32 value
+    can sit on the other side of a rounding boundary.  Returns
+    (worst excess over that bound in ulps (<= 0 passes), fraction of elements
+    not equal to the rounded oracle).  Rounding to nearest even leaves that
+    fraction near zero; truncation or another rounding mode makes it about
+    one half."""
+    got = np.asarray(got, dtype=np.float64)
+    r = bf16_rne(ref)
+    ulp = bf16_ulp(r)
+    abs_err = rel_err * np.abs(ref).max(axis=axes, keepdims=True)
+    excess = (np.abs(got - r) - (ulp + abs_err)) / ulp
+    return float(excess.max()), float(np.mean(got != r))
+
+
+# elements of a bfloat16 result that may differ from the rounded oracle
+BF16_MISMATCH_MAX = 0.02

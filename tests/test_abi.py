@@ -196,9 +196,12 @@ def test_plan_shapes():
     # d = 128 reads out over persistent work items of at least 1,024 tokens:
     # 64 heads x 4 items = 256 workgroups; a request sets the item count (up
     # to the resident grid of 512); float32 inputs keep per-head workgroups
-    # (512 at d = 128: 8 per head here)
-    assert la.plan(4, 16, 4096, 128)[1] == 256
+    # (512 at d = 128: 8 per head here).  One chunk at d = 128 over 64 heads
+    # takes the quadrant KV kernel: one "split".
+    assert la.plan(4, 16, 4096, 128) == (1, 256)
     assert la.plan(4, 16, 4096, 128, readout_workgroups=2048)[1] == 512
+    assert la.plan(4, 16, 4096, 128, kv_splits=4)[0] == 4  # a request keeps the splits
+    assert la.plan(2, 16, 4096, 128)[0] > 1                # 32 heads: token splits
     assert la.plan(4, 16, 40 * 4096, 128)[1] == 512
     assert la.plan(4, 16, 4096, 128, in_dtype=la.torch.float32)[1] == 4 * 16 * 8
     with pytest.raises(la.LinAttnError):

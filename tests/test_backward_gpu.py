@@ -15,7 +15,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import TOL, dev, host, normwise, report, state_err, state_np
+from helpers import (BF16_MISMATCH_MAX, TOL, bf16_rounding, dev, host, normwise, report,
+                     state_err, state_np)
 
 import block_causal_linear_amd as la
 
@@ -71,6 +72,23 @@ def check(name, got, ref, bounds, tol, dsi=None, dsi_ref=None):
     report(name, **vals)
     assert max(vals.values()) <= tol, vals
 
+def check_bf16_grads(name, got, ref, bounds):
+    """bfloat16 gradients against the oracle's rounded to bfloat16 (ties to
+    even), per (b, h, block) slice: every element within one ulp plus the
+    float32 arithmetic error (5e-5 of the slice's largest value), and equal
+    to the rounded oracle almost everywhere (the fraction over all blocks)."""
+    vals = {}
+    for nm, g, r in zip(("dq", "dk", "dv"), got, ref):
+        worst, diff = -1e30, 0.0
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            e, m = bf16_rounding(g[:, :, a:b], r[:, :, a:b], (2, 3), 5e-5)
+            worst, diff = max(worst, e), diff + m * (b - a)
+        vals[nm + "_ulp_excess"], vals[nm + "_mismatch"] = worst, diff / bounds[-1]
+    report(name + " rounding", **vals)
+    assert all(v <= 0.0 for k, v in vals.items() if k.endswith("excess")), vals
+    assert all(v <= BF16_MISMATCH_MAX for k, v in vals.items() if k.endswith("mismatch")), vals
+
+
 
 # ---------------------------------------------------------------------------
 # small shapes: several tiles, ragged tails, one-token blocks, a state input
@@ -109,6 +127,7 @@ def test_backward_bf16_gradients(d):
     got = gpu_backward(Q, K, V, dO, T, "bf16", gdt="bf16")
     ref = oracle.blockcausal_backward(Q, K, V, bounds_of(N, T), dO, EPS)
     check(f"backward bf16 grads d={d}", got[:3], ref[:3], bounds_of(N, T), BF16_OUT_TOL)
+    check_bf16_grads(f"backward bf16 grads d={d}", got[:3], ref[:3], bounds_of(N, T))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

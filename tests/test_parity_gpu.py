@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import TOL, dev, host, out_err, report, state_err, state_np
+from helpers import (BF16_MISMATCH_MAX, TOL, bf16_rounding, dev, host, out_err, report,
+                     state_err, state_np)
 
 import block_causal_linear_amd as la
 
@@ -61,6 +62,26 @@ def test_chunk_small(dtype, d, L):
     S_in, z_in = workloads.random_state(L + d, B, H, d)
     S_in, z_in = S_in.astype(np.float64), z_in.astype(np.float64)
     check_chunk(f"chunk {dtype} d={d} L={L}", Q, K, V, S_in, z_in, dtype)
+
+
+# One block at d = 128 over 64 or more (b, h) pairs takes the quadrant KV
+# kernel (no token split, the state written directly); head counts that are
+# not a multiple of 8 leave idle workgroups in its grid.
+@pytest.mark.parametrize("B,H,L", [(1, 64, 300), (2, 33, 130), (1, 65, 1), (4, 16, 4096)])
+def test_chunk_d128_quadrants(B, H, L):
+    d = 128
+    assert la.plan(B, H, L, d)[0] == 1  # the quadrant path
+    Q, K, V = workloads.random_qkv(3100 + H, B, H, L, d)
+    S_in, z_in = workloads.random_state(3200 + H, B, H, d)
+    S_in, z_in = S_in.astype(np.float64), z_in.astype(np.float64)
+    O, st = check_chunk(f"chunk quadrants B={B} H={H} L={L}", Q, K, V, S_in, z_in, "bf16")
+    # in place (state_out = state_in) gives the same bits
+    st_io = torch.from_numpy(state_np(S_in, z_in)).cuda()
+    out, st2 = la.chunk_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), st_io,
+                                state_out=st_io, eps=EPS)
+    torch.cuda.synchronize()
+    assert st2.data_ptr() == st_io.data_ptr()
+    assert np.array_equal(host(st2), st) and np.array_equal(host(out), O)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -281,8 +302,11 @@ def test_bf16_output():
     O_ref, _, _ = oracle.chunk_forward(Q, K, V, S_in, z_in, EPS)
     O, _ = run_chunk(Q, K, V, state_np(S_in, z_in), "bf16", out_dtype=torch.bfloat16)
     eo = out_err(O, O_ref)
-    report("bf16 out", out=eo)
-    assert eo <= 2.0 ** -8
+    # against the oracle rounded to bf16 (ties to even): within one ulp plus
+    # the float32 arithmetic error, and equal to it almost everywhere
+    excess, mismatch = bf16_rounding(O, O_ref, (2, 3), 2e-5)
+    report("bf16 out", out=eo, ulp_excess=excess, mismatch=mismatch)
+    assert excess <= 0.0 and mismatch <= BF16_MISMATCH_MAX, (excess, mismatch)
 
 
 def test_binding_rejects_bad_buffers():

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from helpers import dev, host, normwise, report
+from helpers import BF16_MISMATCH_MAX, bf16_rounding, dev, host, normwise, report
 
 import block_causal_linear_amd as la
 
@@ -56,6 +56,11 @@ def test_tconv_chunk_small(xdt, ydt, F, P, C, with_cache):
     e = err(host(y), ref)
     report(f"tconv chunk x={xdt} y={ydt} F={F} P={P} C={C} cache={with_cache}", y=e)
     assert e <= TOL[ydt], e
+    if ydt == "bf16":
+        # against the oracle rounded to bf16 (ties to even), per (b, frame)
+        excess, mismatch = bf16_rounding(host(y), ref, (2, 3), 1e-5)
+        report("tconv bf16 rounding", ulp_excess=excess, mismatch=mismatch)
+        assert excess <= 0.0 and mismatch <= BF16_MISMATCH_MAX, (excess, mismatch)
     assert np.array_equal(host(co), ref_cache)
 
 
