@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256, bwd_key_rope_min_waves<D>()) void bwd_key_rope
 
     lds_barrier();  // the previous item's LDS readers are done
     build_row_frags<D>(rs, rrow, wave, lane);
-    build_col_frags<D>(rs, rcol, wave, lane);
+    build_col_frags_scalar<D>(rs, rcol, wave, lane);
     if (tid < D) rsh[tid] = rs[D * D + tid];
     lds_barrier();
 

@@ -57,8 +57,41 @@ __device__ void build_row_frags(const float* X, uint4 (*frag)[kWave], int wave, 
 
 // MFMA B operand "columns of X": B[k = a][n] = X[32 s + a][acc_col(nb, n)]
 // for the products sum_a x[a] X[a][c] with x in the A operand (tokens x a).
+// A lane needs eight rows of one column per fragment, but the W column
+// blocks nb = W q .. W q + W - 1 place lane n's columns side by side
+// (acc_col = 16 W q + W n + nb % W), so one W-float vector load per row
+// serves W fragments: the waves take (k-step, group) units and issue 8
+// vector loads per unit instead of 8 scalar loads per fragment.
 template <int D>
 __device__ void build_col_frags(const float* X, uint4 (*frag)[kWave], int wave, int lane) {
+  using Sh = RowTile<D>;
+  constexpr int W = Sh::W;
+  typedef float vecW __attribute__((ext_vector_type(W)));
+  const int n = lane & 15, g = lane >> 4;
+  for (int u = wave; u < Sh::KS * Sh::GRP; u += 4) {
+    const int s = u / Sh::GRP, q = u % Sh::GRP;
+    const float* src = X + (32 * s + 8 * g) * D + 16 * W * q + W * n;
+    vecW x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = *reinterpret_cast<const vecW*>(src + j * D);
+#pragma unroll
+    for (int e = 0; e < W; ++e) {
+      const int p = s * Sh::NBK + W * q + e;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) split_bf16x2(x[j][e], x[j + 1][e], &h[j / 2], &l[j / 2]);
+      frag[2 * p][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+      frag[2 * p + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+  }
+}
+
+// The same fragments with one scalar load per value: fewer live registers
+// during the build.  The key-gradient kernels, which build two operand sets
+// per item at four waves per SIMD, spill less with it (372 against 374 us
+// per key kernel at the 720p chunk); the readouts gain from the vector loads.
+template <int D>
+__device__ void build_col_frags_scalar(const float* X, uint4 (*frag)[kWave], int wave, int lane) {
   using Sh = RowTile<D>;
   const int n = lane & 15, g = lane >> 4;
   for (int p = wave; p < Sh::KS * Sh::NBK; p += 4) {

@@ -11,7 +11,7 @@ namespace la {
 
 // One workgroup per 64 float4 of the (d*d + d) state of one (b, h): its
 // four wavefronts each sum one contiguous quarter of the splits (in split
-// order, loads unrolled by four), then wave 0 adds the four quarters in
+// order, loads in batches of eight and four), then wave 0 adds the four quarters in
 // order and adds the result to S_in.  The order is fixed, so repeated runs
 // are bitwise identical.  splits == 0 copies state_in (or writes zeros when
 // state_in is null).  state_in may equal state_out: each element is read
@@ -41,7 +41,16 @@ __global__ __launch_bounds__(kBlock) void state_reduce(const float4* __restrict_
   if (j == 0 && e < n4 && state_in != nullptr) si = state_in[idx];
   if (e < n4) {
     const float4* p = partials + bh * static_cast<size_t>(splits) * n4 + e;
+    // batches of 8 independent loads, then the adds in split order: a
+    // quarter of up to 8 splits (32 splits per block) waits on memory once
     int s = s0;
+    for (; s + 8 <= s1; s += 8) {
+      float4 x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = p[static_cast<size_t>(s + i) * n4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) add(kv, x[i]);
+    }
     for (; s + 4 <= s1; s += 4) {
       const float4 x0 = p[static_cast<size_t>(s) * n4];
       const float4 x1 = p[static_cast<size_t>(s + 1) * n4];
