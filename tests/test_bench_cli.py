@@ -1,5 +1,6 @@
 """bench.py's command line on the CPU: more than one GPU is refused with a
-message and exit status 2 before anything touches a device."""
+message and exit status 2 before anything touches a device, and the commands
+the profile summaries quote use options bench.py still accepts."""
 
 import os
 import subprocess
@@ -14,3 +15,27 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_profile_commands_use_current_options():
+    """Every bench.py command quoted in profiles/ and the docs names only
+    options bench.py accepts, so each summary's command can be run again."""
+    import glob
+    import re
+
+    accepted = set(re.findall(r'add_argument\("(--[\w-]+)"', open(os.path.join(ROOT, "bench.py")).read()))
+    assert {"--workload", "--steps", "--warmup", "--no-cpu-baseline"} <= accepted
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    files += [os.path.join(ROOT, n) for n in ("DESIGN.md", "README.md")]
+    stale = []
+    for f in files:
+        text = open(f).read().replace("\\\n", " ")
+        for m in re.finditer(r"bench\.py([^\n`]*)", text):
+            bad = set(re.findall(r"(--[\w-]+)", m.group(1))) - accepted
+            if bad:
+                stale.append((os.path.basename(f), sorted(bad)))
+    assert not stale, stale
+    workloads = set(re.findall(r'"(\w+)"', open(os.path.join(ROOT, "bench.py")).read()))
+    for f in files:
+        for w in re.findall(r"--workload (\w+)", open(f).read()):
+            assert w in workloads or w == "W", (os.path.basename(f), w)
