@@ -755,6 +755,12 @@ def bench_backward(args):
     ms = timed_region(step, args.steps)
     per = sampled_pass(step, max(args.steps, args.sample_calls))
     call_b, q_b, k_b = bwd_bytes(B, H, N, d, C)
+    streams = la.backward_stream_count(B, H, N, T, d)
+    rf = roofline(f"bwd_key_{'rope_' if rope else ''}bf16<{d}>", k_b, per[:, 2])
+    if streams == 2:
+        rf["source"] += ("; stage events keep a call on one stream, so this is the kernel of "
+                         "a one-stream call, while the timed calls run the two halves of the "
+                         "(b, h) pairs on two streams")
     result = {
         "metric": "latent tokens/sec + % peak HBM BW, block-causal linear attn backward",
         "value": B * N / (ms * 1e-3), "unit": "latent tokens/s", "n_gpus": 1,
@@ -769,7 +775,8 @@ def bench_backward(args):
                    **({"frame0": f0, "grid": [gh, gw]} if rope else {})},
         "hbm_frac": call_b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "us_per_block": ms * 1e3 / C,
-        "roofline": roofline(f"bwd_key_{'rope_' if rope else ''}bf16<{d}>", k_b, per[:, 2]),
+        "roofline": rf,
+        "streams": streams,
         "stages_us": stage_summary(per, ["bwd_query", "suffix_scan", "bwd_key"]),
         "bwd_query_GBs": q_b / (float(per[:, 0].mean()) * 1e-3) / 1e9,
         "bwd_key_GBs": k_b / (float(per[:, 2].mean()) * 1e-3) / 1e9,

@@ -31,7 +31,7 @@ static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES]
 
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
 
 // The address of `scratch` on the device of `stream` (the current device for
 // the null stream), looked up on that device's first call and kept.
@@ -60,6 +60,48 @@ int device_scratch(hipStream_t stream, void** out) {
   }
   *out = g_scratch_ptr[dev];
   return LA_OK;
+}
+
+// A second stream of the library's own per device (default priority, created
+// on the first backward call that can use it, kept until the process ends),
+// with the two events that fork work onto it and join it back.  The backward
+// runs the second half of its (b, h) pairs there (see backward()).
+struct AuxStream {
+  std::mutex mu;  // creation, then each call's fork / enqueue / join sequence
+  bool tried = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+AuxStream g_aux[kMaxDevices];
+
+AuxStream* aux_stream(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  AuxStream& a = g_aux[dev];
+  std::lock_guard<std::mutex> lock(a.mu);
+  if (!a.tried) {
+    a.tried = true;  // a failed creation is not retried: calls stay on one stream
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    const bool ok = hipStreamCreateWithFlags(&st, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&f, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&j, hipEventDisableTiming) == hipSuccess;
+    const bool back = cur == dev || hipSetDevice(cur) == hipSuccess;
+    if (ok && back) {
+      a.s = st;
+      a.fork = f;
+      a.join = j;
+    }
+  }
+  return a.s != nullptr ? &a : nullptr;
 }
 
 // KV workgroups the planner aims for: two per compute unit of a 256-CU
@@ -113,6 +155,10 @@ int bwd_key_capacity(int d, bool rope) {
 constexpr int kRopeMaxTokens = 1 << 22;
 // float32 backward kernels: workgroups over contiguous token ranges.
 constexpr int kBwdF32TargetWorkgroups = 512;
+// Token-heads (B H N) from which a bfloat16 backward call runs its two halves
+// of (b, h) pairs on two streams; below it the fork and join cost more than
+// the overlap gains.
+constexpr long long kBwdSplitMinTokens = 1LL << 20;
 
 long long gcd_ll(long long a, long long b) {
   while (b != 0) {
@@ -682,6 +728,37 @@ int check_rope(const la::RopeGrid* rope, int N) {
   return LA_OK;
 }
 
+// Whether a backward call of this shape runs its two halves of (b, h) pairs on
+// two streams (outside stream capture, without stage events, with the
+// device's second stream available; see backward()).
+bool bwd_two_streams(int B, int H, int N, int in_dt) {
+  const long long P = static_cast<long long>(B) * H;
+  return in_dt == LA_BF16 && P >= 2 && P - P / 2 <= 65535 && N > 0 &&
+         P * static_cast<long long>(N) >= kBwdSplitMinTokens;
+}
+
+// run_bwd for the head dimension and gradient type of a call.
+int run_bwd_d(int d, bool gb, const BwdPlan& p, const void* q, const void* k, const void* v,
+              const float* states, const void* dout, const float* dstates, void* dq, void* dk,
+              void* dv, float* dstate_in, int B, int H, int N, int in_dt, float eps,
+              void* workspace, const la::RopeGrid* rope, const la_launch_opts* opts,
+              hipStream_t stream) {
+#define LA_RUN_BWD(DD)                                                                          \
+  return gb ? run_bwd<DD, true>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, \
+                                N, in_dt, eps, workspace, rope, opts, stream)                   \
+            : run_bwd<DD, false>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H,\
+                                 N, in_dt, eps, workspace, rope, opts, stream)
+  switch (d) {
+    case 32:
+      LA_RUN_BWD(32);
+    case 64:
+      LA_RUN_BWD(64);
+    default:
+      LA_RUN_BWD(128);
+  }
+#undef LA_RUN_BWD
+}
+
 // Checks shared by every backward call, then the launches.  The sequence of
 // N tokens per (b, h) is cut into blocks of T (one block: T >= N); `states`
 // holds the forward's state after every block.  `empty_block`: the chunk
@@ -761,20 +838,75 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
   }
   if (static_scratch && (rc = device_scratch(stream, &workspace)) != LA_OK) return rc;
   const bool gb = grad_dt == LA_BF16;
-#define LA_RUN_BWD(DD)                                                                          \
-  return gb ? run_bwd<DD, true>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, \
-                                N, in_dt, eps, workspace, rope, opts, stream)                   \
-            : run_bwd<DD, false>(p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H,\
-                                 N, in_dt, eps, workspace, rope, opts, stream)
-  switch (d) {
-    case 32:
-      LA_RUN_BWD(32);
-    case 64:
-      LA_RUN_BWD(64);
-    default:
-      LA_RUN_BWD(128);
+
+  // Two halves of the (b, h) pairs, each with its own plan, on two streams at
+  // once: the caller's stream and this device's second stream (AuxStream).
+  // On one stream the query-gradient kernel (bound by its own latency and VALU
+  // work) and the key-gradient kernel (bound by its writes) run one after the
+  // other, and each kernel's last round of workgroups leaves compute units
+  // idle; with two, each half's kernels fill the compute units the other's
+  // leave idle, and one half's key kernel can run beside the other's query
+  // kernel.  Measured per call at the 720p chunk: 690 us against 699-701 us
+  // on one stream, the rotary backward 706-707 against 721-724 us, the 480p
+  // stream in one call 1,762 against 1,767 us.  (Forking the second half only
+  // after the first half's query kernel: 783 us.)  Each half keeps the whole
+  // call's query splits per (b, h), so every result is bitwise that of one
+  // stream, and the halves' workspaces tile exactly the one the whole call
+  // needs.  Not taken for the float32 path, for the static scratch, for small
+  // calls, under stream capture (one stream is captured as it is), or when
+  // stage events are asked for (they time the kernels of one stream).
+  const long long P = static_cast<long long>(bh);
+  if (!static_scratch && !empty_block && bwd_two_streams(B, H, N, in_dt) &&
+      (opts == nullptr || opts->stage_events == nullptr)) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    AuxStream* aux = nullptr;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+      aux = aux_stream(stream);
+    const int pa = static_cast<int>(P / 2), pb = static_cast<int>(P - P / 2);
+    const int kreq = opts ? opts->readout_workgroups : 0;
+    const BwdPlan plan_a = make_bwd_plan(1, pa, N, T, d, in_dt, p.qs, kreq, SIZE_MAX,
+                                         rope != nullptr);
+    const BwdPlan plan_b = make_bwd_plan(1, pb, N, T, d, in_dt, p.qs, kreq, SIZE_MAX,
+                                         rope != nullptr);
+    if (aux != nullptr && plan_a.qs == p.qs && plan_b.qs == p.qs &&
+        plan_a.ws_bytes + plan_b.ws_bytes <= need) {
+      // half B starts pa pairs in: its tokens, states and workspace follow half A's
+      const size_t tok = static_cast<size_t>(pa) * N * d;
+      const size_t sts = static_cast<size_t>(pa) * nblk * (static_cast<size_t>(d) * d + d);
+      const size_t st1 = static_cast<size_t>(pa) * (static_cast<size_t>(d) * d + d);
+      const size_t ie = elem_size(in_dt), ge = elem_size(grad_dt);
+      auto at = [](const void* x, size_t bytes) -> void* {
+        return x == nullptr ? nullptr
+                            : static_cast<char*>(const_cast<void*>(x)) + bytes;
+      };
+      auto atf = [](const float* x, size_t n) -> float* {
+        return x == nullptr ? nullptr : const_cast<float*>(x) + n;
+      };
+      std::lock_guard<std::mutex> lock(aux->mu);
+      if (hipEventRecord(aux->fork, stream) != hipSuccess ||
+          hipStreamWaitEvent(aux->s, aux->fork, 0) != hipSuccess)
+        return LA_E_HIP;
+      const int rc_a = run_bwd_d(d, gb, plan_a, q, k, v, states, dout, dstates, dq, dk, dv,
+                                 dstate_in, 1, pa, N, in_dt, eps, workspace, rope, opts, stream);
+      const int rc_b =
+          rc_a != LA_OK
+              ? rc_a
+              : run_bwd_d(d, gb, plan_b, at(q, tok * ie), at(k, tok * ie), at(v, tok * ie),
+                          atf(states, sts), at(dout, tok * ge), atf(dstates, sts),
+                          at(dq, tok * ge), at(dk, tok * ge), at(dv, tok * ge),
+                          atf(dstate_in, st1), 1, pb, N, in_dt, eps,
+                          at(workspace, plan_a.ws_bytes), rope, opts, aux->s);
+      // join even after an error: the caller's stream never runs ahead of
+      // work already on the second stream
+      const bool joined = hipEventRecord(aux->join, aux->s) == hipSuccess &&
+                          hipStreamWaitEvent(stream, aux->join, 0) == hipSuccess;
+      if (rc_a != LA_OK) return rc_a;
+      if (rc_b != LA_OK) return rc_b;
+      return joined ? LA_OK : LA_E_HIP;
+    }
   }
-#undef LA_RUN_BWD
+  return run_bwd_d(d, gb, p, q, k, v, states, dout, dstates, dq, dk, dv, dstate_in, B, H, N,
+                   in_dt, eps, workspace, rope, opts, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -1020,6 +1152,15 @@ int la_backward_workspace_size(int B, int H, int N, int T, int d, int in_dt, siz
   const BwdPlan p = N == 0 ? make_bwd_plan(B, H, 1, 1, d, in_dt, 1, 1, SIZE_MAX)
                            : make_bwd_plan(B, H, N, T, d, in_dt, 0, 0, SIZE_MAX);
   *bytes = p.ws_bytes;
+  return LA_OK;
+}
+
+int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int* count) {
+  int rc = check_shape(B, H, N, d, in_dt, LA_F32);
+  if (rc != LA_OK) return rc;
+  if (T <= 0 || count == nullptr) return LA_E_INVAL;
+  if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
+  *count = bwd_two_streams(B, H, N, in_dt) ? 2 : 1;
   return LA_OK;
 }
 

@@ -272,11 +272,28 @@ int la_global_forward_rope(const void* q, const void* k, const void* v, void* ou
  * any input (LA_E_ALIAS); inputs may overlap each other.  A workspace that is
  * NULL or too small gives LA_E_INVAL.  Other errors as for the forward calls.
  * Results are bitwise reproducible run to run.
+ *
+ * Streams.  A call with bfloat16 inputs and at least 2^20 token-heads (B H N)
+ * runs the two halves of its (b, h) pairs at once: the first on `stream`, the
+ * second on a stream the library creates on the device at the first such call
+ * (default priority, held until the process ends).  The call forks that
+ * stream from `stream` and joins it back, so everything it does is ordered on
+ * `stream` as for any other call.  Calls from several host threads share the
+ * second stream (their halves run there one after another).  Under stream
+ * capture, with stage events (la_launch_opts), in the allocation-free entry
+ * point, or if the second stream cannot be created, a call runs on `stream`
+ * alone.  The results are bitwise the same either way, and the workspace
+ * size does not change.
  */
 
 /* Bytes of workspace a backward call with these arguments needs (T as for
  * la_blockcausal_backward; L or N for the chunk and global calls). */
 int la_backward_workspace_size(int B, int H, int N, int T, int d, int in_dt, size_t* bytes);
+
+/* Streams (1 or 2, in *count) a backward call with these arguments runs its
+ * kernels on when it may use two (see "Streams" above).  Errors as for
+ * la_backward_workspace_size. */
+int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int* count);
 
 /*
  * la_blockcausal_backward - gradients of la_blockcausal_forward.

@@ -314,3 +314,54 @@ def test_backward_degenerate_rows():
     assert np.all(dk[:, :, 450] == 0.0) and np.all(dv[:, :, 450] == 0.0)
     ref = oracle.blockcausal_backward(Q, K, V, bounds_of(N, T), dO, EPS)
     check("backward degenerate rows", [dq, dk, dv], ref[:3], bounds_of(N, T), TOL["bf16"])
+
+
+# ---------------------------------------------------------------------------
+# two streams: a bfloat16 call of at least 2^20 token-heads runs its two halves
+# of (b, h) pairs on the caller's stream and the library's second stream
+
+
+@pytest.mark.parametrize("B,H,N,T,d,rope", [
+    (1, 32, 40000, 40000, 64, False),   # one block, even pair count
+    (1, 5, 300000, 300000, 64, False),  # odd: halves of 2 and 3 pairs
+    (3, 3, 120000, 9000, 128, False),   # several blocks, B > 1, ragged last block
+    (2, 4, 140000, 140000, 32, True),   # rotary
+])
+def test_backward_two_streams_bitwise(B, H, N, T, d, rope):
+    """Against the same call on one stream (stage events keep a call on the
+    caller's stream), bit for bit: each half keeps the whole call's query
+    splits, so nothing differs but the stream.  With a state input and state
+    gradients, and the caller's stream a side stream."""
+    assert B * H * N >= 1 << 20
+    print(f"[two streams] B={B} H={H} N={N} T={T} d={d} rope={rope}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(B * 1000 + H * 10 + d)
+    q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    do = torch.randn((B, H, N, d), generator=g, device="cuda")
+    st_in = torch.rand((B, H, d * d + d), generator=g, device="cuda") * 10
+    grid = (7, 40, 60)
+    if rope:
+        _, states = la.blockcausal_forward_rope(q, k, v, T, *grid, state_in=st_in, eps=EPS)
+    else:
+        _, states = la.blockcausal_forward(q, k, v, T, state_in=st_in, eps=EPS)
+    ds = torch.randn(states.shape, generator=g, device="cuda") * 1e-4
+
+    def run(events):
+        kw = dict(dstates=ds, want_dstate_in=True, eps=EPS, stage_events=events)
+        if rope:
+            return la.blockcausal_backward_rope(q, k, v, states, do, T, *grid, **kw)
+        return la.blockcausal_backward(q, k, v, states, do, T, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one = [t.clone() for t in run(la.StageEvents())]   # one stream
+        two = [t.clone() for t in run(None)]               # two halves on two streams
+        again = [t.clone() for t in run(None)]
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for name, a, b, c in zip(("dq", "dk", "dv", "dstate_in"), one, two, again):
+        assert torch.equal(a, b), name
+        assert torch.equal(b, c), name
+        assert torch.isfinite(b).all(), name
+    report(f"two-stream backward B={B} H={H} N={N} d={d} rope={rope}", bitwise=1.0)
