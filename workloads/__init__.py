@@ -67,9 +67,9 @@ WORKLOADS = {
 
 # Latent token grid (rows, columns) of one frame per workload, for the
 # rotary-position calls: chunk n of a workload starts at frame
-# n * L / (rows * columns).  Config 1 (64 tokens per chunk) is taken as four
-# 4 x 4 frames and config 5 (4,096 tokens) as four 32 x 32 frames; the
-# video workloads use the grids above.
+# n * L / (rows * columns).  The tiny block-causal workload (64 tokens per
+# chunk) is taken as four 4 x 4 frames and the long-horizon one (4,096 tokens)
+# as four 32 x 32 frames; the video workloads use their latent grids.
 GRIDS = {1: (4, 4), 2: (30, 52), 3: (45, 80), 4: (30, 52), 5: (32, 32)}
 ROPE_THETA = 10000.0
 
