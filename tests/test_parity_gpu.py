@@ -295,17 +295,23 @@ def test_degenerate_rows():
     assert out_err(host(out), O_ref) <= TOL["bf16"]
 
 
-def test_bf16_output():
-    B, H, L, d = 1, 4, 3000, 64
+# every readout that writes bfloat16 rows: the sweep (d = 32, 64), the item
+# readout (d = 128, after the split KV reduction or, over 64 heads, the
+# quadrant one) and the float32-input readout
+@pytest.mark.parametrize("B,H,L,d,dtype", [(1, 4, 3000, 64, "bf16"), (1, 4, 3000, 32, "bf16"),
+                                           (1, 4, 3000, 128, "bf16"), (4, 16, 700, 128, "bf16"),
+                                           (1, 2, 1000, 64, "f32")])
+def test_bf16_output(B, H, L, d, dtype):
     Q, K, V = workloads.random_qkv(13, B, H, L, d)
     S_in, z_in = workloads.random_state(14, B, H, d)
     O_ref, _, _ = oracle.chunk_forward(Q, K, V, S_in, z_in, EPS)
-    O, _ = run_chunk(Q, K, V, state_np(S_in, z_in), "bf16", out_dtype=torch.bfloat16)
+    O, _ = run_chunk(Q, K, V, state_np(S_in, z_in), dtype, out_dtype=torch.bfloat16)
     eo = out_err(O, O_ref)
     # against the oracle rounded to bf16 (ties to even): within one ulp plus
     # the float32 arithmetic error, and equal to it almost everywhere
     excess, mismatch = bf16_rounding(O, O_ref, (2, 3), 2e-5)
-    report("bf16 out", out=eo, ulp_excess=excess, mismatch=mismatch)
+    report(f"bf16 out B={B} H={H} L={L} d={d} {dtype} in", out=eo, ulp_excess=excess,
+           mismatch=mismatch)
     assert excess <= 0.0 and mismatch <= BF16_MISMATCH_MAX, (excess, mismatch)
 
 
