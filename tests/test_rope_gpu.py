@@ -389,3 +389,24 @@ def test_rope_zero_eps_ragged():
     es = _states_err(host(st), S_pre, z_pre)
     report("rope eps=0", out=eo, state=es)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("d,dtype", [(32, "bf16"), (128, "bf16"), (64, "f32")])
+def test_rope_bf16_output_every_readout(d, dtype):
+    """bfloat16 rows from the rotary readouts not covered above (d = 32 and
+    128 on bf16 inputs, the float32-input readout): against the oracle
+    rounded to bf16, within one ulp plus the float32 arithmetic error and
+    equal to it almost everywhere."""
+    B, H, L, gh, gw = 1, 3, 2085, 3, 5
+    Q, K, V = workloads.random_qkv(47 + d, B, H, L, d)
+    S_in, z_in = workloads.random_state(48 + d, B, H, d)
+    S_in, z_in = S_in.astype(np.float64), z_in.astype(np.float64)
+    O_ref, _, _ = oracle.rope_chunk_forward(Q, K, V, S_in, z_in, EPS, 7, gh, gw, THETA)
+    st_in = torch.from_numpy(state_np(S_in, z_in)).cuda()
+    out, _ = la.chunk_forward_rope(dev(Q, dtype), dev(K, dtype), dev(V, dtype), st_in, 7, gh, gw,
+                                   THETA, eps=EPS, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    excess, mismatch = bf16_rounding(host(out), O_ref, (2, 3), 2e-5)
+    report(f"rope bf16 out d={d} {dtype} in", out=out_err(host(out), O_ref), ulp_excess=excess,
+           mismatch=mismatch)
+    assert excess <= 0.0 and mismatch <= BF16_MISMATCH_MAX, (excess, mismatch)
