@@ -321,23 +321,24 @@ def test_backward_degenerate_rows():
 # of (b, h) pairs on the caller's stream and the library's second stream
 
 
-@pytest.mark.parametrize("B,H,N,T,d,rope", [
-    (1, 32, 40000, 40000, 64, False),   # one block, even pair count
-    (1, 5, 300000, 300000, 64, False),  # odd: halves of 2 and 3 pairs
-    (3, 3, 120000, 9000, 128, False),   # several blocks, B > 1, ragged last block
-    (2, 4, 140000, 140000, 32, True),   # rotary
+@pytest.mark.parametrize("B,H,N,T,d,rope,gdt", [
+    (1, 32, 40000, 40000, 64, False, torch.float32),   # one block, even pair count
+    (1, 5, 300000, 300000, 64, False, torch.float32),  # odd: halves of 2 and 3 pairs
+    (3, 3, 120000, 9000, 128, False, torch.float32),   # several blocks, B > 1, ragged last block
+    (2, 4, 140000, 140000, 32, True, torch.float32),   # rotary
+    (1, 8, 140000, 70000, 64, False, torch.bfloat16),  # bfloat16 gradients
 ])
-def test_backward_two_streams_bitwise(B, H, N, T, d, rope):
+def test_backward_two_streams_bitwise(B, H, N, T, d, rope, gdt):
     """Against the same call on one stream (stage events keep a call on the
     caller's stream), bit for bit: each half keeps the whole call's query
     splits, so nothing differs but the stream.  With a state input and state
     gradients, and the caller's stream a side stream."""
-    assert B * H * N >= 1 << 20
-    print(f"[two streams] B={B} H={H} N={N} T={T} d={d} rope={rope}", flush=True)
+    assert B * H * N >= 1 << 20 and la.backward_stream_count(B, H, N, T, d) == 2
+    print(f"[two streams] B={B} H={H} N={N} T={T} d={d} rope={rope} grads={gdt}", flush=True)
     g = torch.Generator(device="cuda").manual_seed(B * 1000 + H * 10 + d)
     q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
                for _ in range(3))
-    do = torch.randn((B, H, N, d), generator=g, device="cuda")
+    do = torch.randn((B, H, N, d), generator=g, device="cuda").to(gdt)
     st_in = torch.rand((B, H, d * d + d), generator=g, device="cuda") * 10
     grid = (7, 40, 60)
     if rope:
@@ -364,4 +365,4 @@ def test_backward_two_streams_bitwise(B, H, N, T, d, rope):
         assert torch.equal(a, b), name
         assert torch.equal(b, c), name
         assert torch.isfinite(b).all(), name
-    report(f"two-stream backward B={B} H={H} N={N} d={d} rope={rope}", bitwise=1.0)
+    report(f"two-stream backward B={B} H={H} N={N} d={d} rope={rope} grads={gdt}", bitwise=1.0)
