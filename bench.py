@@ -590,7 +590,8 @@ def bench_rope(args):
         q, k, v = sets[i % len(sets)]
         la.blockcausal_forward_rope(q, k, v, L, f0, gh, gw, workloads.ROPE_THETA,
                                     state_in=state0, out=out, states=states, eps=workloads.EPS,
-                                    kv_splits=args.kv_splits, stage_events=ev)
+                                    kv_splits=args.kv_splits,
+                                    readout_workgroups=args.readout_workgroups, stage_events=ev)
 
     wcalls = warm_up(step, args.warmup, args.min_warmup_s)
     ms = timed_region(step, args.steps)
