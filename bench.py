@@ -59,7 +59,7 @@ PROBE_LIB = os.path.join(ROOT, "block_causal_linear_amd", "libla_probes.so")
 # What defines the readout kernel's HBM traffic at the 720p chunk: its
 # sources, and the planner constants that set its grid.
 KERNEL_SOURCES = ["la_common.h", "row_tiles.h", "readout.h"]
-PLAN_CONSTANTS = ("kSweepWorkgroups", "LA_READOUT_ROWS", "LA_READOUT_STREAM", "LA_READOUT_RUN")
+PLAN_CONSTANTS = ("kSweepWorkgroups", "LA_READOUT_ROWS", "LA_READOUT_STREAM", "run_log2")
 
 
 def log(msg):

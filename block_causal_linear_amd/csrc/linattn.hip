@@ -203,6 +203,7 @@ struct Plan {
   int readout_tpw;     // readout_f32: tokens per workgroup
   int readout_wgs;     // readout workgroups in the grid
   int units_per_block; // sweep readout: four-tile units per block
+  int run_log2;        // sweep readout: log2 of the units per workgroup step
 };
 
 int check_shape(int B, int H, int N, int d, int in_dt, int out_dt) {
@@ -328,8 +329,16 @@ Plan make_plan(int B, int H, int N, int T, int d, int in_dt, int out_dt, int req
     const int unit = 4 * 16 * LA_READOUT_ROWS;
     p.units_per_block = (Tb + unit - 1) / unit;
     long long wgs = readout_request > 0 ? readout_request : kSweepWorkgroups;
-    // workgroup steps take runs of LA_READOUT_RUN units
-    const long long runs = (pairs * p.units_per_block + LA_READOUT_RUN - 1) / LA_READOUT_RUN;
+    // Workgroup steps take runs of one unit when a block has at least as many
+    // units as the grid has workgroups, else runs of two (which halve the
+    // operand rebuilds).  Measured, one box: the 720p chunk 261.0 us with
+    // single units against 263.4-264.8 with runs of two; the 480p chunk
+    // stream 789-791 us per 12 calls with runs of two against 803 with single
+    // units, the 480p global call 60.0 against 61.5, the 480p stream in one
+    // call 685-692 against 695 us.
+    p.run_log2 = p.units_per_block >= wgs ? 0 : 1;
+    const int run = 1 << p.run_log2;
+    const long long runs = (pairs * p.units_per_block + run - 1) / run;
     if (wgs > runs) wgs = runs;
     if (wgs < 1) wgs = 1;
     p.readout_wgs = static_cast<int>(wgs);
@@ -457,10 +466,10 @@ int launch_readout(const Plan& p, const void* q, int out_dt, int B, int H, int N
       constexpr int nt = la::sweep_threads<D>();
       if (out_dt == LA_BF16)
         la::readout_sweep_bf16<D, true><<<p.readout_wgs, nt, 0, stream>>>(
-            qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
+            qq, states, out, N, p.T, p.nblk, p.units_per_block, total, p.run_log2, eps);
       else
         la::readout_sweep_bf16<D, false><<<p.readout_wgs, nt, 0, stream>>>(
-            qq, states, out, N, p.T, p.nblk, p.units_per_block, total, eps);
+            qq, states, out, N, p.T, p.nblk, p.units_per_block, total, p.run_log2, eps);
       return launched();
     }
     return LA_E_UNSUPPORTED;

@@ -22,10 +22,6 @@
 #ifndef LA_READOUT_ROWS
 #define LA_READOUT_ROWS 2
 #endif
-// Consecutive units per workgroup step run in the sweep readout.
-#ifndef LA_READOUT_RUN
-#define LA_READOUT_RUN 2
-#endif
 
 namespace la {
 
@@ -99,7 +95,7 @@ constexpr int sweep_min_waves() {
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void readout_sweep_bf16(
     const uint16_t* __restrict__ q, const float* __restrict__ state, void* __restrict__ out, int N,
-    int T, int nblk, int units_per_block, int total_units, float eps) {
+    int T, int nblk, int units_per_block, int total_units, int run_log2, float eps) {
   using Sh = ReadoutShape<D>;
   using Sw = SweepShape<D>;
   constexpr int E = D * D + D;
@@ -237,13 +233,16 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
     t0 = blk * T + ((rem - blk * upb) * 4 + tw) * Sh::TILE;
     te = min(N, (blk + 1) * T);
   };
-  // Step j of workgroup w takes unit (w + (j / M) G) M + j % M: runs of M
-  // consecutive units, the runs of all workgroups sweeping together.  Within
-  // a run the state usually stays the same; its operands are then neither
-  // reloaded nor rebuilt, and no barrier is taken.
-  constexpr int M = LA_READOUT_RUN;
+  // Step j of workgroup w takes unit (w + (j / M) G) M + j % M with
+  // M = 2^run_log2: runs of M consecutive units, the runs of all workgroups
+  // sweeping together (the planner picks M).  When the next unit reads the
+  // same state its operands are neither reloaded nor rebuilt; the workgroup
+  // still takes a barrier at every unit, which keeps its four waves on the
+  // same unit and so keeps the swept window narrow (without it the waves
+  // drift apart and the readout is slower).
   auto unit_of = [&](int j) {
-    return (static_cast<int>(blockIdx.x) + (j / M) * static_cast<int>(gridDim.x)) * M + j % M;
+    return ((static_cast<int>(blockIdx.x) + (j >> run_log2) * static_cast<int>(gridDim.x))
+            << run_log2) + (j & ((1 << run_log2) - 1));
   };
   int unit = unit_of(0);
   if (unit >= total_units) return;
@@ -263,6 +262,8 @@ __global__ __launch_bounds__(sweep_threads<D>(), sweep_min_waves<D>()) void read
       build(buf);
       lds_barrier();
       built = sb;
+    } else {
+      lds_barrier();  // the waves stay on one unit (see above)
     }
     const int next = unit_of(j + 1);
     const bool more = next < total_units;
