@@ -366,3 +366,55 @@ def test_backward_two_streams_bitwise(B, H, N, T, d, rope, gdt):
         assert torch.equal(b, c), name
         assert torch.isfinite(b).all(), name
     report(f"two-stream backward B={B} H={H} N={N} d={d} rope={rope} grads={gdt}", bitwise=1.0)
+
+
+def test_backward_two_streams_from_two_threads():
+    """Two host threads, each with its own stream, issue large backward calls
+    at once (both fork onto the device's one second stream): every result
+    equals the same call issued alone, bit for bit."""
+    import threading
+
+    B, H, N, T, d = 1, 16, 70000, 70000, 64
+    assert la.backward_stream_count(B, H, N, T, d) == 2
+    g = torch.Generator(device="cuda").manual_seed(77)
+    cases = []
+    for _ in range(2):
+        q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+                   for _ in range(3))
+        do = torch.randn((B, H, N, d), generator=g, device="cuda")
+        _, states = la.blockcausal_forward(q, k, v, T, eps=EPS)
+        cases.append((q, k, v, states, do))
+    torch.cuda.synchronize()
+    alone = []
+    for q, k, v, states, do in cases:
+        grads = la.blockcausal_backward(q, k, v, states, do, T, eps=EPS)[:3]
+        alone.append([t.clone() for t in grads])
+    torch.cuda.synchronize()
+
+    results = [None, None]
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = []
+                for _ in range(3):
+                    q, k, v, states, do = cases[i]
+                    outs = la.blockcausal_backward(q, k, v, states, do, T, eps=EPS)[:3]
+                s.synchronize()
+                results[i] = [t.clone() for t in outs]
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for a, b in zip(alone[i], results[i]):
+            assert torch.equal(a, b)
+    report("two-stream backward from two host threads", bitwise=1.0)
