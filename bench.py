@@ -746,18 +746,24 @@ def bench_backward(args):
                                          workloads.ROPE_THETA, dstates=dstates,
                                          eps=workloads.EPS, dq=dq, dk=dk, dv=dv, dstate_in=dsi,
                                          workspace=ws, kv_splits=args.kv_splits,
+                                         readout_workgroups=args.readout_workgroups,
                                          stage_events=ev)
         else:
             la.blockcausal_backward(q, k, v, states, dout, T, dstates=dstates, eps=workloads.EPS,
                                     dq=dq, dk=dk, dv=dv, dstate_in=dsi, workspace=ws,
-                                    kv_splits=args.kv_splits, stage_events=ev)
+                                    kv_splits=args.kv_splits,
+                                    readout_workgroups=args.readout_workgroups, stage_events=ev)
 
     wcalls = warm_up(step, args.warmup, args.min_warmup_s)
     ms = timed_region(step, args.steps)
     per = sampled_pass(step, max(args.steps, args.sample_calls))
     call_b, q_b, k_b = bwd_bytes(B, H, N, d, C)
-    streams = la.backward_stream_count(B, H, N, T, d)
-    rf = roofline(f"bwd_key_{'rope_' if rope else ''}bf16<{d}>", k_b, per[:, 2])
+    streams = la.backward_stream_count(B, H, N, T, d, rope=rope)
+    # bf16 at d <= 64 without a key-workgroup request: the sweep kernel
+    key_kernel = ("bwd_key_rope_bf16" if rope
+                  else "bwd_key_sweep_bf16" if d <= 64 and args.readout_workgroups <= 0
+                  else "bwd_key_bf16")
+    rf = roofline(f"{key_kernel}<{d}>", k_b, per[:, 2])
     if streams == 2:
         rf["source"] += ("; stage events keep a call on one stream, so this is the kernel of "
                          "a one-stream call, while the timed calls run the two halves of the "
@@ -946,7 +952,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--kv-splits", type=int, default=0)
     ap.add_argument("--readout-workgroups", type=int, default=0,
-                    help="launch option of the forward calls (0: the planner's choice)")
+                    help="launch option: the readout grid of the forward calls, the "
+                         "key-gradient workgroups of the backward calls (0: the planner's "
+                         "choice)")
     ap.add_argument("--workload", default="chunk720p",
                     choices=["chunk720p", "ceiling"] + list(OTHER) + list(BACKWARD)
                     + list(TCONV) + list(ROPE))

@@ -71,7 +71,7 @@ _SIGNATURES = {
     "la_blockcausal_forward_rope_ex": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                        _I, _I, _I, _F, ctypes.POINTER(LaunchOpts), _P],
     "la_backward_workspace_size": [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)],
-    "la_backward_stream_count": [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)],
+    "la_backward_stream_count": [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)],
     "la_blockcausal_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _I, _F, _P, _Z, _P],
     "la_blockcausal_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -390,13 +390,15 @@ def _prepare_grads(q, k, v, dout, dq, dk, dv):
     return grads
 
 
-def backward_stream_count(B, H, N, T, d, in_dtype=torch.bfloat16):
-    """Streams (1 or 2) a backward call of this shape runs on when it may use
-    two: the second half of its (b, h) pairs goes to the library's second
-    stream, joined back before the call's work completes on the caller's."""
+def backward_stream_count(B, H, N, T, d, in_dtype=torch.bfloat16, rope=False):
+    """Streams (1 or 2) a backward call of this shape (rope: the rotary
+    backward) runs on when it may use two: the second half of its (b, h)
+    pairs goes to the library's second stream, joined back before the call's
+    work completes on the caller's."""
     c = ctypes.c_int()
     _check(lib().la_backward_stream_count(B, H, N, max(int(T), 1), d, _DTYPE[in_dtype],
-                                          ctypes.byref(c)), "la_backward_stream_count")
+                                          int(bool(rope)), ctypes.byref(c)),
+           "la_backward_stream_count")
     return c.value
 
 

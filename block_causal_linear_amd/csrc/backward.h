@@ -504,6 +504,238 @@ __global__ __launch_bounds__(256, bwd_key_min_waves<D>()) void bwd_key_bf16(
 }
 
 // ---------------------------------------------------------------------------
+// bwd_key_sweep_bf16: the same dK and dV on the forward readout's sweep
+// schedule (bf16 keys and values, d <= 64).  A unit is four wave tiles of RB
+// 16-token row blocks inside one block; step j of workgroup w takes unit
+// w + j G, so the whole grid moves through the (b, h, block, token) space
+// together, one narrow window of keys, values and gradients at a time (runs
+// of two consecutive units per step, which the forward readout takes on
+// short blocks, measured slower here: 1,782 against 1,693 us per call on the
+// 480p stream in one call).  The two operand
+// sets of R (rows and columns, bf16 hi/lo) and r are rebuilt only when a
+// step's block differs from the last one, from slices of R that each wave
+// loads one step ahead into registers, into one of two LDS buffers; a
+// barrier at every step keeps the workgroup's four waves on one unit.  Per
+// token the arithmetic, down to the order of the MFMAs into each
+// accumulator, is that of bwd_key_bf16: the results are bitwise equal.
+// (LDS: 16 / 64 KB per workgroup at d = 32 / 64.)
+#ifndef LA_BWDK_SWEEP_ROWS
+#define LA_BWDK_SWEEP_ROWS 2  // 16-token row blocks per wave tile
+#endif
+template <int D>
+struct KeySweep {
+  static constexpr int RB = LA_BWDK_SWEEP_ROWS;
+  static constexpr int TILE = 16 * RB;   // tokens per wave tile
+  static constexpr int UNIT = 4 * TILE;  // tokens per unit
+  static constexpr int MIN_WAVES = 2;    // waves per SIMD = workgroups per CU
+};
+
+template <int D, bool GO_BF16>
+__global__ __launch_bounds__(256, KeySweep<D>::MIN_WAVES) void bwd_key_sweep_bf16(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ R,
+    void* __restrict__ dk, void* __restrict__ dv, int N, int T, int nblk, int units_per_block,
+    int total_units) {
+  static_assert(D <= 64, "the key sweep is built for d <= 64");
+  using Sh = RowTile<D>;
+  using Kw = KeySweep<D>;
+  constexpr int KS = Sh::KS, NBK = Sh::NBK, W = Sh::W, GRP = Sh::GRP, UPR = Sh::UPR;
+  constexpr int RB = Kw::RB, TILE = Kw::TILE;
+  constexpr int E = D * D + D;
+  constexpr int NF = Sh::NF;
+  constexpr int GE = GO_BF16 ? 2 : 4;
+  constexpr int PAIRS = KS * NBK;                  // (k-step, column block) pairs
+  constexpr int PW = PAIRS >= 4 ? PAIRS / 4 : 1;   // pairs per producer wave
+  static_assert(PAIRS % PW == 0 && NBK % PW == 0 && W % PW == 0, "pair split");
+  using vecP = float __attribute__((ext_vector_type(PW)));
+  __shared__ uint4 rrow[2][NF][kWave];  // rows of R, hi/lo
+  __shared__ uint4 rcol[2][NF][kWave];  // columns of R, hi/lo
+  __shared__ float rsh[2][D];           // r
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  const int sig = 4 * (n & 3) + (n >> 2);
+
+  // this wave's pairs: k-step ps, column blocks pc0 .. pc0 + PW - 1 (adjacent
+  // columns of one store group, acc_col)
+  const bool producer = wave * PW < PAIRS;
+  const int p0 = producer ? wave * PW : 0;
+  const int ps = p0 / NBK, pc0 = p0 % NBK;
+
+  float4 rraw[PW][2];  // rows of R: 8 consecutive values of row acc_col(nb, n)
+  vecP craw[8];        // columns of R: rows 32 ps + 8 g + j, PW adjacent columns
+  float rval = 0.f;
+  auto load_r = [&](int sb) {  // sb = (b H + h) nblk + block
+    const float* rs = R + static_cast<size_t>(sb) * E;
+    if (producer) {
+#pragma unroll
+      for (int c = 0; c < PW; ++c) {
+        const float* src = rs + acc_col<D>(pc0 + c, n) * D + 32 * ps + 8 * g;
+        rraw[c][0] = *reinterpret_cast<const float4*>(src);
+        rraw[c][1] = *reinterpret_cast<const float4*>(src + 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        craw[j] = *reinterpret_cast<const vecP*>(rs + (32 * ps + 8 * g + j) * D +
+                                                 acc_col<D>(pc0, n));
+    }
+    if (tid < D) rval = rs[D * D + tid];
+  };
+  auto build = [&](int buf) {
+    if (producer) {
+#pragma unroll
+      for (int c = 0; c < PW; ++c) {
+        const int p = ps * NBK + pc0 + c;
+        uint32_t h[4], l[4];
+        split_bf16x2(rraw[c][0].x, rraw[c][0].y, &h[0], &l[0]);
+        split_bf16x2(rraw[c][0].z, rraw[c][0].w, &h[1], &l[1]);
+        split_bf16x2(rraw[c][1].x, rraw[c][1].y, &h[2], &l[2]);
+        split_bf16x2(rraw[c][1].z, rraw[c][1].w, &h[3], &l[3]);
+        rrow[buf][2 * p][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+        rrow[buf][2 * p + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) split_bf16x2(craw[j][c], craw[j + 1][c], &h[j / 2], &l[j / 2]);
+        rcol[buf][2 * p][lane] = make_uint4(h[0], h[1], h[2], h[3]);
+        rcol[buf][2 * p + 1][lane] = make_uint4(l[0], l[1], l[2], l[3]);
+      }
+    }
+    if (tid < D) rsh[buf][tid] = rval;
+  };
+  // Rows past the end of the block load its last row (their outputs are never
+  // stored: every output row depends on its own input row only).
+  auto load_kv = [&](uint4 (&ka)[RB][KS], uint4 (&va)[RB][KS], int bh, int t0, int te) {
+    const size_t row0 = static_cast<size_t>(bh) * N;
+    const uint4* kb = reinterpret_cast<const uint4*>(k + row0 * D);
+    const uint4* vb = reinterpret_cast<const uint4*>(v + row0 * D);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int tok = min(t0 + 16 * r + sig, te - 1);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        ka[r][s] = kb[static_cast<size_t>(tok) * UPR + 4 * s + g];
+        va[r][s] = vb[static_cast<size_t>(tok) * UPR + 4 * s + g];
+      }
+    }
+  };
+  auto consume = [&](int buf, const uint4 (&ka)[RB][KS], const uint4 (&va)[RB][KS], int bh,
+                     int t0, int te) {
+    // the wave tile's rows inside the block; stores past them are dropped
+    const int valid = max(0, min(TILE, te - t0));
+    const size_t e0 = (static_cast<size_t>(bh) * N + t0) * D;
+    const rsrc_t rdk = tile_rsrc(dk, e0, GE, valid * D * GE);
+    const rsrc_t rdv = tile_rsrc(dv, e0, GE, valid * D * GE);
+    // each operand fragment read from LDS serves the RB row blocks
+    uint4 kp[RB][KS];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kp[r][s] = relu_bf16x8(ka[r][s]);
+    f32x4 acck[RB][NBK], accv[RB][NBK];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) {
+        acck[r][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accv[r][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NBK; ++nb) {
+        const int f = 2 * (s * NBK + nb);
+        const uint4 rh = rrow[buf][f][lane], rl = rrow[buf][f + 1][lane];
+        const uint4 ch = rcol[buf][f][lane], cl = rcol[buf][f + 1][lane];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          acck[r][nb] = mfma_16x16x32(va[r][s], rh, acck[r][nb]);
+          acck[r][nb] = mfma_16x16x32(va[r][s], rl, acck[r][nb]);
+          accv[r][nb] = mfma_16x16x32(kp[r][s], ch, accv[r][nb]);
+          accv[r][nb] = mfma_16x16x32(kp[r][s], cl, accv[r][nb]);
+        }
+      }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      f32x4 kacc[NBK];
+      rows_to_acc<D>(kp[r], kacc, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = 16 * r + 4 * i + g;  // row within the wave tile
+#pragma unroll
+        for (int gr = 0; gr < GRP; ++gr) {
+          float xk[W], xv[W];
+          const int col = 16 * W * gr + W * n;
+#pragma unroll
+          for (int e = 0; e < W; ++e) {
+            const int nb = gr * W + e;
+            const float rr = rsh[buf][col + e];
+            const float gk = acck[r][nb][i] + rr;
+            xk[e] = kacc[nb][i] > 0.f ? gk : 0.f;
+            xv[e] = accv[r][nb][i];
+          }
+          store_row_buf<W, GO_BF16, true>(rdk, (tt * D + col) * GE, xk);
+          store_row_buf<W, GO_BF16, true>(rdv, (tt * D + col) * GE, xv);
+        }
+      }
+    }
+  };
+
+  // unit -> (b, h), block, this wave's tile, end of the block
+  auto locate = [&](int u, int& bh, int& sb, int& t0, int& te) {
+    const int upb = units_per_block;
+    bh = u / (nblk * upb);
+    const int rem = u - bh * nblk * upb;
+    const int blk = rem / upb;
+    sb = bh * nblk + blk;
+    t0 = blk * T + ((rem - blk * upb) * 4 + wave) * TILE;
+    te = min(N, (blk + 1) * T);
+  };
+  // The unit index is uniform across the workgroup: every wave takes the
+  // same barriers, and waves whose tile lies past the block store nothing.
+  int unit = blockIdx.x;
+  if (unit >= total_units) return;
+  int bh, sb, t0, te;
+  locate(unit, bh, sb, t0, te);
+  uint4 ka[RB][KS], va[RB][KS];
+  load_r(sb);
+  load_kv(ka, va, bh, t0, te);
+  int built = -1;  // the block whose operands the current buffer holds
+  int buf = 1;
+  for (;;) {
+    // buffer buf ^ 1 was last read before the previous build's barrier,
+    // which every wave has passed
+    if (sb != built) {
+      buf ^= 1;
+      build(buf);
+      built = sb;
+    }
+    lds_barrier();
+    const int next = unit + static_cast<int>(gridDim.x);
+    const bool more = next < total_units;
+    const int nu = more ? next : unit;
+    int nbh, nsb, nt0, nte;
+    locate(nu, nbh, nsb, nt0, nte);
+    uint4 kn[RB][KS], vn[RB][KS];
+    if (nsb != sb) load_r(nsb);
+    load_kv(kn, vn, nbh, nt0, nte);
+    consume(buf, ka, va, bh, t0, te);
+    if (!more) break;
+    unit = next;
+    bh = nbh;
+    sb = nsb;
+    t0 = nt0;
+    te = nte;
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        ka[r][s] = kn[r][s];
+        va[r][s] = vn[r][s];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // float32 inputs: plain VALU versions of the two kernels above (the float32
 // path is for exactness checks and small problems).  Same grids and outputs.
 template <int D, bool GO_BF16>

@@ -31,7 +31,7 @@ static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES]
 
 namespace {
 
-constexpr int kAbiVersion = 11;
+constexpr int kAbiVersion = 12;
 
 // The address of `scratch` on the device of `stream` (the current device for
 // the null stream), looked up on that device's first call and kept.
@@ -155,6 +155,18 @@ int bwd_key_capacity(int d, bool rope) {
 constexpr int kRopeMaxTokens = 1 << 22;
 // float32 backward kernels: workgroups over contiguous token ranges.
 constexpr int kBwdF32TargetWorkgroups = 512;
+// The key-gradient sweep (bf16, d <= 64, no rotary) and its grid: two
+// workgroups per CU (64 KB of LDS each at d = 64).  Measured per call: the
+// 720p chunk 664 us with 512 workgroups, 684 with 256, 703 with 384; the 480p
+// stream in one call 1,693, 1,680 and 1,821 us.  LA_BWDK_SWEEP 0 keeps the
+// work-item kernel for every call.
+#ifndef LA_BWDK_SWEEP
+#define LA_BWDK_SWEEP 1
+#endif
+#ifndef LA_BWDK_SWEEP_WGS
+#define LA_BWDK_SWEEP_WGS 512
+#endif
+constexpr int kBwdKeySweepWorkgroups = LA_BWDK_SWEEP_WGS;
 // Token-heads (B H N) from which a bfloat16 backward call runs its two halves
 // of (b, h) pairs on two streams; below it the fork and join cost more than
 // the overlap gains.
@@ -545,10 +557,18 @@ struct BwdPlan {
   int qgrid;       // its grid (bf16: persistent, <= items)
   int qtps;        // float32: tokens per split
   int ks;          // key-gradient items per block
-  int kgrid;
+  int kgrid;       // its grid (bf16: persistent)
   int ktps;
+  bool ksweep;     // bwd_key_sweep_bf16 instead of the work items
+  int kupb;        // its units per block
   size_t ws_bytes; // workspace the plan needs
 };
+
+// Whether the planner gives a backward call the key-gradient sweep (bf16
+// inputs at d <= 64 without rotary and without a key-workgroup request).
+bool bwd_key_sweep(int d, int in_dt, bool rope) {
+  return LA_BWDK_SWEEP && in_dt == LA_BF16 && d <= 64 && !rope;
+}
 
 // ws_avail: the caller's workspace size (SIZE_MAX when planning the size).
 // rope: the rotary kernels (the key kernel's grid differs; the workspace,
@@ -618,6 +638,14 @@ BwdPlan make_bwd_plan(int B, int H, int N, int T, int d, int in_dt, int qrequest
     p.ktps = (per + tile - 1) / tile * tile;
     p.ks = (Tb + p.ktps - 1) / p.ktps;
   }
+  // bf16 at d <= 64 without a key-item request: the sweep
+  if (bwd_key_sweep(d, in_dt, rope) && krequest <= 0) {
+    const int unit = la::KeySweep<64>::UNIT;
+    p.ksweep = true;
+    p.kupb = (Tb + unit - 1) / unit;
+    const long long units = pairs * p.kupb;
+    p.kgrid = static_cast<int>(units < kBwdKeySweepWorkgroups ? units : kBwdKeySweepWorkgroups);
+  }
   return p;
 }
 
@@ -676,6 +704,15 @@ int launch_bwd_key(const BwdPlan& p, const void* k, const void* v, const float* 
           p.ktps, *rope);
     }
     return launched();
+  }
+  if constexpr (D <= 64) {
+    if (p.ksweep) {
+      const int total = B * H * p.nblk * p.kupb;
+      la::bwd_key_sweep_bf16<D, GO_BF16><<<p.kgrid, la::RowTile<D>::NT, 0, stream>>>(
+          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), R, dk, dv, N, p.T,
+          p.nblk, p.kupb, total);
+      return launched();
+    }
   }
   if (in_dt == LA_BF16) {
     const int items = B * H * p.nblk * p.ks;
@@ -739,11 +776,13 @@ int check_rope(const la::RopeGrid* rope, int N) {
 
 // Whether a backward call of this shape runs its two halves of (b, h) pairs on
 // two streams (outside stream capture, without stage events, with the
-// device's second stream available; see backward()).
-bool bwd_two_streams(int B, int H, int N, int in_dt) {
+// device's second stream available; see backward()).  Only calls whose
+// key-gradient kernel works on items: the sweep takes the whole GPU by itself
+// (the 720p chunk: 666 us per call on one stream, 686 us with two).
+bool bwd_two_streams(int B, int H, int N, int d, int in_dt, bool rope) {
   const long long P = static_cast<long long>(B) * H;
-  return in_dt == LA_BF16 && P >= 2 && P - P / 2 <= 65535 && N > 0 &&
-         P * static_cast<long long>(N) >= kBwdSplitMinTokens;
+  return in_dt == LA_BF16 && !bwd_key_sweep(d, in_dt, rope) && P >= 2 && P - P / 2 <= 65535 &&
+         N > 0 && P * static_cast<long long>(N) >= kBwdSplitMinTokens;
 }
 
 // run_bwd for the head dimension and gradient type of a call.
@@ -855,17 +894,19 @@ int backward(const void* q, const void* k, const void* v, const float* states, c
   // other, and each kernel's last round of workgroups leaves compute units
   // idle; with two, each half's kernels fill the compute units the other's
   // leave idle, and one half's key kernel can run beside the other's query
-  // kernel.  Measured per call at the 720p chunk: 690 us against 699-701 us
-  // on one stream, the rotary backward 706-707 against 721-724 us, the 480p
-  // stream in one call 1,762 against 1,767 us.  (Forking the second half only
-  // after the first half's query kernel: 783 us.)  Each half keeps the whole
+  // kernel.  Measured per call with the work-item key kernel: the 720p chunk
+  // 690 us against 699-701 us on one stream, the rotary backward 706-707
+  // against 721-724 us, the 480p stream in one call 1,762 against 1,767 us.
+  // (Forking the second half only after the first half's query kernel:
+  // 783 us.)  Calls that take the key-gradient sweep stay on one stream
+  // (bwd_two_streams).  Each half keeps the whole
   // call's query splits per (b, h), so every result is bitwise that of one
   // stream, and the halves' workspaces tile exactly the one the whole call
   // needs.  Not taken for the float32 path, for the static scratch, for small
   // calls, under stream capture (one stream is captured as it is), or when
   // stage events are asked for (they time the kernels of one stream).
   const long long P = static_cast<long long>(bh);
-  if (!static_scratch && !empty_block && bwd_two_streams(B, H, N, in_dt) &&
+  if (!static_scratch && !empty_block && bwd_two_streams(B, H, N, d, in_dt, rope != nullptr) &&
       (opts == nullptr || opts->stage_events == nullptr)) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     AuxStream* aux = nullptr;
@@ -1164,12 +1205,13 @@ int la_backward_workspace_size(int B, int H, int N, int T, int d, int in_dt, siz
   return LA_OK;
 }
 
-int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int* count) {
+int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int rotary,
+                             int* count) {
   int rc = check_shape(B, H, N, d, in_dt, LA_F32);
   if (rc != LA_OK) return rc;
   if (T <= 0 || count == nullptr) return LA_E_INVAL;
   if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
-  *count = bwd_two_streams(B, H, N, in_dt) ? 2 : 1;
+  *count = bwd_two_streams(B, H, N, d, in_dt, rotary != 0) ? 2 : 1;
   return LA_OK;
 }
 

@@ -274,7 +274,10 @@ int la_global_forward_rope(const void* q, const void* k, const void* v, void* ou
  * Results are bitwise reproducible run to run.
  *
  * Streams.  A call with bfloat16 inputs and at least 2^20 token-heads (B H N)
- * runs the two halves of its (b, h) pairs at once: the first on `stream`, the
+ * whose key-gradient kernel works on items (d = 128, and the rotary calls at
+ * every d; at d <= 64 the plain calls take the key-gradient sweep, which
+ * fills the GPU by itself) runs the two halves of its (b, h) pairs at once:
+ * the first on `stream`, the
  * second on a stream the library creates on the device at the first such call
  * (default priority, held until the process ends).  The call forks that
  * stream from `stream` and joins it back, so everything it does is ordered on
@@ -291,9 +294,10 @@ int la_global_forward_rope(const void* q, const void* k, const void* v, void* ou
 int la_backward_workspace_size(int B, int H, int N, int T, int d, int in_dt, size_t* bytes);
 
 /* Streams (1 or 2, in *count) a backward call with these arguments runs its
- * kernels on when it may use two (see "Streams" above).  Errors as for
- * la_backward_workspace_size. */
-int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int* count);
+ * kernels on when it may use two (see "Streams" above); rotary != 0 asks for
+ * la_blockcausal_backward_rope.  Errors as for la_backward_workspace_size. */
+int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int rotary,
+                             int* count);
 
 /*
  * la_blockcausal_backward - gradients of la_blockcausal_forward.

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 11
+    assert la.abi_version() == 12
     for code in range(7):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
@@ -419,19 +419,25 @@ def test_backward_noalloc_scratch_limit():
 
 
 def test_backward_stream_count():
-    """Two streams for large bfloat16 calls, one otherwise; shape errors as
-    for the workspace size."""
-    assert la.backward_stream_count(1, 32, 75600, 75600, 64) == 2        # the 720p chunk
-    assert la.backward_stream_count(1, 16, 12 * 32760, 32760, 64) == 2   # the 480p stream
-    assert la.backward_stream_count(1, 32, 75600, 75600, 64, torch.float32) == 1
-    assert la.backward_stream_count(1, 1, 1 << 22, 1 << 22, 64) == 1     # one (b, h) pair
-    assert la.backward_stream_count(1, 2, (1 << 19) - 1, 1000, 64) == 1  # below 2^20 token-heads
-    assert la.backward_stream_count(1, 2, 1 << 19, 1000, 64) == 2
-    assert la.backward_stream_count(1, 8, 0, 1, 64) == 1                 # no tokens
+    """Two streams for large bfloat16 calls whose key-gradient kernel works on
+    items (d = 128, rotary), one otherwise (the key-gradient sweep at d <= 64
+    fills the GPU by itself); shape errors as for the workspace size."""
+    assert la.backward_stream_count(1, 32, 75600, 75600, 64) == 1        # the 720p chunk: sweep
+    assert la.backward_stream_count(1, 32, 75600, 75600, 32) == 1
+    assert la.backward_stream_count(1, 32, 75600, 75600, 64, rope=True) == 2
+    assert la.backward_stream_count(1, 32, 75600, 75600, 32, rope=True) == 2
+    assert la.backward_stream_count(1, 16, 12 * 32760, 32760, 64, rope=True) == 2
+    assert la.backward_stream_count(4, 16, 40 * 4096, 4096, 128) == 2    # the long-horizon stream
+    assert la.backward_stream_count(4, 16, 40 * 4096, 4096, 128, torch.float32) == 1
+    assert la.backward_stream_count(1, 1, 1 << 22, 1 << 22, 128) == 1    # one (b, h) pair
+    assert la.backward_stream_count(1, 2, (1 << 19) - 1, 1000, 128) == 1  # below 2^20 token-heads
+    assert la.backward_stream_count(1, 2, 1 << 19, 1000, 128) == 2
+    assert la.backward_stream_count(1, 8, 0, 1, 128) == 1                 # no tokens
     L_ = la.lib()
     c = ctypes.c_int(-1)
-    assert L_.la_backward_stream_count(1, 2, 100, 0, 64, BF16, ctypes.byref(c)) == la.LA_E_INVAL
-    assert L_.la_backward_stream_count(1, 2, 100, 100, 48, BF16, ctypes.byref(c)) == \
+    assert L_.la_backward_stream_count(1, 2, 100, 0, 64, BF16, 0, ctypes.byref(c)) == \
+        la.LA_E_INVAL
+    assert L_.la_backward_stream_count(1, 2, 100, 100, 48, BF16, 0, ctypes.byref(c)) == \
         la.LA_E_UNSUPPORTED
-    assert L_.la_backward_stream_count(1, 2, 100, 100, 64, BF16, None) == la.LA_E_INVAL
+    assert L_.la_backward_stream_count(1, 2, 100, 100, 64, BF16, 0, None) == la.LA_E_INVAL
     assert c.value == -1

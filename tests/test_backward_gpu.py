@@ -284,6 +284,41 @@ def test_backward_splits_and_reproducibility():
         assert max(errs) <= 1e-5, errs
 
 
+@pytest.mark.parametrize("B,H,N,T,d,gdt", [
+    (1, 4, 3000, 3000, 64, torch.float32),     # one block, ragged last unit
+    (2, 3, 2085, 500, 64, torch.float32),      # several blocks, short last block, B > 1
+    (1, 2, 777, 7, 64, torch.float32),         # 7-token blocks: most wave tiles store nothing
+    (1, 2, 100, 100, 64, torch.float32),       # less than one unit: a one-workgroup grid
+    (1, 3, 5000, 1200, 32, torch.bfloat16),    # d = 32, bfloat16 gradients
+    (1, 32, 40000, 40000, 64, torch.float32),  # 10,016 units over the 512-workgroup grid
+    (1, 8, 75600, 75600, 64, torch.float32),   # a block longer than the grid's 512 units
+])
+def test_backward_key_sweep_matches_items(B, H, N, T, d, gdt):
+    """bf16 inputs at d <= 64 take the key-gradient sweep; a key-workgroup
+    request takes the work-item kernel.  Both compute every token's dk and dv
+    with the same operands and the same MFMA order: bit for bit equal (and
+    dq, dstate_in untouched by the choice).  Both run on one stream."""
+    print(f"[key sweep] B={B} H={H} N={N} T={T} d={d} grads={gdt}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(B * 100 + H * 10 + d + N)
+    q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+               for _ in range(3))
+    do = torch.randn((B, H, N, d), generator=g, device="cuda").to(gdt)
+    st_in = torch.rand((B, H, d * d + d), generator=g, device="cuda") * 10
+    _, states = la.blockcausal_forward(q, k, v, T, state_in=st_in, eps=EPS)
+    ds = torch.randn(states.shape, generator=g, device="cuda") * 1e-4
+    kw = dict(dstates=ds, want_dstate_in=True, eps=EPS)
+    sweep = [t.clone() for t in la.blockcausal_backward(q, k, v, states, do, T, **kw)]
+    items = [t.clone() for t in la.blockcausal_backward(q, k, v, states, do, T,
+                                                       readout_workgroups=1024, **kw)]
+    again = [t.clone() for t in la.blockcausal_backward(q, k, v, states, do, T, **kw)]
+    torch.cuda.synchronize()
+    for name, a, b, c in zip(("dq", "dk", "dv", "dstate_in"), sweep, items, again):
+        assert torch.isfinite(a).all(), name
+        assert torch.equal(a, b), name
+        assert torch.equal(a, c), name
+    report(f"key sweep against work items B={B} H={H} N={N} T={T} d={d}", bitwise=1.0)
+
+
 def test_backward_zero_eps_ragged():
     """eps = 0 (every denominator kept > 0 by one positive feature per row):
     the rows past the end of a ragged last tile and block stay out of every
@@ -322,18 +357,18 @@ def test_backward_degenerate_rows():
 
 
 @pytest.mark.parametrize("B,H,N,T,d,rope,gdt", [
-    (1, 32, 40000, 40000, 64, False, torch.float32),   # one block, even pair count
-    (1, 5, 300000, 300000, 64, False, torch.float32),  # odd: halves of 2 and 3 pairs
+    (1, 16, 70000, 70000, 128, False, torch.float32),  # one block, even pair count
+    (1, 5, 300000, 300000, 64, True, torch.float32),   # odd: halves of 2 and 3 pairs
     (3, 3, 120000, 9000, 128, False, torch.float32),   # several blocks, B > 1, ragged last block
-    (2, 4, 140000, 140000, 32, True, torch.float32),   # rotary
-    (1, 8, 140000, 70000, 64, False, torch.bfloat16),  # bfloat16 gradients
+    (2, 4, 140000, 140000, 32, True, torch.float32),   # rotary at d = 32
+    (1, 8, 140000, 70000, 64, True, torch.bfloat16),   # bfloat16 gradients
 ])
 def test_backward_two_streams_bitwise(B, H, N, T, d, rope, gdt):
     """Against the same call on one stream (stage events keep a call on the
     caller's stream), bit for bit: each half keeps the whole call's query
     splits, so nothing differs but the stream.  With a state input and state
     gradients, and the caller's stream a side stream."""
-    assert B * H * N >= 1 << 20 and la.backward_stream_count(B, H, N, T, d) == 2
+    assert B * H * N >= 1 << 20 and la.backward_stream_count(B, H, N, T, d, rope=rope) == 2
     print(f"[two streams] B={B} H={H} N={N} T={T} d={d} rope={rope} grads={gdt}", flush=True)
     g = torch.Generator(device="cuda").manual_seed(B * 1000 + H * 10 + d)
     q, k, v = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
@@ -374,7 +409,7 @@ def test_backward_two_streams_from_two_threads():
     equals the same call issued alone, bit for bit."""
     import threading
 
-    B, H, N, T, d = 1, 16, 70000, 70000, 64
+    B, H, N, T, d = 1, 16, 70000, 70000, 128
     assert la.backward_stream_count(B, H, N, T, d) == 2
     g = torch.Generator(device="cuda").manual_seed(77)
     cases = []
