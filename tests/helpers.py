@@ -1,7 +1,9 @@
 """Comparison and transfer helpers for the GPU parity tests (no attention
 arithmetic here)."""
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -88,3 +90,26 @@ def bf16_rounding(got, ref, axes, rel_err):
 
 # elements of a bfloat16 result that may differ from the rounded oracle
 BF16_MISMATCH_MAX = 0.02
+
+
+def draw_workers():
+    """Host threads for drawing test inputs: the cores this process may use,
+    at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def drawn_chunks(draw, chunks, ahead=8):
+    """Yield (n, draw(n)) for each n of `chunks`, in order, while up to
+    `ahead` later draws run on a thread pool.  Every chunk's tensors come
+    from generators seeded by the chunk's own index, so the values do not
+    depend on the order or thread the draws run in; numpy fills large arrays
+    without holding the interpreter lock, so the draws run in parallel."""
+    chunks = list(chunks)
+    with ThreadPoolExecutor(min(draw_workers(), max(1, ahead))) as ex:
+        futs = {}
+        nxt = 0
+        for i, n in enumerate(chunks):
+            while nxt < len(chunks) and nxt < i + max(1, ahead):
+                futs[nxt] = ex.submit(draw, chunks[nxt])
+                nxt += 1
+            yield n, futs.pop(i).result()

@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import (BF16_MISMATCH_MAX, TOL, bf16_rounding, dev, host, out_err, report,
-                     state_err, state_np)
+from helpers import (BF16_MISMATCH_MAX, TOL, bf16_rounding, dev, drawn_chunks, host, out_err,
+                     report, state_err, state_np)
 
 import block_causal_linear_amd as la
 
@@ -161,8 +161,7 @@ def test_stream_480p_1min():
     state = la.new_state(w.B, w.H, w.d)
     KVs, ks = [], []
     worst = [0.0, 0.0, 0.0]
-    for n in range(w.chunks):
-        Q, K, V = workloads.chunk_qkv(w, n)
+    for n, (Q, K, V) in drawn_chunks(lambda c: workloads.chunk_qkv(w, c), range(w.chunks)):
         out, state = la.chunk_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), state,
                                       state_out=state, eps=EPS)
         KV, k = oracle.kv_of_block(K, V)
@@ -181,19 +180,33 @@ def test_stream_480p_1min():
 
 def test_long_horizon_d128():
     """40 chunks, B=4, H=16, d=128, 1% outlier rows x8; per-chunk drift of
-    S, z and O against the fp64 carried state."""
+    S and z (every head) and O against the fp64 carried state.  O is
+    compared on every head at the first and last chunk and on eight sampled
+    (b, h) pairs at the others (the oracle's chunk step, composed of its KV
+    and readout steps, with the readout on those pairs)."""
     w = workloads.WORKLOADS[5]
+    heads = [(0, 0), (0, 13), (1, 6), (1, 15), (2, 0), (2, 9), (3, 2), (3, 15)]
+    bi = [b for b, _ in heads]
+    hi = [h for _, h in heads]
+    bt = torch.tensor(bi, device="cuda")
+    ht = torch.tensor(hi, device="cuda")
     state = la.new_state(w.B, w.H, w.d)
     S = np.zeros((w.B, w.H, w.d, w.d))
     z = np.zeros((w.B, w.H, w.d))
     worst = 0.0
-    for n in range(w.chunks):
-        Q, K, V = workloads.chunk_qkv(w, n)
+    for n, (Q, K, V) in drawn_chunks(lambda c: workloads.chunk_qkv(w, c), range(w.chunks)):
         out, state = la.chunk_forward(dev(Q, "bf16"), dev(K, "bf16"), dev(V, "bf16"), state,
                                       state_out=state, eps=EPS)
-        O_ref, S, z = oracle.chunk_forward(Q, K, V, S, z, EPS)
+        KV, kk = oracle.kv_of_block(K, V)
+        S, z = S + KV, z + kk
+        if n in (0, w.chunks - 1):
+            O_ref = oracle.readout(Q, S, z, EPS)
+            got = out
+        else:
+            O_ref = oracle.readout(Q[bi, hi][None], S[bi, hi][None], z[bi, hi][None], EPS)
+            got = out[bt, ht][None]
         torch.cuda.synchronize()
-        eo = out_err(host(out), O_ref)
+        eo = out_err(host(got), O_ref)
         es, ez = state_err(host(state), S, z)
         report(f"long-horizon chunk {n}", out=eo, S=es, z=ez)
         worst = max(worst, eo, es, ez)
@@ -413,8 +426,7 @@ def test_blockcausal_480p_1min_one_call():
     q = torch.empty((w.B, w.H, N, w.d), dtype=torch.bfloat16, device="cuda")
     k, v = torch.empty_like(q), torch.empty_like(q)
     blocks = []
-    for n in range(w.chunks):
-        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
+    for n, (Qn, Kn, Vn) in drawn_chunks(lambda c: workloads.chunk_qkv(w, c), range(w.chunks)):
         sl = slice(n * T, (n + 1) * T)
         q[:, :, sl], k[:, :, sl], v[:, :, sl] = dev(Qn, "bf16"), dev(Kn, "bf16"), dev(Vn, "bf16")
         blocks.append((Qn, Kn, Vn))
@@ -438,28 +450,32 @@ def test_blockcausal_480p_1min_one_call():
 def test_blockcausal_long_horizon_d128_one_call():
     """The 40-block d = 128 long-horizon sequence (B=4, H=16, 163,840 tokens)
     in one call: every block's state, and the outputs of every fourth block
-    and the last, against the fp64 carried state."""
+    and the last, against the fp64 carried state.  Each block is drawn once:
+    the oracle's carried state and sampled outputs are formed as the blocks
+    are uploaded."""
     w = workloads.WORKLOADS[5]
     N, T = w.L * w.chunks, w.L
     q = torch.empty((w.B, w.H, N, w.d), dtype=torch.bfloat16, device="cuda")
     k, v = torch.empty_like(q), torch.empty_like(q)
-    for n in range(w.chunks):
-        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
-        sl = slice(n * T, (n + 1) * T)
-        q[:, :, sl], k[:, :, sl], v[:, :, sl] = dev(Qn, "bf16"), dev(Kn, "bf16"), dev(Vn, "bf16")
-    out, states = la.blockcausal_forward(q, k, v, T, eps=EPS)
-    torch.cuda.synchronize()
     S = np.zeros((w.B, w.H, w.d, w.d))
     z = np.zeros((w.B, w.H, w.d))
-    worst = 0.0
-    for n in range(w.chunks):
-        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
+    ref_states, ref_outs = [], {}
+    for n, (Qn, Kn, Vn) in drawn_chunks(lambda c: workloads.chunk_qkv(w, c), range(w.chunks)):
+        sl = slice(n * T, (n + 1) * T)
+        q[:, :, sl], k[:, :, sl], v[:, :, sl] = dev(Qn, "bf16"), dev(Kn, "bf16"), dev(Vn, "bf16")
         KV, kk = oracle.kv_of_block(Kn, Vn)
         S, z = S + KV, z + kk
+        ref_states.append((S, z))
+        if n % 4 == 0 or n == w.chunks - 1:
+            ref_outs[n] = oracle.readout(Qn, S, z, EPS)
+    out, states = la.blockcausal_forward(q, k, v, T, eps=EPS)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for n, (S, z) in enumerate(ref_states):
         es = max(state_err(host(states[:, :, n]), S, z))
         eo = 0.0
-        if n % 4 == 0 or n == w.chunks - 1:
-            eo = out_err(host(out[:, :, n * T:(n + 1) * T]), oracle.readout(Qn, S, z, EPS))
+        if n in ref_outs:
+            eo = out_err(host(out[:, :, n * T:(n + 1) * T]), ref_outs[n])
             report(f"long-horizon one-call block {n}", out=eo, state=es)
         else:
             report(f"long-horizon one-call block {n}", state=es)

@@ -12,8 +12,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import (BF16_MISMATCH_MAX, TOL, bf16_rounding, dev, host, out_err, report,
-                     state_err, state_np)
+from helpers import (BF16_MISMATCH_MAX, TOL, bf16_rounding, dev, drawn_chunks, host, out_err,
+                     report, state_err, state_np)
 
 import block_causal_linear_amd as la
 
@@ -241,21 +241,24 @@ def test_rope_480p_1min_one_call():
     N, T = w.L * w.chunks, w.L
     q = torch.empty((w.B, w.H, N, w.d), dtype=torch.bfloat16, device="cuda")
     k, v = torch.empty_like(q), torch.empty_like(q)
-    for n in range(w.chunks):
-        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
+    # each block is drawn once: the oracle carries its state as the blocks are uploaded
+    S, z = oracle.zero_state(w.B, w.H, w.d)
+    ref_states, ref_outs = [], {}
+    for n, (Qn, Kn, Vn) in drawn_chunks(lambda c: workloads.chunk_qkv(w, c), range(w.chunks)):
         sl = slice(n * T, (n + 1) * T)
         q[:, :, sl], k[:, :, sl], v[:, :, sl] = dev(Qn, "bf16"), dev(Kn, "bf16"), dev(Vn, "bf16")
-    out, states = la.blockcausal_forward_rope(q, k, v, T, 0, gh, gw, THETA, eps=EPS)
-    torch.cuda.synchronize()
-    S, z = oracle.zero_state(w.B, w.H, w.d)
-    worst = 0.0
-    for n in range(w.chunks):
-        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
         O_ref, S, z = oracle.rope_chunk_forward(Qn, Kn, Vn, S, z, EPS, workloads.chunk_frame0(w, n),
                                                 gh, gw, THETA)
-        es = max(state_err(host(states[:, :, n]), S, z))
+        ref_states.append((S, z))
         if n in (0, 5, w.chunks - 1):
-            eo = out_err(host(out[:, :, n * T:(n + 1) * T]), O_ref)
+            ref_outs[n] = O_ref
+    out, states = la.blockcausal_forward_rope(q, k, v, T, 0, gh, gw, THETA, eps=EPS)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for n, (S, z) in enumerate(ref_states):
+        es = max(state_err(host(states[:, :, n]), S, z))
+        if n in ref_outs:
+            eo = out_err(host(out[:, :, n * T:(n + 1) * T]), ref_outs[n])
             report(f"rope 480p one-call block {n}", out=eo, state=es)
             worst = max(worst, eo)
         else:
@@ -275,8 +278,7 @@ def test_rope_long_horizon_d128_one_call():
     q = torch.empty((w.B, w.H, N, w.d), dtype=torch.bfloat16, device="cuda")
     k, v = torch.empty_like(q), torch.empty_like(q)
     Qs, Ks, Vs = ([np.empty((N, w.d), dtype=np.float32) for _ in heads] for _ in range(3))
-    for n in range(w.chunks):
-        Qn, Kn, Vn = workloads.chunk_qkv(w, n)
+    for n, (Qn, Kn, Vn) in drawn_chunks(lambda c: workloads.chunk_qkv(w, c), range(w.chunks)):
         sl = slice(n * T, (n + 1) * T)
         q[:, :, sl], k[:, :, sl], v[:, :, sl] = dev(Qn, "bf16"), dev(Kn, "bf16"), dev(Vn, "bf16")
         for i, (b, h) in enumerate(heads):
