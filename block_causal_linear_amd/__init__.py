@@ -45,6 +45,12 @@ class LaunchOpts(ctypes.Structure):
                 ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
 
 
+class BackwardShape(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_int), ("query_splits", ctypes.c_int),
+                ("query_workgroups", ctypes.c_int), ("key_items", ctypes.c_int),
+                ("key_workgroups", ctypes.c_int), ("key_sweep_units", ctypes.c_int)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -72,6 +78,7 @@ _SIGNATURES = {
                                        _I, _I, _I, _F, ctypes.POINTER(LaunchOpts), _P],
     "la_backward_workspace_size": [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_Z)],
     "la_backward_stream_count": [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)],
+    "la_backward_plan": [_I, _I, _I, _I, _I, _I, _I, _I, _I, _Z, ctypes.POINTER(BackwardShape)],
     "la_blockcausal_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                 _I, _I, _F, _P, _Z, _P],
     "la_blockcausal_backward_ex": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
@@ -400,6 +407,19 @@ def backward_stream_count(B, H, N, T, d, in_dtype=torch.bfloat16, rope=False):
                                           int(bool(rope)), ctypes.byref(c)),
            "la_backward_stream_count")
     return c.value
+
+
+def backward_plan(B, H, N, T, d, in_dtype=torch.bfloat16, rope=False, query_splits=0,
+                  key_workgroups=0, workspace_bytes=0):
+    """The launch shape (a dict of la_backward_shape's fields) a backward call
+    of this shape would use on one stream; query_splits and key_workgroups
+    are the launch requests (0: the library's choice), workspace_bytes the
+    workspace it is given (0: as much as it needs)."""
+    sh = BackwardShape()
+    _check(lib().la_backward_plan(B, H, N, max(int(T), 1), d, _DTYPE[in_dtype], int(bool(rope)),
+                                  int(query_splits), int(key_workgroups), int(workspace_bytes),
+                                  ctypes.byref(sh)), "la_backward_plan")
+    return {name: getattr(sh, name) for name, _ in BackwardShape._fields_}
 
 
 def _workspace(workspace, need, device):

@@ -31,7 +31,7 @@ static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES]
 
 namespace {
 
-constexpr int kAbiVersion = 12;
+constexpr int kAbiVersion = 13;
 
 // The address of `scratch` on the device of `stream` (the current device for
 // the null stream), looked up on that device's first call and kept.
@@ -1212,6 +1212,33 @@ int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int r
   if (T <= 0 || count == nullptr) return LA_E_INVAL;
   if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
   *count = bwd_two_streams(B, H, N, d, in_dt, rotary != 0) ? 2 : 1;
+  return LA_OK;
+}
+
+int la_backward_plan(int B, int H, int N, int T, int d, int in_dt, int rotary,
+                     int query_splits_request, int key_workgroups_request,
+                     size_t workspace_bytes, la_backward_shape* shape) {
+  int rc = check_shape(B, H, N, d, in_dt, LA_F32);
+  if (rc != LA_OK) return rc;
+  if (T <= 0 || shape == nullptr || query_splits_request < 0 || key_workgroups_request < 0)
+    return LA_E_INVAL;
+  if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
+  *shape = la_backward_shape{};
+  if (N == 0) return LA_OK;
+  const BwdPlan p = make_bwd_plan(B, H, N, T, d, in_dt, query_splits_request,
+                                  key_workgroups_request,
+                                  workspace_bytes == 0 ? SIZE_MAX : workspace_bytes,
+                                  rotary != 0);
+  if (workspace_bytes != 0 && p.ws_bytes > workspace_bytes) return LA_E_INVAL;
+  // float32 kernels launch one workgroup per (b, h, block, split or item)
+  const long long pairs = static_cast<long long>(B) * H * p.nblk;
+  const bool bf = in_dt == LA_BF16;
+  shape->blocks = p.nblk;
+  shape->query_splits = p.qs;
+  shape->query_workgroups = bf ? p.qgrid : static_cast<int>(pairs * p.qs);
+  shape->key_items = p.ksweep ? 0 : p.ks;
+  shape->key_workgroups = p.ksweep || bf ? p.kgrid : static_cast<int>(pairs * p.ks);
+  shape->key_sweep_units = p.ksweep ? p.kupb : 0;
   return LA_OK;
 }
 

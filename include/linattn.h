@@ -300,6 +300,33 @@ int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int r
                              int* count);
 
 /*
+ * la_backward_plan - the launch shape a backward call with these arguments
+ * would use on one stream, with no device work (the two halves of a
+ * two-stream call keep its query splits).  query_splits_request and
+ * key_workgroups_request are the kv_splits and readout_workgroups fields of
+ * la_launch_opts in the _ex calls (0: the library's choice); workspace_bytes
+ * is the size of the workspace the call is given (0: as much as it needs,
+ * la_backward_workspace_size); rotary != 0 asks for the RoPE'd backward.
+ * Errors as for la_backward_workspace_size, plus LA_E_INVAL for a negative
+ * request or a workspace too small for any plan (as the call itself).
+ */
+typedef struct la_backward_shape {
+  int blocks;           /* blocks of T tokens (0 when N = 0) */
+  int query_splits;     /* query-gradient items per (b, h, block); above 1, each
+                           writes a partial state gradient to the workspace */
+  int query_workgroups; /* the query-gradient kernel's workgroups */
+  int key_items;        /* key-gradient items per (b, h, block); 0 with the sweep */
+  int key_workgroups;   /* the key-gradient kernel's workgroups */
+  int key_sweep_units;  /* the key-gradient sweep's 128-token units per block
+                           (bf16 inputs at d <= 64 without rotary or a key
+                           request); 0 when the key gradients take work items */
+} la_backward_shape;
+
+int la_backward_plan(int B, int H, int N, int T, int d, int in_dt, int rotary,
+                     int query_splits_request, int key_workgroups_request,
+                     size_t workspace_bytes, la_backward_shape* shape);
+
+/*
  * la_blockcausal_backward - gradients of la_blockcausal_forward.
  *   states    : [B][H][C][d*d+d] float32, read: the forward's `states`.
  *   dstates   : [B][H][C][d*d+d] float32, read, or NULL (zero): dL/dS_n, dL/dz_n.

@@ -30,7 +30,7 @@ int main(void) {
   la_launch_opts opts;
   memset(&opts, 0, sizeof opts);
 
-  expect("abi version", la_abi_version(), 12);
+  expect("abi version", la_abi_version(), 13);
   expect("status string", strcmp(la_status_string(LA_E_ALIAS), "illegal buffer overlap"), 0);
   expect("chunk d=48", la_chunk_forward(A, B, C, S, O, S2, 1, 2, 64, 48, LA_BF16, LA_F32, 1e-6f, 0),
          LA_E_UNSUPPORTED);
@@ -64,6 +64,20 @@ int main(void) {
     expect("plan", la_plan(1, 32, 75600, 64, LA_BF16, LA_F32, 0, 0, &splits, &wgs), LA_OK);
     expect("plan splits", splits, 16);
     expect("plan readout", wgs, 512);
+  }
+  {
+    la_backward_shape sh;
+    memset(&sh, 0xff, sizeof sh);
+    expect("backward plan", la_backward_plan(1, 32, 75600, 75600, 64, LA_BF16, 0, 0, 0, 0, &sh),
+           LA_OK);
+    expect("backward plan blocks", sh.blocks, 1);
+    expect("backward plan query splits", sh.query_splits, 16);
+    expect("backward plan query grid", sh.query_workgroups, 512);
+    expect("backward plan key items", sh.key_items, 0);
+    expect("backward plan key grid", sh.key_workgroups, 512);
+    expect("backward plan sweep units", sh.key_sweep_units, 591);
+    expect("backward plan no output",
+           la_backward_plan(1, 32, 75600, 75600, 64, LA_BF16, 0, 0, 0, 0, NULL), LA_E_INVAL);
   }
   if (failures == 0) printf("abi_smoke ok\n");
   return failures == 0 ? 0 : 1;

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.abi_version() == 12
+    assert la.abi_version() == 13
     for code in range(7):
         assert la._status_string(code) != "unknown status"
     assert la._status_string(99) == "unknown status"
