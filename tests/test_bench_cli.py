@@ -1,6 +1,7 @@
 """bench.py's command line on the CPU: more than one GPU is refused with a
-message and exit status 2 before anything touches a device, and the commands
-the profile summaries quote use options bench.py still accepts."""
+message and exit status 2 before anything touches a device, the commands the
+profile summaries quote use options bench.py still accepts, and the tests the
+docs name exist."""
 
 import os
 import subprocess
@@ -39,3 +40,23 @@ def test_profile_commands_use_current_options():
     for f in files:
         for w in re.findall(r"--workload (\w+)", open(f).read()):
             assert w in workloads or w == "W", (os.path.basename(f), w)
+
+
+def test_docs_name_existing_tests():
+    """Every test function or test file the docs and profile summaries name
+    exists under tests/."""
+    import glob
+    import re
+
+    sources = sorted(glob.glob(os.path.join(ROOT, "tests", "*.py")))
+    known = {os.path.basename(f)[:-3] for f in sources}
+    for f in sources:
+        known |= set(re.findall(r"def (test_\w+)", open(f).read()))
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md")))
+    files += [os.path.join(ROOT, n) for n in ("DESIGN.md", "README.md")]
+    missing = []
+    for f in files:
+        for name in set(re.findall(r"\b(test_[a-z0-9_]+)\b", open(f).read())):
+            if name not in known:
+                missing.append((os.path.basename(f), name))
+    assert not missing, missing
