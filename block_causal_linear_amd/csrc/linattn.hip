@@ -1223,6 +1223,7 @@ int la_backward_plan(int B, int H, int N, int T, int d, int in_dt, int rotary,
   if (T <= 0 || shape == nullptr || query_splits_request < 0 || key_workgroups_request < 0)
     return LA_E_INVAL;
   if ((rc = check_sizes(B, H, N, T, d)) != LA_OK) return rc;
+  if (rotary != 0 && N >= kRopeMaxTokens - 64) return LA_E_INVAL;  // as check_rope
   *shape = la_backward_shape{};
   if (N == 0) return LA_OK;
   const BwdPlan p = make_bwd_plan(B, H, N, T, d, in_dt, query_splits_request,

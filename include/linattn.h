@@ -308,7 +308,8 @@ int la_backward_stream_count(int B, int H, int N, int T, int d, int in_dt, int r
  * is the size of the workspace the call is given (0: as much as it needs,
  * la_backward_workspace_size); rotary != 0 asks for the RoPE'd backward.
  * Errors as for la_backward_workspace_size, plus LA_E_INVAL for a negative
- * request or a workspace too small for any plan (as the call itself).
+ * request, a workspace too small for any plan (as the call itself), or, with
+ * rotary != 0, a sequence the rotary calls refuse (N >= 2^22 - 64).
  */
 typedef struct la_backward_shape {
   int blocks;           /* blocks of T tokens (0 when N = 0) */
